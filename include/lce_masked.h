@@ -1,0 +1,157 @@
+/*
+ * lce_masked.h — C ABI of the MI355X (gfx950) masked cross-entropy library.
+ *
+ * Two layers, both sum-reduced masked cross-entropy over a large vocabulary:
+ *
+ *   1. Chunked CE over materialised bf16 logits (ce_chunked_*). Defined by NeMo Automodel
+ *      PR #2996, "feat(loss): chunked masked CE, packing-mask preservation, scoped MoE AC":
+ *      the first commit message (forward = per-row fp32 logsumexp and label-logit gather
+ *      summed into one scalar; backward = softmax recomputed, minus one-hot, times
+ *      1/num_label_tokens; zero num_label_tokens guard), the fourth commit message (the
+ *      gradient is written into the logits storage) and the *Motivation* section (the fp32
+ *      working set is bounded by one [chunk_size, V] slice).
+ *
+ *   2. Fused linear CE (flce_*): logits z = hidden · weightᵀ (+ bias) never kept in full; the
+ *      call returns the loss, grad_hidden, an fp32 grad_weight and grad_bias. Defined by
+ *      Liger-Kernel issue #533, "Gradient checkpointing for grad_weight in LFCE" (feature
+ *      pitch: per-chunk logits GEMM, grad_weight += (logits gradient)ᵀ · input chunk; the
+ *      comments on a fully recomputed variant) and Liger-Kernel issue #941, "No gain in VRAM
+ *      usage with LigerFusedLinearCrossEntropyLoss" (inputs: hidden, targets, lm_head weight,
+ *      optional bias; the lm_head weight may be tied to the embedding, hence the accumulate
+ *      flag).
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller. The library never allocates,
+ *     frees or synchronises: it validates arguments on the host, enqueues kernels on `stream`
+ *     (a hipStream_t; NULL = the null stream) and returns.
+ *   - bf16 tensors are passed as uint16_t bit patterns, row-major.
+ *   - Labels are int32. A row carries a label when label != ignore_index and
+ *     0 <= label < V. Any other label that is not ignore_index sets bit
+ *     LCE_STATUS_BAD_LABEL in *status_out (device int32, may be NULL) and the row is treated
+ *     as ignored; nothing is ever read out of bounds.
+ *   - num_label_tokens (T): >= 0 uses that value as the normaliser; < 0 counts the rows that
+ *     carry a label, on the device. s = 1/T, and T == 0 gives loss 0 and all-zero gradients
+ *     (never NaN).
+ *   - grad_output: device pointer to one fp32 upstream gradient g, or NULL for g = 1.
+ *     Every gradient is g · s · (softmax − onehot) propagated through the op.
+ *   - loss_out: device fp32 scalar, = s · Σ_{labelled rows} (lse_i − z_{i,y_i}); the sum is
+ *     taken in fp64 in a fixed order, so results are bitwise repeatable run to run and do not
+ *     depend on chunk_size.
+ *   - workspace: caller-provided device memory of at least the size the matching
+ *     *_workspace_size query returns (256-byte aligned). Its contents on entry do not
+ *     matter. Calls that share a workspace must be ordered on one stream.
+ *   - Return value: LCE_OK or an error code. Argument errors are reported before any device
+ *     work is enqueued; LCE_ERR_HIP means a launch failed (the stream state is then the
+ *     caller's to inspect).
+ */
+#ifndef LCE_MASKED_H
+#define LCE_MASKED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define LCE_OK                   0
+#define LCE_ERR_NULL_ARG         1  /* a required pointer is NULL                                 */
+#define LCE_ERR_BAD_SHAPE        2  /* n < 0, v < 1, h < 1, ld < v, or a size overflows int64     */
+#define LCE_ERR_BAD_CHUNK        3  /* chunk_size <= 0                                            */
+#define LCE_ERR_WORKSPACE        4  /* workspace NULL or smaller than the query's answer          */
+#define LCE_ERR_HIP              5  /* a HIP call or kernel launch failed                         */
+#define LCE_ERR_DEVICE           6  /* the current device is not gfx950                           */
+#define LCE_ERR_BAD_FLAGS        7  /* unknown flag bits                                          */
+#define LCE_ERR_ALIGNMENT        8  /* a pointer is not aligned to its element size               */
+
+/* bits of *status_out */
+#define LCE_STATUS_BAD_LABEL     1  /* some label was neither ignore_index nor in [0, V)          */
+
+/* flce flags */
+#define FLCE_RECOMPUTE           1u /* do not store the fp32 logits slice; recompute the logits
+                                       tile by tile for the gradients (the fully recomputed
+                                       schedule of Liger-Kernel issue #533's comments)           */
+#define FLCE_ACCUMULATE          2u /* add into grad_weight / grad_bias instead of overwriting
+                                       (tied embedding and lm_head, Liger-Kernel issue #941)     */
+
+/* Human-readable name of a return code (static storage; never NULL). */
+const char* lce_status_str(int status);
+
+/* ------------------------------------------------------------------ chunked CE */
+
+/* Workspace bytes needed by ce_chunked_fwd / ce_chunked_bwd* for n rows. O(n): the CE kernels
+ * stream each row through registers and never build an fp32 [chunk_size, V] slice, so the
+ * size does not depend on v or chunk_size. Returns LCE_ERR_BAD_SHAPE / LCE_ERR_BAD_CHUNK /
+ * LCE_ERR_NULL_ARG on bad input. Host-only; safe without a GPU. */
+int ce_chunked_workspace_size(int64_t n, int64_t v, int64_t chunk_size, size_t* bytes);
+
+/* Forward: loss_out = s · Σ_i (lse_i − z_{i,y_i}) over labelled rows.
+ *   logits      bf16 [n, ld] row-major, first v columns used, read only. Rows without a label
+ *               are not read.
+ *   labels      int32 [n]
+ *   chunk_size  rows per loss partial; must be > 0. The per-row terms are combined in one
+ *               fixed order whatever its value (results are chunk-size invariant).
+ *   lse_out     fp32 [n] or NULL. Receives lse_i = ln Σ_v exp(z_iv) for labelled rows and 0
+ *               for the others. Passing it to the backward saves one read of each row.
+ *   status_out  device int32 or NULL; overwritten with LCE_STATUS_* bits.
+ * n == 0 is valid (loss 0). */
+int ce_chunked_fwd(const uint16_t* logits, int64_t n, int64_t v, int64_t ld,
+                   const int32_t* labels, int32_t ignore_index, int64_t chunk_size,
+                   int64_t num_label_tokens, float* loss_out, float* lse_out,
+                   int32_t* status_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward, out of place: grad[i, :] = g · s · (softmax(z_i) − onehot(y_i)) for labelled rows,
+ * exactly 0 for the others; fp32 math, rounded to bf16 (nearest even).
+ *   logits      bf16 [n, ld] (read)
+ *   grad        bf16 [n, ldg] (written, first v columns). grad == logits with ldg == ld is the
+ *               in-place case; any other overlap of the two ranges is undefined.
+ *   lse         fp32 [n] from ce_chunked_fwd, or NULL to recompute each row's logsumexp
+ *               (one more read of every labelled row). */
+int ce_chunked_bwd(const uint16_t* logits, int64_t n, int64_t v, int64_t ld,
+                   uint16_t* grad, int64_t ldg, const int32_t* labels, int32_t ignore_index,
+                   int64_t chunk_size, int64_t num_label_tokens, const float* grad_output,
+                   const float* lse, int32_t* status_out, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* Backward in place: as ce_chunked_bwd with grad = logits_inout, ldg = ld. The logits are
+ * destroyed; rows without a label are overwritten with zeros (fourth commit message of NeMo
+ * Automodel PR #2996: the logits storage is reused as the gradient buffer). */
+int ce_chunked_bwd_inplace(uint16_t* logits_inout, int64_t n, int64_t v, int64_t ld,
+                           const int32_t* labels, int32_t ignore_index, int64_t chunk_size,
+                           int64_t num_label_tokens, const float* grad_output, const float* lse,
+                           int32_t* status_out, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* ------------------------------------------------------------------ fused linear CE */
+
+/* Workspace bytes for flce_fwd_bwd: one fp32 [chunk, V] logits slice (rows padded to the
+ * kernels' tile width) plus O(n + chunk) bookkeeping; with FLCE_RECOMPUTE the slice holds
+ * bf16 probabilities only (half the bytes). Host-only; safe without a GPU. */
+int flce_workspace_size(int64_t n, int64_t h, int64_t v, int64_t chunk_size, uint32_t flags,
+                        size_t* bytes);
+
+/* Fused linear CE forward + backward in one call, one chunk of rows at a time.
+ *   hidden       bf16 [n, h] row-major            weight  bf16 [v, h] row-major
+ *   bias         fp32 [v] or NULL                 labels  int32 [n]
+ *   loss_out     fp32 scalar (required)
+ *   lse_out      fp32 [n] or NULL (logsumexp of labelled rows; 0 for the others)
+ *   grad_hidden  bf16 [n, h] or NULL: g·s·(P − Y)·W per row, 0 for rows without a label
+ *   grad_weight  fp32 [v, h] or NULL: g·s·(P − Y)ᵀ·hidden (+= with FLCE_ACCUMULATE)
+ *   grad_bias    fp32 [v] or NULL (needs bias): g·s·Σ_rows (P − Y) (+= with FLCE_ACCUMULATE)
+ * where P is the row softmax of z = hidden·weightᵀ + bias and Y the one-hot labels.
+ * h must be a multiple of 8 (16-byte rows). Matrix products run on bf16 MFMA with fp32
+ * accumulation; the probabilities enter the gradient products as bf16, the one-hot term and
+ * the scale g·s are applied in fp32. */
+int flce_fwd_bwd(const uint16_t* hidden, const uint16_t* weight, const float* bias,
+                 const int32_t* labels, int64_t n, int64_t h, int64_t v, int32_t ignore_index,
+                 int64_t chunk_size, int64_t num_label_tokens, uint32_t flags,
+                 const float* grad_output, float* loss_out, float* lse_out,
+                 uint16_t* grad_hidden, float* grad_weight, float* grad_bias,
+                 int32_t* status_out, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCE_MASKED_H */

@@ -1,0 +1,167 @@
+// extern "C" entry points of liblce_masked.so: argument validation, workspace carving and
+// the launch schedule. Every error that can be detected from the arguments is returned
+// before any HIP call, so these checks run (and are tested) on a machine without a GPU.
+#include <atomic>
+#include <cstring>
+#include <limits>
+
+#include "common.h"
+#include "flce.h"
+#include "lce_masked.h"
+
+namespace {
+
+using lce::CeWorkspace;
+
+constexpr int64_t kI64Max = std::numeric_limits<int64_t>::max();
+
+bool mul_overflows(int64_t a, int64_t b) { return a != 0 && b > kI64Max / a; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Per-device cache: 0 = unknown, 1 = gfx950, 2 = other.
+std::atomic<int> g_arch_ok[64];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LCE_ERR_HIP;
+  if (dev >= 0 && dev < 64) {
+    int c = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (c) return c == 1 ? LCE_OK : LCE_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return LCE_ERR_HIP;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev >= 0 && dev < 64) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? LCE_OK : LCE_ERR_DEVICE;
+}
+
+int ce_check_shape(int64_t n, int64_t v, int64_t ld, int64_t chunk_size) {
+  if (n < 0 || v < 1 || ld < v) return LCE_ERR_BAD_SHAPE;
+  if (n > int64_t(std::numeric_limits<int32_t>::max())) return LCE_ERR_BAD_SHAPE;  // grid.x
+  if (mul_overflows(n, ld) || mul_overflows(n * ld, 2)) return LCE_ERR_BAD_SHAPE;
+  if (chunk_size <= 0) return LCE_ERR_BAD_CHUNK;
+  return LCE_OK;
+}
+
+#define LCE_TRY_HIP(expr)                        \
+  do {                                           \
+    if ((expr) != hipSuccess) return LCE_ERR_HIP; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* lce_status_str(int status) {
+  switch (status) {
+    case LCE_OK: return "ok";
+    case LCE_ERR_NULL_ARG: return "a required pointer is NULL";
+    case LCE_ERR_BAD_SHAPE: return "bad shape (n < 0, v < 1, h < 1, ld < v, h % 8 != 0, or size overflow)";
+    case LCE_ERR_BAD_CHUNK: return "chunk_size must be > 0";
+    case LCE_ERR_WORKSPACE: return "workspace is NULL or smaller than the size query's answer";
+    case LCE_ERR_HIP: return "a HIP call or kernel launch failed";
+    case LCE_ERR_DEVICE: return "the current device is not gfx950 (MI355X)";
+    case LCE_ERR_BAD_FLAGS: return "unknown flag bits";
+    case LCE_ERR_ALIGNMENT: return "a pointer is not aligned to its element size";
+    default: return "unknown status";
+  }
+}
+
+int ce_chunked_workspace_size(int64_t n, int64_t v, int64_t chunk_size, size_t* bytes) {
+  if (!bytes) return LCE_ERR_NULL_ARG;
+  const int rc = ce_check_shape(n, v, v, chunk_size);
+  if (rc != LCE_OK) return rc;
+  *bytes = lce::ce_workspace_bytes(n);
+  return LCE_OK;
+}
+
+int ce_chunked_fwd(const uint16_t* logits, int64_t n, int64_t v, int64_t ld,
+                   const int32_t* labels, int32_t ignore_index, int64_t chunk_size,
+                   int64_t num_label_tokens, float* loss_out, float* lse_out,
+                   int32_t* status_out, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = ce_check_shape(n, v, ld, chunk_size);
+  if (rc != LCE_OK) return rc;
+  if (!loss_out || (n > 0 && (!logits || !labels))) return LCE_ERR_NULL_ARG;
+  if (!workspace || workspace_bytes < lce::ce_workspace_bytes(n)) return LCE_ERR_WORKSPACE;
+  if (!aligned(logits, 2) || !aligned(labels, 4) || !aligned(loss_out, 4) ||
+      !aligned(lse_out, 4) || !aligned(status_out, 4) || !aligned(workspace, 256))
+    return LCE_ERR_ALIGNMENT;
+  if ((rc = check_device()) != LCE_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  CeWorkspace ws = lce::ce_workspace_carve(workspace, n);
+  LCE_TRY_HIP(lce::launch_label_prep(labels, n, v, ignore_index, ws.count, status_out, s));
+  LCE_TRY_HIP(lce::launch_ce_fwd_rows(logits, n, v, ld, labels, ignore_index, ws.row_loss,
+                                      lse_out, s));
+  LCE_TRY_HIP(lce::launch_loss_reduce(ws.row_loss, n, ws.count,
+                                      num_label_tokens >= 0 ? num_label_tokens : -1, loss_out, s));
+  return LCE_OK;
+}
+
+int ce_chunked_bwd(const uint16_t* logits, int64_t n, int64_t v, int64_t ld, uint16_t* grad,
+                   int64_t ldg, const int32_t* labels, int32_t ignore_index, int64_t chunk_size,
+                   int64_t num_label_tokens, const float* grad_output, const float* lse,
+                   int32_t* status_out, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = ce_check_shape(n, v, ld, chunk_size);
+  if (rc != LCE_OK) return rc;
+  if (ldg < v || mul_overflows(n, ldg) || mul_overflows(n * ldg, 2)) return LCE_ERR_BAD_SHAPE;
+  if (n > 0 && (!logits || !grad || !labels)) return LCE_ERR_NULL_ARG;
+  if (!workspace || workspace_bytes < lce::ce_workspace_bytes(n)) return LCE_ERR_WORKSPACE;
+  if (!aligned(logits, 2) || !aligned(grad, 2) || !aligned(labels, 4) ||
+      !aligned(grad_output, 4) || !aligned(lse, 4) || !aligned(status_out, 4) ||
+      !aligned(workspace, 256))
+    return LCE_ERR_ALIGNMENT;
+  if ((rc = check_device()) != LCE_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  CeWorkspace ws = lce::ce_workspace_carve(workspace, n);
+  LCE_TRY_HIP(lce::launch_label_prep(labels, n, v, ignore_index, ws.count, status_out, s));
+  LCE_TRY_HIP(lce::launch_ce_bwd_rows(logits, ld, grad, ldg, n, v, labels, ignore_index, lse,
+                                      ws.count, num_label_tokens >= 0 ? num_label_tokens : -1,
+                                      grad_output, s));
+  return LCE_OK;
+}
+
+int ce_chunked_bwd_inplace(uint16_t* logits_inout, int64_t n, int64_t v, int64_t ld,
+                           const int32_t* labels, int32_t ignore_index, int64_t chunk_size,
+                           int64_t num_label_tokens, const float* grad_output, const float* lse,
+                           int32_t* status_out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return ce_chunked_bwd(logits_inout, n, v, ld, logits_inout, ld, labels, ignore_index,
+                        chunk_size, num_label_tokens, grad_output, lse, status_out, workspace,
+                        workspace_bytes, stream);
+}
+
+int flce_workspace_size(int64_t n, int64_t h, int64_t v, int64_t chunk_size, uint32_t flags,
+                        size_t* bytes) {
+  if (!bytes) return LCE_ERR_NULL_ARG;
+  const int rc = lce::flce_check_shape(n, h, v, chunk_size, flags);
+  if (rc != LCE_OK) return rc;
+  *bytes = lce::flce_workspace_bytes(n, h, v, chunk_size, flags);
+  return LCE_OK;
+}
+
+int flce_fwd_bwd(const uint16_t* hidden, const uint16_t* weight, const float* bias,
+                 const int32_t* labels, int64_t n, int64_t h, int64_t v, int32_t ignore_index,
+                 int64_t chunk_size, int64_t num_label_tokens, uint32_t flags,
+                 const float* grad_output, float* loss_out, float* lse_out,
+                 uint16_t* grad_hidden, float* grad_weight, float* grad_bias,
+                 int32_t* status_out, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = lce::flce_check_shape(n, h, v, chunk_size, flags);
+  if (rc != LCE_OK) return rc;
+  if (!loss_out || !weight || (n > 0 && (!hidden || !labels)) || (grad_bias && !bias))
+    return LCE_ERR_NULL_ARG;
+  if (!workspace || workspace_bytes < lce::flce_workspace_bytes(n, h, v, chunk_size, flags))
+    return LCE_ERR_WORKSPACE;
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(bias, 4) || !aligned(labels, 4) ||
+      !aligned(grad_output, 4) || !aligned(loss_out, 4) || !aligned(lse_out, 4) ||
+      !aligned(grad_hidden, 16) || !aligned(grad_weight, 16) || !aligned(grad_bias, 4) ||
+      !aligned(status_out, 4) || !aligned(workspace, 256))
+    return LCE_ERR_ALIGNMENT;
+  if ((rc = check_device()) != LCE_OK) return rc;
+  lce::FlceArgs a{hidden, weight, bias, labels, n, h, v, ignore_index, chunk_size,
+                  num_label_tokens, flags, grad_output, loss_out, lse_out, grad_hidden,
+                  grad_weight, grad_bias, status_out, workspace};
+  return lce::flce_run(a, static_cast<hipStream_t>(stream)) == hipSuccess ? LCE_OK : LCE_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,329 @@
+// Chunked masked cross-entropy over materialised bf16 logits, for gfx950.
+//
+// What is computed follows NeMo Automodel PR #2996 ("feat(loss): chunked masked CE,
+// packing-mask preservation, scoped MoE AC"), first and fourth commit messages: an fp32
+// logsumexp per row and the label logit gathered, summed into one scalar scaled by
+// 1/num_label_tokens; the backward recomputes softmax minus one-hot and may write the
+// gradient over the logits storage.
+//
+// How it is computed here: the PR bounds the fp32 working set by processing one
+// [chunk_size, V] slice at a time. These kernels go further and never build an fp32 slice
+// at all: one workgroup streams one bf16 row through registers with 16-byte loads, keeps an
+// online (max, sum-exp) per lane, and merges lanes with wavefront shuffles. The work is
+// HBM-bound (2 bytes per element read in the forward, 2 read + 2 written in the backward),
+// so the kernels are written around coalesced 16-byte accesses, several loads in flight per
+// lane, and about 7 VALU operations per element (unpack, max, one FMA, exp2, add).
+#include "common.h"
+
+namespace lce {
+
+namespace {
+
+constexpr int kRowThreads = 256;  // 4 wavefronts per row
+constexpr int kUnroll = 4;        // 16-byte loads in flight per lane
+
+// Split a row of v bf16 elements starting at p into: `head` scalar elements up to the first
+// 16-byte boundary, `nvec` aligned 8-element vectors, and `tail` trailing scalars.
+struct RowSplit {
+  int head;
+  int64_t nvec;
+  int tail;
+};
+
+__device__ __forceinline__ RowSplit split_row(const void* p, int64_t v) {
+  uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  int head = int(((16u - (a & 15u)) & 15u) >> 1);
+  if (head > v) head = int(v);
+  int64_t rest = v - head;
+  return RowSplit{head, rest >> 3, int(rest & 7)};
+}
+
+__device__ __forceinline__ bool row_has_label(int32_t y, int64_t v, int32_t ignore_index) {
+  return y != ignore_index && y >= 0 && int64_t(y) < v;
+}
+
+// Block-wide merge of per-lane (m, s); result broadcast to every lane.
+__device__ __forceinline__ void block_lse_reduce(float& m, float& s) {
+  __shared__ float sm[kRowThreads / 64], ss[kRowThreads / 64];
+  wave_lse_reduce(m, s);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sm[wave] = m;
+    ss[wave] = s;
+  }
+  __syncthreads();
+  m = sm[0];
+  s = ss[0];
+#pragma unroll
+  for (int w = 1; w < kRowThreads / 64; ++w) lse_merge(m, s, sm[w], ss[w]);
+}
+
+// Per-lane online logsumexp over one row. Returns the lane's (m, s) pair.
+__device__ __forceinline__ void row_lse_partial(const uint16_t* row, int64_t v, float& m_out,
+                                                float& s_out) {
+  const RowSplit sp = split_row(row, v);
+  const uint4* vec = reinterpret_cast<const uint4*>(row + sp.head);
+  float m = -INFINITY, s = 0.f;
+  const int tid = threadIdx.x;
+
+  auto absorb = [&](const float* x, int cnt) {
+    float mx = x[0];
+    for (int k = 1; k < cnt; ++k) mx = fmaxf(mx, x[k]);
+    float mn = fmaxf(m, mx);
+    if (mn == -INFINITY) return;
+    const float c = mn * kLog2e;
+    float acc = (m == mn) ? s : s * fast_exp2(fmaf(m, kLog2e, -c));
+    for (int k = 0; k < cnt; ++k) acc += fast_exp2(fmaf(x[k], kLog2e, -c));
+    s = acc;
+    m = mn;
+  };
+
+  int64_t j = tid;
+  // main loop: kUnroll full vectors per lane per iteration
+  for (; j + int64_t(kRowThreads) * (kUnroll - 1) < sp.nvec; j += int64_t(kRowThreads) * kUnroll) {
+    uint4 q[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) q[u] = vec[j + int64_t(u) * kRowThreads];
+    float x[8 * kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      x[8 * u + 0] = bf16_lo(q[u].x); x[8 * u + 1] = bf16_hi(q[u].x);
+      x[8 * u + 2] = bf16_lo(q[u].y); x[8 * u + 3] = bf16_hi(q[u].y);
+      x[8 * u + 4] = bf16_lo(q[u].z); x[8 * u + 5] = bf16_hi(q[u].z);
+      x[8 * u + 6] = bf16_lo(q[u].w); x[8 * u + 7] = bf16_hi(q[u].w);
+    }
+    absorb(x, 8 * kUnroll);
+  }
+  for (; j < sp.nvec; j += kRowThreads) {
+    uint4 q = vec[j];
+    float x[8] = {bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y),
+                  bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w)};
+    absorb(x, 8);
+  }
+  if (tid < sp.head) {
+    float x = bf16_to_f32(row[tid]);
+    absorb(&x, 1);
+  }
+  if (tid < sp.tail) {
+    float x = bf16_to_f32(row[sp.head + sp.nvec * 8 + tid]);
+    absorb(&x, 1);
+  }
+  m_out = m;
+  s_out = s;
+}
+
+__global__ void __launch_bounds__(1024) label_prep_kernel(const int32_t* __restrict__ labels,
+                                                          int64_t n, int64_t v,
+                                                          int32_t ignore_index,
+                                                          long long* __restrict__ count_out,
+                                                          int32_t* __restrict__ status_out) {
+  __shared__ long long part[1024 / 64];
+  __shared__ int bad_any[1024 / 64];
+  long long cnt = 0;
+  int bad = 0;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+    const int32_t y = labels[i];
+    if (row_has_label(y, v, ignore_index)) ++cnt;
+    else if (y != ignore_index) bad = 1;
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    cnt += __shfl_xor(cnt, off, 64);
+    bad |= __shfl_xor(bad, off, 64);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    part[threadIdx.x >> 6] = cnt;
+    bad_any[threadIdx.x >> 6] = bad;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long t = 0;
+    int b = 0;
+    for (int w = 0; w < int(blockDim.x >> 6); ++w) {
+      t += part[w];
+      b |= bad_any[w];
+    }
+    if (count_out) *count_out = t;
+    if (status_out) *status_out = b ? 1 : 0;
+  }
+}
+
+__global__ void __launch_bounds__(kRowThreads) ce_fwd_rows_kernel(
+    const uint16_t* logits, int64_t v, int64_t ld, const int32_t* __restrict__ labels,
+    int32_t ignore_index, float* __restrict__ row_loss, float* __restrict__ lse_out) {
+  const int64_t i = blockIdx.x;
+  const int32_t y = labels[i];
+  if (!row_has_label(y, v, ignore_index)) {  // rows without a label are never read
+    if (threadIdx.x == 0) {
+      row_loss[i] = 0.f;
+      if (lse_out) lse_out[i] = 0.f;
+    }
+    return;
+  }
+  const uint16_t* row = logits + i * ld;
+  float m, s;
+  row_lse_partial(row, v, m, s);
+  block_lse_reduce(m, s);
+  if (threadIdx.x == 0) {
+    const float lse = m + fast_log2(s) * kLn2;
+    row_loss[i] = lse - bf16_to_f32(row[y]);
+    if (lse_out) lse_out[i] = lse;
+  }
+}
+
+// Fixed-order fp64 sum of the per-row terms, times 1/T (0 when T == 0).
+__global__ void __launch_bounds__(1024) loss_reduce_kernel(const float* __restrict__ row_loss,
+                                                           int64_t n,
+                                                           const long long* __restrict__ count_dev,
+                                                           long long count_host,
+                                                           float* __restrict__ loss_out) {
+  __shared__ double part[1024 / 64];
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) acc += double(row_loss[i]);
+  acc = wave_sum_f64(acc);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double total = 0.0;
+    for (int w = 0; w < int(blockDim.x >> 6); ++w) total += part[w];
+    const long long t = count_host >= 0 ? count_host : *count_dev;
+    *loss_out = t > 0 ? float(total / double(t)) : 0.f;
+  }
+}
+
+__global__ void __launch_bounds__(kRowThreads) ce_bwd_rows_kernel(
+    const uint16_t* logits, int64_t ld, uint16_t* grad, int64_t ldg, int64_t v,
+    const int32_t* __restrict__ labels, int32_t ignore_index, const float* __restrict__ lse_in,
+    const long long* __restrict__ count_dev, long long count_host,
+    const float* __restrict__ grad_output) {
+  // No __restrict__ on logits/grad: in place they are the same memory, and every element is
+  // read before the same lane overwrites it.
+  const int64_t i = blockIdx.x;
+  const int32_t y = labels[i];
+  uint16_t* grow = grad + i * ldg;
+  const long long t = count_host >= 0 ? count_host : *count_dev;
+  const float g = grad_output ? *grad_output : 1.f;
+  const RowSplit gs = split_row(grow, v);
+  const int tid = threadIdx.x;
+
+  if (!row_has_label(y, v, ignore_index) || t <= 0) {  // zero row (also the T == 0 guard)
+    uint4* gv = reinterpret_cast<uint4*>(grow + gs.head);
+    const uint4 z = {0u, 0u, 0u, 0u};
+    for (int64_t j = tid; j < gs.nvec; j += kRowThreads) gv[j] = z;
+    if (tid < gs.head) grow[tid] = 0;
+    if (tid < gs.tail) grow[gs.head + gs.nvec * 8 + tid] = 0;
+    return;
+  }
+  const uint16_t* row = logits + i * ld;
+  float lse;
+  if (lse_in) {
+    lse = lse_in[i];
+  } else {
+    float m, s;
+    row_lse_partial(row, v, m, s);
+    block_lse_reduce(m, s);
+    lse = m + fast_log2(s) * kLn2;
+  }
+  const float coef = float(double(g) / double(t));
+  const float c = lse * kLog2e;
+  // The input and output rows share their alignment when ld == ldg (always in place); the
+  // vector path needs it, otherwise fall back to scalars.
+  const RowSplit sp = split_row(row, v);
+  if (sp.head == gs.head) {
+    const uint4* xv = reinterpret_cast<const uint4*>(row + sp.head);
+    uint4* gv = reinterpret_cast<uint4*>(grow + sp.head);
+    const int64_t ylocal = int64_t(y) - sp.head;  // label position relative to the vector base
+    auto one = [&](uint4 q, int64_t j) -> uint4 {
+      float x[8] = {bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y),
+                    bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w)};
+      float p[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) p[k] = fast_exp2(fmaf(x[k], kLog2e, -c));
+      const int64_t off = ylocal - j * 8;
+      if (off >= 0 && off < 8) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (k == off) p[k] -= 1.f;
+      }
+      uint4 o;
+      o.x = pack_bf16x2(coef * p[0], coef * p[1]);
+      o.y = pack_bf16x2(coef * p[2], coef * p[3]);
+      o.z = pack_bf16x2(coef * p[4], coef * p[5]);
+      o.w = pack_bf16x2(coef * p[6], coef * p[7]);
+      return o;
+    };
+    int64_t j = tid;
+    for (; j + int64_t(kRowThreads) * (kUnroll - 1) < sp.nvec; j += int64_t(kRowThreads) * kUnroll) {
+      uint4 q[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) q[u] = xv[j + int64_t(u) * kRowThreads];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t jj = j + int64_t(u) * kRowThreads;
+        gv[jj] = one(q[u], jj);
+      }
+    }
+    for (; j < sp.nvec; j += kRowThreads) gv[j] = one(xv[j], j);
+    auto scalar = [&](int64_t col) {
+      float p = fast_exp2(fmaf(bf16_to_f32(row[col]), kLog2e, -c));
+      if (col == y) p -= 1.f;
+      grow[col] = f32_to_bf16(coef * p);
+    };
+    if (tid < sp.head) scalar(tid);
+    if (tid < sp.tail) scalar(sp.head + sp.nvec * 8 + tid);
+  } else {
+    for (int64_t col = tid; col < v; col += kRowThreads) {
+      float p = fast_exp2(fmaf(bf16_to_f32(row[col]), kLog2e, -c));
+      if (col == y) p -= 1.f;
+      grow[col] = f32_to_bf16(coef * p);
+    }
+  }
+}
+
+}  // namespace
+
+size_t ce_workspace_bytes(int64_t n) {
+  const size_t rows = (size_t(n) * sizeof(float) + 255) & ~size_t(255);
+  return 256 + rows;
+}
+
+CeWorkspace ce_workspace_carve(void* base, int64_t n) {
+  (void)n;
+  char* b = static_cast<char*>(base);
+  return CeWorkspace{reinterpret_cast<long long*>(b), reinterpret_cast<float*>(b + 256)};
+}
+
+hipError_t launch_label_prep(const int32_t* labels, int64_t n, int64_t v, int32_t ignore_index,
+                             long long* count_out, int32_t* status_out, hipStream_t stream) {
+  hipLaunchKernelGGL(label_prep_kernel, dim3(1), dim3(1024), 0, stream, labels, n, v,
+                     ignore_index, count_out, status_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_fwd_rows(const uint16_t* logits, int64_t n, int64_t v, int64_t ld,
+                              const int32_t* labels, int32_t ignore_index, float* row_loss,
+                              float* lse_out, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(ce_fwd_rows_kernel, dim3(unsigned(n)), dim3(kRowThreads), 0, stream,
+                     logits, v, ld, labels, ignore_index, row_loss, lse_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_loss_reduce(const float* row_loss, int64_t n, const long long* count_dev,
+                              long long count_host, float* loss_out, hipStream_t stream) {
+  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(1024), 0, stream, row_loss, n,
+                     count_dev, count_host, loss_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_bwd_rows(const uint16_t* logits, int64_t ld, uint16_t* grad, int64_t ldg,
+                              int64_t n, int64_t v, const int32_t* labels, int32_t ignore_index,
+                              const float* lse, const long long* count_dev, long long count_host,
+                              const float* grad_output, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(ce_bwd_rows_kernel, dim3(unsigned(n)), dim3(kRowThreads), 0, stream,
+                     logits, ld, grad, ldg, v, labels, ignore_index, lse, count_dev, count_host,
+                     grad_output);
+  return hipGetLastError();
+}
+
+}  // namespace lce

@@ -1,0 +1,81 @@
+// Shared device helpers for the gfx950 kernels (bf16 unpacking, wave reductions) and the
+// host-side launch declarations used by the C ABI in capi.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lce {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// bf16 is the upper half of an fp32: widening is a shift (low element) or a mask (high).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t p = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, p);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Merge two (max, sum of exp(x - max)) pairs.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;  // both empty
+  s = s * fast_exp2((m - mn) * kLog2e) + s2 * fast_exp2((m2 - mn) * kLog2e);
+  m = mn;
+}
+
+// Reduce (m, s) over a 64-lane wavefront; every lane ends with the result.
+__device__ __forceinline__ void wave_lse_reduce(float& m, float& s) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    float m2 = __shfl_xor(m, off, 64);
+    float s2 = __shfl_xor(s, off, 64);
+    lse_merge(m, s, m2, s2);
+  }
+}
+
+__device__ __forceinline__ double wave_sum_f64(double x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+}  // namespace lce
+
+// ---- host launchers (defined in the kernel files, called from capi.hip) ----
+namespace lce {
+
+struct CeWorkspace {
+  long long* count;  // device int64: number of labelled rows
+  float* row_loss;   // device fp32 [n]
+};
+
+size_t ce_workspace_bytes(int64_t n);
+CeWorkspace ce_workspace_carve(void* base, int64_t n);
+
+hipError_t launch_label_prep(const int32_t* labels, int64_t n, int64_t v, int32_t ignore_index,
+                             long long* count_out, int32_t* status_out, hipStream_t stream);
+hipError_t launch_ce_fwd_rows(const uint16_t* logits, int64_t n, int64_t v, int64_t ld,
+                              const int32_t* labels, int32_t ignore_index, float* row_loss,
+                              float* lse_out, hipStream_t stream);
+hipError_t launch_loss_reduce(const float* row_loss, int64_t n, const long long* count_dev,
+                              long long count_host, float* loss_out, hipStream_t stream);
+hipError_t launch_ce_bwd_rows(const uint16_t* logits, int64_t ld, uint16_t* grad, int64_t ldg,
+                              int64_t n, int64_t v, const int32_t* labels, int32_t ignore_index,
+                              const float* lse, const long long* count_dev, long long count_host,
+                              const float* grad_output, hipStream_t stream);
+
+}  // namespace lce

@@ -1,0 +1,482 @@
+// Fused linear cross-entropy for gfx950: loss, grad_hidden, fp32 grad_weight and grad_bias
+// from hidden [n, h] and weight [v, h] without keeping the [n, v] logits.
+//
+// What is computed follows Liger-Kernel issue #533 ("Gradient checkpointing for grad_weight
+// in LFCE"), feature pitch: per chunk of rows the logits are input · weightᵀ, the CE
+// gradient of those logits is formed, and grad_weight collects (logits gradient)ᵀ · input;
+// and Liger-Kernel issue #941 ("No gain in VRAM usage with
+// LigerFusedLinearCrossEntropyLoss"): hidden, targets, lm_head weight and optional bias.
+// The CE part is the sum-reduced masked CE of NeMo Automodel PR #2996 (first commit
+// message).
+//
+// Schedule, per chunk of C rows (rows are processed chunk after chunk on one stream):
+//   1. logits GEMM   Z = H_c · Wᵀ + b  (bf16 MFMA, fp32 accumulate) → fp32 slice [C, ldz]
+//   2. row pass      lse_i, loss term lse_i − z_{i,y_i}
+//   3. bias pass     grad_bias += g·s·Σ_i (p_iv − [y_i = v])   (only when requested)
+//   4. convert       P = bf16(exp(Z − lse)) written in place over the fp32 slice: each
+//                    64-column group keeps its probabilities in the first half of the
+//                    bytes its fp32 logits occupied, so the slice is the only big buffer
+//   5. grad_hidden   dH_c = g·s·(P · W − W[y])     (bf16 MFMA over K = V; the one-hot
+//                    term is subtracted exactly in fp32 in the epilogue)
+//   6. grad_weight   dW (=|+=) g·s·Pᵀ · H_c         (bf16 MFMA over K = C)
+//   7. one-hot fix   dW[y] −= g·s·Σ_{i: y_i = y} h_i, in a fixed order (no atomics)
+// The probabilities enter the MFMA as unscaled bf16; the scale g·s and the one-hot are
+// applied in fp32, which keeps the fp32 grad_weight within 1e-4 normwise of the exact
+// result (scaling or subtracting inside the bf16 operand would not).
+#include "common.h"
+#include "flce.h"
+#include "lce_masked.h"
+
+namespace lce {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kGroup = 64;  // column-group width of the logits slice / probability layout
+
+__host__ __device__ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Row-major bf16 matrix view whose contiguous dimension is split into 64-wide groups placed
+// `gs` elements apart (gs == 64 is a plain dense matrix).
+struct View {
+  const uint16_t* p;
+  int64_t ld;    // elements between consecutive rows
+  int64_t gs;    // elements between consecutive 64-column groups
+  int64_t rows;  // valid rows
+  int64_t cols;  // valid columns
+  __device__ __forceinline__ const uint16_t* at(int64_t r, int64_t c) const {
+    return p + r * ld + (c >> 6) * gs + (c & 63);
+  }
+  // 8 consecutive columns starting at c (c % 8 == 0), zero outside the valid range.
+  __device__ __forceinline__ uint4 load8(int64_t r, int64_t c) const {
+    if (r < rows && c + 8 <= cols) return *reinterpret_cast<const uint4*>(at(r, c));
+    uint16_t e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = (r < rows && c + j < cols) ? *at(r, c + j) : uint16_t(0);
+    uint4 q;
+    q.x = uint32_t(e[0]) | (uint32_t(e[1]) << 16);
+    q.y = uint32_t(e[2]) | (uint32_t(e[3]) << 16);
+    q.z = uint32_t(e[4]) | (uint32_t(e[5]) << 16);
+    q.w = uint32_t(e[6]) | (uint32_t(e[7]) << 16);
+    return q;
+  }
+};
+
+__device__ __forceinline__ float flce_coef(const long long* count_dev, long long count_host,
+                                           const float* gout) {
+  const long long t = count_host >= 0 ? count_host : *count_dev;
+  const float g = gout ? *gout : 1.f;
+  return t > 0 ? float(double(g) / double(t)) : 0.f;
+}
+
+__device__ __forceinline__ bool has_label(int32_t y, int64_t v, int32_t ignore_index) {
+  return y != ignore_index && y >= 0 && int64_t(y) < v;
+}
+
+// ------------------------------------------------------------------ generic MFMA GEMM
+//
+// C[M, N] = Σ_k A(m, k) · B(k, n) on v_mfma_f32_16x16x32_bf16. A is K-major (row m holds
+// contiguous k) when AK, else M-major (row k holds contiguous m); likewise B with BK_.
+// 256 threads = 4 wavefronts in a 2 × 2 arrangement; both operands are staged in LDS
+// K-contiguous (an M/N-major operand is transposed on its way into LDS), so each lane feeds
+// the MFMA with one 16-byte LDS read per 16 × 32 fragment.
+template <int BM, int BN, int BKT, bool AK, bool BKM, class Epi>
+__global__ void __launch_bounds__(256) gemm_kernel(View A, View B, int64_t M, int64_t N,
+                                                   int64_t K, Epi epi) {
+  constexpr int PAD = 8;
+  constexpr int LDP = BKT + PAD;
+  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int TM = WTM / 16, TN = WTN / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[BM * LDP];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[BN * LDP];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t m0 = int64_t(blockIdx.y) * BM;
+  const int64_t n0 = int64_t(blockIdx.x) * BN;
+
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto stage = [&](const View& X, bool kmajor, int64_t r0, int64_t k0, uint16_t* s, int R) {
+    if (kmajor) {
+      const int vecs = R * (BKT / 8);
+      for (int e = tid; e < vecs; e += 256) {
+        const int r = e / (BKT / 8);
+        const int kv = (e % (BKT / 8)) * 8;
+        *reinterpret_cast<uint4*>(&s[r * LDP + kv]) = X.load8(r0 + r, k0 + kv);
+      }
+    } else {
+      const int vecs = BKT * (R / 8);
+      for (int e = tid; e < vecs; e += 256) {
+        const int k = e / (R / 8);
+        const int rv = (e % (R / 8)) * 8;
+        const uint4 q = X.load8(k0 + k, r0 + rv);
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          s[(rv + 2 * j) * LDP + k] = uint16_t(w[j] & 0xffffu);
+          s[(rv + 2 * j + 1) * LDP + k] = uint16_t(w[j] >> 16);
+        }
+      }
+    }
+  };
+
+  for (int64_t k0 = 0; k0 < K; k0 += BKT) {
+    __syncthreads();
+    stage(A, AK, m0, k0, sA, BM);
+    stage(B, BKM, n0, k0, sB, BN);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < BKT; ks += 32) {
+      bf16x8_t af[TM], bfr[TN];
+      const int kq = ks + 8 * (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(&sA[(wm * WTM + i * 16 + (lane & 15)) * LDP + kq]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&sB[(wn * WTN + j * 16 + (lane & 15)) * LDP + kq]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  epi.begin();
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t gm = m0 + wm * WTM + i * 16 + 4 * (lane >> 4) + q;
+        const int64_t gn = n0 + wn * WTN + j * 16 + (lane & 15);
+        if (gm < M && gn < N) epi(gm, gn, acc[i][j][q]);
+      }
+}
+
+// Z[m, n] = acc + bias[n] into the fp32 slice.
+struct EpiLogits {
+  float* z;
+  int64_t ldz;
+  const float* bias;
+  __device__ void begin() {}
+  __device__ __forceinline__ void operator()(int64_t m, int64_t n, float a) {
+    z[m * ldz + n] = bias ? a + bias[n] : a;
+  }
+};
+
+// dH[m, n] = coef · (acc − W[y_m, n]) for labelled rows, 0 otherwise; bf16 out.
+struct EpiGradHidden {
+  uint16_t* dh;
+  int64_t ldh;
+  const int32_t* labels;  // chunk rows
+  const uint16_t* w;
+  int64_t ldw, v;
+  int32_t ignore_index;
+  const long long* count_dev;
+  long long count_host;
+  const float* gout;
+  float coef;
+  __device__ void begin() { coef = flce_coef(count_dev, count_host, gout); }
+  __device__ __forceinline__ void operator()(int64_t m, int64_t n, float a) {
+    const int32_t y = labels[m];
+    float r = 0.f;
+    if (has_label(y, v, ignore_index)) r = coef * (a - bf16_to_f32(w[int64_t(y) * ldw + n]));
+    dh[m * ldh + n] = f32_to_bf16(r);
+  }
+};
+
+// dW[m, n] = (overwrite ? 0 : dW[m, n]) + coef · acc.
+struct EpiGradWeight {
+  float* dw;
+  int64_t ldw;
+  int overwrite;
+  const long long* count_dev;
+  long long count_host;
+  const float* gout;
+  float coef;
+  __device__ void begin() { coef = flce_coef(count_dev, count_host, gout); }
+  __device__ __forceinline__ void operator()(int64_t m, int64_t n, float a) {
+    float* p = dw + m * ldw + n;
+    *p = overwrite ? coef * a : *p + coef * a;
+  }
+};
+
+// ------------------------------------------------------------------ row / column passes
+
+constexpr int kRowThreads = 256;
+
+// lse of one fp32 slice row; loss term and lse written for labelled rows.
+__global__ void __launch_bounds__(kRowThreads) slice_row_lse_kernel(
+    const float* __restrict__ z, int64_t ldz, int64_t v, const int32_t* __restrict__ labels,
+    int32_t ignore_index, float* __restrict__ lse_c, float* __restrict__ row_loss,
+    float* __restrict__ lse_out) {
+  const int64_t i = blockIdx.x;
+  const int32_t y = labels[i];
+  if (!has_label(y, v, ignore_index)) {
+    if (threadIdx.x == 0) {
+      lse_c[i] = 0.f;
+      row_loss[i] = 0.f;
+      if (lse_out) lse_out[i] = 0.f;
+    }
+    return;
+  }
+  const float* row = z + i * ldz;
+  float m = -INFINITY, s = 0.f;
+  for (int64_t c = threadIdx.x; c < v; c += kRowThreads) {
+    const float x = row[c];
+    const float mn = fmaxf(m, x);
+    s = (mn == m ? s : s * fast_exp2((m - mn) * kLog2e)) + fast_exp2((x - mn) * kLog2e);
+    m = mn;
+  }
+  __shared__ float sm[kRowThreads / 64], ss[kRowThreads / 64];
+  wave_lse_reduce(m, s);
+  if ((threadIdx.x & 63) == 0) {
+    sm[threadIdx.x >> 6] = m;
+    ss[threadIdx.x >> 6] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float mm = sm[0], sss = ss[0];
+    for (int w = 1; w < kRowThreads / 64; ++w) lse_merge(mm, sss, sm[w], ss[w]);
+    const float lse = mm + fast_log2(sss) * kLn2;
+    lse_c[i] = lse;
+    row_loss[i] = lse - row[y];
+    if (lse_out) lse_out[i] = lse;
+  }
+}
+
+// grad_bias[v] (=|+=) coef · (Σ_{labelled i} p_iv − #{i: y_i = v}) from the fp32 slice.
+__global__ void __launch_bounds__(256) slice_bias_grad_kernel(
+    const float* __restrict__ z, int64_t ldz, int64_t rows, int64_t v,
+    const int32_t* __restrict__ labels, int32_t ignore_index, const float* __restrict__ lse_c,
+    float* __restrict__ grad_bias, int overwrite, const long long* count_dev,
+    long long count_host, const float* gout) {
+  const int64_t col = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (col >= v) return;
+  float sp = 0.f;
+  int cnt = 0;
+  for (int64_t i = 0; i < rows; ++i) {
+    const int32_t y = labels[i];
+    if (!has_label(y, v, ignore_index)) continue;
+    sp += fast_exp2((z[i * ldz + col] - lse_c[i]) * kLog2e);
+    cnt += (int64_t(y) == col);
+  }
+  const float coef = flce_coef(count_dev, count_host, gout);
+  const float d = coef * (sp - float(cnt));
+  grad_bias[col] = overwrite ? d : grad_bias[col] + d;
+}
+
+// In place: the fp32 logits of row i, column group g (bytes [256 g, 256 g + 256) of the row)
+// become 64 bf16 probabilities in the group's first 128 bytes. One wavefront owns one
+// group, and each lane's store depends on its own load, so no lane can overwrite bytes
+// another lane has yet to read.
+__global__ void __launch_bounds__(256) slice_to_probs_kernel(float* z, int64_t ldz, int64_t v,
+                                                             const int32_t* __restrict__ labels,
+                                                             int32_t ignore_index,
+                                                             const float* __restrict__ lse_c) {
+  const int64_t i = blockIdx.y;
+  const int64_t g = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t groups = ldz / kGroup;
+  if (g >= groups) return;
+  const int32_t y = labels[i];
+  const bool ok = has_label(y, v, ignore_index);
+  const int64_t col = g * kGroup + lane;
+  float* row = z + i * ldz;
+  const float x = row[col];
+  float p = 0.f;
+  if (ok && col < v) p = fast_exp2((x - lse_c[i]) * kLog2e);
+  uint16_t* out = reinterpret_cast<uint16_t*>(row) + g * (2 * kGroup) + lane;
+  *out = f32_to_bf16(p);
+}
+
+// dW[y] −= coef · Σ_{i in chunk, y_i = y} h_i. The first chunk row carrying label y owns that
+// dW row and adds the matching hidden rows in increasing row order.
+__global__ void __launch_bounds__(256) onehot_weight_fix_kernel(
+    const uint16_t* __restrict__ hidden, int64_t h, int64_t rows,
+    const int32_t* __restrict__ labels, int32_t ignore_index, int64_t v, float* grad_weight,
+    const long long* count_dev, long long count_host, const float* gout) {
+  const int64_t i = blockIdx.x;
+  const int32_t y = labels[i];
+  if (!has_label(y, v, ignore_index)) return;
+  __shared__ int earlier;
+  __shared__ int nmatch;
+  __shared__ int match[1024];
+  if (threadIdx.x == 0) earlier = 0;
+  __syncthreads();
+  for (int64_t j = threadIdx.x; j < i; j += 256)
+    if (labels[j] == y) earlier = 1;
+  __syncthreads();
+  if (earlier) return;
+  const float coef = flce_coef(count_dev, count_host, gout);
+  // Rows j >= i with the same label, gathered in increasing order, 1024 at a time.
+  for (int64_t base = i; base < rows; base += 1024) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int c = 0;
+      const int64_t end = base + 1024 < rows ? base + 1024 : rows;
+      for (int64_t j = base; j < end; ++j)
+        if (labels[j] == y) match[c++] = int(j - base);
+      nmatch = c;
+    }
+    __syncthreads();
+    const int cnt = nmatch;
+    if (cnt == 0) continue;
+    for (int64_t col = threadIdx.x; col < h; col += 256) {
+      float acc = 0.f;
+      for (int k = 0; k < cnt; ++k) acc += bf16_to_f32(hidden[(base + match[k]) * h + col]);
+      grad_weight[int64_t(y) * h + col] -= coef * acc;
+    }
+  }
+}
+
+__global__ void fill_zero_f32(float* p, int64_t count) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < count;
+       i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = 0.f;
+}
+
+struct FlceWs {
+  long long* count;
+  float* row_loss;  // [n]
+  float* lse_c;     // [C]
+  float* slice;     // [C, ldz] fp32
+  int64_t ldz;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+FlceWs flce_carve(void* base, int64_t n, int64_t v, int64_t chunk) {
+  char* b = static_cast<char*>(base);
+  FlceWs w;
+  w.count = reinterpret_cast<long long*>(b);
+  size_t off = 256;
+  w.row_loss = reinterpret_cast<float*>(b + off);
+  off += align256(size_t(n) * 4);
+  w.lse_c = reinterpret_cast<float*>(b + off);
+  off += align256(size_t(chunk) * 4);
+  w.slice = reinterpret_cast<float*>(b + off);
+  w.ldz = round_up(v, kGroup);
+  return w;
+}
+
+template <int BM, int BN, bool AK, bool BKM, class Epi>
+hipError_t launch_gemm(const View& A, const View& B, int64_t M, int64_t N, int64_t K,
+                       const Epi& epi, hipStream_t s) {
+  const dim3 grid(unsigned((N + BN - 1) / BN), unsigned((M + BM - 1) / BM));
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, 64, AK, BKM, Epi>), grid, dim3(256), 0, s, A, B, M,
+                     N, K, epi);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int flce_check_shape(int64_t n, int64_t h, int64_t v, int64_t chunk_size, uint32_t flags) {
+  if (flags & ~(FLCE_RECOMPUTE | FLCE_ACCUMULATE)) return LCE_ERR_BAD_FLAGS;
+  if (n < 0 || h < 1 || v < 1 || (h % 8) != 0) return LCE_ERR_BAD_SHAPE;
+  if (n > (int64_t(1) << 31) - 1 || v > (int64_t(1) << 31) - 1) return LCE_ERR_BAD_SHAPE;
+  if (h > (int64_t(1) << 20)) return LCE_ERR_BAD_SHAPE;
+  if (chunk_size <= 0) return LCE_ERR_BAD_CHUNK;
+  return LCE_OK;
+}
+
+size_t flce_workspace_bytes(int64_t n, int64_t h, int64_t v, int64_t chunk_size, uint32_t flags) {
+  (void)h;
+  (void)flags;
+  const int64_t c = chunk_size < n ? chunk_size : (n > 0 ? n : 1);
+  const int64_t ldz = round_up(v, kGroup);
+  return 256 + align256(size_t(n) * 4) + align256(size_t(c) * 4) +
+         align256(size_t(c) * size_t(ldz) * 4);
+}
+
+hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
+  const int64_t n = a.n, h = a.h, v = a.v;
+  const int64_t chunk = a.chunk_size < n ? a.chunk_size : (n > 0 ? n : 1);
+  FlceWs ws = flce_carve(a.workspace, n, v, chunk);
+  const long long th = a.num_label_tokens >= 0 ? a.num_label_tokens : -1;
+  const bool accumulate = (a.flags & FLCE_ACCUMULATE) != 0;
+  hipError_t e;
+
+  if ((e = launch_label_prep(a.labels, n, v, a.ignore_index, ws.count, a.status_out, s)) != hipSuccess)
+    return e;
+  if (n == 0 && !accumulate) {
+    if (a.grad_weight) {
+      hipLaunchKernelGGL(fill_zero_f32, dim3(1024), dim3(256), 0, s, a.grad_weight, v * h);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (a.grad_bias) {
+      hipLaunchKernelGGL(fill_zero_f32, dim3(64), dim3(256), 0, s, a.grad_bias, v);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+
+  for (int64_t c0 = 0; c0 < n; c0 += chunk) {
+    const int64_t rows = (n - c0) < chunk ? (n - c0) : chunk;
+    const bool first = c0 == 0;
+    const int32_t* lab = a.labels + c0;
+    const uint16_t* hid = a.hidden + c0 * h;
+
+    // 1. logits slice
+    View Ah{hid, h, kGroup, rows, h};
+    View Bw{a.weight, h, kGroup, v, h};
+    EpiLogits el{ws.slice, ws.ldz, a.bias};
+    if ((e = launch_gemm<64, 64, true, true>(Ah, Bw, rows, v, h, el, s)) != hipSuccess) return e;
+
+    // 2. row logsumexp and loss terms
+    hipLaunchKernelGGL(slice_row_lse_kernel, dim3(unsigned(rows)), dim3(kRowThreads), 0, s,
+                       ws.slice, ws.ldz, v, lab, a.ignore_index, ws.lse_c, ws.row_loss + c0,
+                       a.lse_out ? a.lse_out + c0 : nullptr);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    // 3. bias gradient from the fp32 logits
+    if (a.grad_bias) {
+      hipLaunchKernelGGL(slice_bias_grad_kernel, dim3(unsigned((v + 255) / 256)), dim3(256), 0, s,
+                         ws.slice, ws.ldz, rows, v, lab, a.ignore_index, ws.lse_c, a.grad_bias,
+                         int(first && !accumulate), ws.count, th, a.grad_output);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (!a.grad_hidden && !a.grad_weight) continue;
+
+    // 4. probabilities in place
+    const int64_t groups = ws.ldz / kGroup;
+    hipLaunchKernelGGL(slice_to_probs_kernel, dim3(unsigned((groups + 3) / 4), unsigned(rows)),
+                       dim3(256), 0, s, ws.slice, ws.ldz, v, lab, a.ignore_index, ws.lse_c);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const uint16_t* P = reinterpret_cast<const uint16_t*>(ws.slice);
+    const int64_t p_ld = 2 * ws.ldz, p_gs = 2 * kGroup;
+
+    // 5. grad_hidden = coef (P W − W[y])
+    if (a.grad_hidden) {
+      View Ap{P, p_ld, p_gs, rows, v};
+      View Bw2{a.weight, h, kGroup, v, h};  // rows = k (vocab), cols = n (hidden)
+      EpiGradHidden eh{a.grad_hidden + c0 * h, h, lab, a.weight, h, v, a.ignore_index,
+                       ws.count, th, a.grad_output, 0.f};
+      if ((e = launch_gemm<64, 64, true, false>(Ap, Bw2, rows, h, v, eh, s)) != hipSuccess) return e;
+    }
+    // 6./7. grad_weight
+    if (a.grad_weight) {
+      View Apt{P, p_ld, p_gs, rows, v};        // rows = k (chunk row), cols = m (vocab)
+      View Bh{hid, h, kGroup, rows, h};       // rows = k, cols = n
+      EpiGradWeight ew{a.grad_weight, h, int(first && !accumulate), ws.count, th, a.grad_output, 0.f};
+      if ((e = launch_gemm<64, 64, false, false>(Apt, Bh, v, h, rows, ew, s)) != hipSuccess) return e;
+      hipLaunchKernelGGL(onehot_weight_fix_kernel, dim3(unsigned(rows)), dim3(256), 0, s, hid, h,
+                         rows, lab, a.ignore_index, v, a.grad_weight, ws.count, th, a.grad_output);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  return launch_loss_reduce(ws.row_loss, n, ws.count, th, a.loss_out, s);
+}
+
+}  // namespace lce

@@ -1,0 +1,147 @@
+"""CPU checks of the C-ABI library: it loads, exports every declared symbol, and rejects bad
+arguments with the documented status codes before touching the GPU (no kernel is launched)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import linear_cross_entropy_masked_amd as lce
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, NULL_ARG, BAD_SHAPE, BAD_CHUNK, WORKSPACE, HIP, DEVICE, BAD_FLAGS, ALIGN = range(9)
+
+
+def _declared_functions():
+    names = []
+    for path in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(lce.library_path()):
+        pytest.skip("library not built")
+    return lce.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert {"ce_chunked_fwd", "ce_chunked_bwd_inplace", "flce_fwd_bwd"} <= set(names)
+    raw = ctypes.CDLL(lce.library_path())
+    for n in names:
+        assert hasattr(raw, n), f"{n} declared in include/ but not exported"
+
+
+def test_status_strings(lib):
+    for code in range(9):
+        assert lce.lce_status_str(code)
+    assert lce.lce_status_str(0) == "ok"
+    assert "unknown" in lce.lce_status_str(12345)
+
+
+def _ws(n, v, c):
+    out = ctypes.c_size_t()
+    rc = lce.load_library().ce_chunked_workspace_size(n, v, c, ctypes.byref(out))
+    return rc, out.value
+
+
+def test_ce_workspace_size_is_small_and_validated(lib):
+    rc, b = _ws(16384, 128256, 1024)
+    assert rc == OK
+    # O(n): no fp32 [chunk, V] slice is ever allocated by the CE layer
+    assert b <= 256 + 16384 * 4 + 256
+    assert _ws(-1, 10, 4)[0] == BAD_SHAPE
+    assert _ws(10, 0, 4)[0] == BAD_SHAPE
+    assert _ws(10, 10, 0)[0] == BAD_CHUNK
+    assert lib.ce_chunked_workspace_size(10, 10, 4, None) == NULL_ARG
+
+
+FAKE = 0x10000  # a 256-aligned non-null address; never dereferenced (validation fails first)
+
+
+def _fwd(n=4, v=8, ld=8, logits=FAKE, labels=FAKE, chunk=2, loss=FAKE, ws=FAKE, wsb=1 << 20,
+         lse=None):
+    return lce.load_library().ce_chunked_fwd(logits, n, v, ld, labels, -100, chunk, -1, loss, lse,
+                                             None, ws, wsb, None)
+
+
+def test_ce_fwd_argument_errors(lib):
+    assert _fwd(n=-1) == BAD_SHAPE
+    assert _fwd(v=0) == BAD_SHAPE
+    assert _fwd(ld=7) == BAD_SHAPE
+    assert _fwd(n=1 << 40, ld=1 << 30, v=8) == BAD_SHAPE
+    assert _fwd(chunk=0) == BAD_CHUNK
+    assert _fwd(chunk=-3) == BAD_CHUNK
+    assert _fwd(logits=None) == NULL_ARG
+    assert _fwd(labels=None) == NULL_ARG
+    assert _fwd(loss=None) == NULL_ARG
+    assert _fwd(ws=None) == WORKSPACE
+    assert _fwd(wsb=16) == WORKSPACE
+    assert _fwd(logits=FAKE + 1) == ALIGN
+    assert _fwd(labels=FAKE + 2) == ALIGN
+    assert _fwd(lse=FAKE + 2) == ALIGN
+
+
+def test_ce_bwd_argument_errors(lib):
+    f = lib.ce_chunked_bwd
+    assert f(FAKE, 4, 8, 8, FAKE, 7, FAKE, -100, 2, -1, None, None, None, FAKE, 1 << 20, None) == BAD_SHAPE
+    assert f(FAKE, 4, 8, 8, None, 8, FAKE, -100, 2, -1, None, None, None, FAKE, 1 << 20, None) == NULL_ARG
+    assert f(FAKE, 4, 8, 8, FAKE, 8, FAKE, -100, 0, -1, None, None, None, FAKE, 1 << 20, None) == BAD_CHUNK
+    g = lib.ce_chunked_bwd_inplace
+    assert g(None, 4, 8, 8, FAKE, -100, 2, -1, None, None, None, FAKE, 1 << 20, None) == NULL_ARG
+    assert g(FAKE, 4, 8, 8, FAKE, -100, 2, -1, None, None, None, FAKE, 8, None) == WORKSPACE
+
+
+def _fws(n, h, v, c, flags=0):
+    out = ctypes.c_size_t()
+    rc = lce.load_library().flce_workspace_size(n, h, v, c, flags, ctypes.byref(out))
+    return rc, out.value
+
+
+def test_flce_workspace_is_one_slice_plus_bookkeeping(lib):
+    # The fp32 working set of one chunk is chunk * V * 4 bytes. Liger-Kernel issue #941's
+    # reply works the same arithmetic for 2 x 1024 rows of V = 32768 fp32 logits: 256 MiB.
+    rc, b = _fws(2048, 768, 32768, 2048)
+    assert rc == OK
+    slice_bytes = 2 * 1024 * 32768 * 4
+    assert slice_bytes == 256 * 1024 * 1024
+    assert slice_bytes <= b <= slice_bytes + 2 * 1024 * 1024
+    # chunking bounds it independently of n
+    rc, b2 = _fws(1 << 20, 4096, 128256, 1024)
+    assert rc == OK and b2 < 1024 * 128320 * 4 + 1 * 1024 * 1024 * 8
+    rc, b3 = _fws(8192, 4096, 128256, 1024, lce.FLCE_RECOMPUTE)
+    assert rc == OK
+
+
+def test_flce_argument_errors(lib):
+    assert _fws(10, 12, 100, 4)[0] == BAD_SHAPE       # h not a multiple of 8
+    assert _fws(10, 0, 100, 4)[0] == BAD_SHAPE
+    assert _fws(10, 16, 0, 4)[0] == BAD_SHAPE
+    assert _fws(-1, 16, 10, 4)[0] == BAD_SHAPE
+    assert _fws(10, 16, 10, 0)[0] == BAD_CHUNK
+    assert _fws(10, 16, 10, 4, 8)[0] == BAD_FLAGS
+    f = lib.flce_fwd_bwd
+    args = dict(hidden=FAKE, weight=FAKE, bias=None, labels=FAKE, n=4, h=16, v=10, ign=-100,
+                chunk=2, t=-1, flags=0, gout=None, loss=FAKE, lse=None, gh=None, gw=None, gb=None,
+                status=None, ws=FAKE, wsb=1 << 22, stream=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(*a.values())
+
+    assert call(weight=None) == NULL_ARG
+    assert call(loss=None) == NULL_ARG
+    assert call(gb=FAKE) == NULL_ARG                 # grad_bias without a bias
+    assert call(flags=4) == BAD_FLAGS
+    assert call(chunk=0) == BAD_CHUNK
+    assert call(h=12) == BAD_SHAPE
+    assert call(ws=None) == WORKSPACE
+    assert call(wsb=64) == WORKSPACE
+    assert call(hidden=FAKE + 8) == ALIGN
+    assert call(gw=FAKE + 4) == ALIGN

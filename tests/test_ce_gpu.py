@@ -1,0 +1,189 @@
+"""GPU parity of the chunked masked CE kernels against the fp64 oracle (through the C ABI).
+
+Bars (loss: relative 1e-5; every gradient element within one bf16 ulp of the exact fp64
+value, which also implies the stated absolute 2e-3; ignored rows exactly zero).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import linear_cross_entropy_masked_amd as lce
+import oracle
+from workloads import WORKLOADS, make_ce_inputs, random_ce
+
+from _helpers import (assert_close_rel, assert_faithful_bf16, bits_to_device, device_to_f64,
+                      gpu_device, oracle_ce_rows_parallel)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return gpu_device()
+
+
+def run_ce(dev, bits, labels, chunk=16, count=None, inplace=True, g=None, save_lse=True, ld=None):
+    n, v = bits.shape
+    if ld is None or ld == v:
+        logits = bits_to_device(bits, dev)
+    else:  # rows ld elements apart
+        buf = torch.zeros((n, ld), dtype=torch.bfloat16, device=dev)
+        buf[:, :v] = bits_to_device(bits, dev)
+        logits = buf[:, :v]
+    lab = torch.from_numpy(labels.astype(np.int32)).to(dev)
+    status = torch.full((), -1, dtype=torch.int32, device=dev)
+    loss, lse = lce.ce_chunked_fwd(logits, lab, chunk_size=chunk, num_label_tokens=count,
+                                   return_lse=save_lse, status=status)
+    gout = None if g is None else torch.tensor(g, dtype=torch.float32, device=dev)
+    if inplace:
+        grad = lce.ce_chunked_bwd_inplace(logits, lab, chunk_size=chunk, num_label_tokens=count,
+                                          grad_output=gout, lse=lse)
+        assert grad.data_ptr() == logits.data_ptr()
+    else:
+        grad = lce.ce_chunked_bwd(logits, lab, chunk_size=chunk, num_label_tokens=count,
+                                  grad_output=gout, lse=lse)
+    torch.cuda.synchronize()
+    return (float(loss.item()), None if lse is None else lse.cpu().numpy(), grad,
+            int(status.item()), logits)
+
+
+def check_against_oracle(bits, labels, loss, lse, grad, count=None, g=1.0):
+    z = oracle.bf16_bits_to_f64(bits)
+    ref = oracle.ce_masked_sum(z, labels, num_label_tokens=count, grad_output=g)
+    assert_close_rel(loss, ref.loss, 1e-5)
+    got = device_to_f64(grad)
+    assert_faithful_bf16(got, ref.grad)
+    assert np.max(np.abs(got - ref.grad), initial=0.0) <= 2e-3
+    ok, _ = oracle.labelled_rows(labels, bits.shape[1])
+    assert not got[~ok].any(), "rows without a label must be exactly zero"
+    if lse is not None and ok.any():
+        d = np.abs(lse[ok] - ref.lse[ok])
+        assert np.all(d <= 2e-6 * np.maximum(1.0, np.abs(ref.lse[ok])))
+        assert not lse[~ok].any()
+    return ref
+
+
+def test_small_workload_parity_in_place(dev):
+    w = WORKLOADS["ce_64x1000"]
+    inp = make_ce_inputs(w, seed=0)
+    loss, lse, grad, status, _ = run_ce(dev, inp.logits, inp.labels, chunk=w.chunk_size)
+    assert status == 0
+    ref = check_against_oracle(inp.logits, inp.labels, loss, lse, grad)
+    assert ref.count == 58
+
+
+@pytest.mark.parametrize("n,v", [(1, 1), (3, 2), (5, 7), (17, 1000), (33, 32777), (6, 128256),
+                                 (300, 517), (64, 8), (9, 9)])
+def test_edge_shapes(dev, n, v):
+    inp = random_ce(n, v, sigma=2.5, ignore_frac=0.2, seed=n * 7 + v)
+    loss, lse, grad, status, _ = run_ce(dev, inp.logits, inp.labels, chunk=5)
+    assert status == 0
+    check_against_oracle(inp.logits, inp.labels, loss, lse, grad)
+
+
+@pytest.mark.parametrize("ld_extra", [1, 3, 8, 13])
+def test_row_stride_larger_than_v(dev, ld_extra):
+    n, v = 21, 777
+    inp = random_ce(n, v, seed=ld_extra)
+    loss, lse, grad, _, _ = run_ce(dev, inp.logits, inp.labels, chunk=4, ld=v + ld_extra)
+    check_against_oracle(inp.logits, inp.labels, loss, lse, grad)
+
+
+def test_empty_input(dev):
+    bits = np.zeros((0, 10), dtype=np.uint16)
+    labels = np.zeros(0, dtype=np.int32)
+    loss, lse, grad, status, _ = run_ce(dev, bits, labels, chunk=4)
+    assert loss == 0.0 and grad.numel() == 0 and status == 0
+
+
+def test_out_of_place_leaves_logits_and_matches_in_place(dev):
+    inp = random_ce(40, 3001, seed=11)
+    l1, _, g_in, _, _ = run_ce(dev, inp.logits, inp.labels, inplace=True)
+    l2, _, g_out, _, logits = run_ce(dev, inp.logits, inp.labels, inplace=False)
+    assert l1 == l2
+    assert torch.equal(g_in, g_out)
+    np.testing.assert_array_equal(
+        logits.view(torch.int16).cpu().numpy().view(np.uint16), inp.logits)
+
+
+def test_recomputed_lse_matches_saved(dev):
+    inp = random_ce(50, 4099, sigma=3.0, seed=12)
+    _, _, g_saved, _, _ = run_ce(dev, inp.logits, inp.labels, save_lse=True)
+    _, _, g_recomp, _, _ = run_ce(dev, inp.logits, inp.labels, save_lse=False)
+    assert torch.equal(g_saved, g_recomp)
+
+
+def test_zero_count_guard_and_all_ignored(dev):
+    inp = random_ce(12, 300, seed=13, ignore_frac=0.0)
+    loss, _, grad, _, _ = run_ce(dev, inp.logits, inp.labels, count=0)
+    assert loss == 0.0 and not grad.any().item()
+    labels = np.full(12, -100, dtype=np.int32)
+    loss, _, grad, status, _ = run_ce(dev, inp.logits, labels)
+    assert loss == 0.0 and not grad.any().item() and status == 0
+
+
+def test_caller_normaliser_and_upstream_grad(dev):
+    inp = random_ce(70, 2048, seed=14)
+    loss, lse, grad, _, _ = run_ce(dev, inp.logits, inp.labels, count=1234, g=0.37)
+    check_against_oracle(inp.logits, inp.labels, loss, lse, grad, count=1234, g=0.37)
+
+
+def test_chunk_size_invariance(dev):
+    inp = random_ce(97, 5003, sigma=3.0, seed=15)
+    base = None
+    for chunk in (1, 7, 16, 1000, 97, 10_000):
+        loss, _, grad, _, _ = run_ce(dev, inp.logits, inp.labels, chunk=chunk)
+        if base is None:
+            base = (loss, grad)
+        else:
+            assert loss == base[0]
+            assert torch.equal(grad, base[1])
+
+
+def test_bitwise_repeatable(dev):
+    inp = random_ce(64, 32777, sigma=3.0, seed=16)
+    runs = [run_ce(dev, inp.logits, inp.labels) for _ in range(3)]
+    for r in runs[1:]:
+        assert r[0] == runs[0][0]
+        assert torch.equal(r[2], runs[0][2])
+
+
+def test_out_of_range_labels_flagged_and_ignored(dev):
+    inp = random_ce(10, 100, seed=17, ignore_frac=0.0)
+    labels = inp.labels.copy()
+    labels[2] = 100
+    labels[5] = -7
+    loss, lse, grad, status, _ = run_ce(dev, inp.logits, labels)
+    assert status & lce.LCE_STATUS_BAD_LABEL
+    ref = check_against_oracle(inp.logits, labels, loss, lse, grad)
+    assert ref.bad_label and ref.count == 8
+
+
+@pytest.mark.timeout(600)
+def test_large_vocab_workload_full_size(dev):
+    """[16384, 128256] in the launch configuration the benchmark times: full loss and every
+    row's lse against the oracle, plus the complete gradient of sampled rows."""
+    w = WORKLOADS["ce_16384x128256"]
+    inp = make_ce_inputs(w, seed=0)
+    labels = inp.labels
+    count = int((labels != -100).sum())
+    assert count == 15565
+    loss, lse, grad, status, _ = run_ce(dev, inp.logits, labels, chunk=w.chunk_size)
+    assert status == 0
+    row_loss, ref_lse = oracle_ce_rows_parallel(inp.logits, labels, count)
+    assert_close_rel(loss, math.fsum(row_loss) / count, 1e-5)
+    ok = labels != -100
+    assert np.all(np.abs(lse[ok] - ref_lse[ok]) <= 2e-6 * np.abs(ref_lse[ok]))
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([
+        [0, w.n - 1], rng.choice(w.n, 24, replace=False), inp.draw.spike_rows[:8],
+        inp.draw.ignored_rows[:4]]))
+    got = device_to_f64(grad[torch.from_numpy(rows).to(dev)])
+    for k, r in enumerate(rows):
+        z = oracle.bf16_bits_to_f64(inp.logits[r:r + 1])
+        one = oracle.ce_masked_sum(z, labels[r:r + 1], num_label_tokens=count)
+        assert_faithful_bf16(got[k:k + 1], one.grad, what=f"grad row {r}")
+        if labels[r] == -100:
+            assert not got[k].any()
