@@ -1,0 +1,339 @@
+#!/usr/bin/env python3
+"""Benchmark of the masked cross-entropy hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step is one forward+backward pass of each layer of the hot path over one batch of seeded
+synthetic input already resident in HBM:
+  * fused linear CE on the Llama3-8B-shaped head: hidden [8192, 4096] bf16, weight
+    [128256, 4096] bf16, no bias, 5% ignored labels, chunk 1024 (loss, grad_hidden, fp32
+    grad_weight) — this is `value` (tokens/s), with the bf16 MFMA roofline;
+  * chunked masked CE on [16384, 128256] bf16 logits (spiked labels, 5% ignored, chunk 1024,
+    in-place backward) — reported under "ce_only" with its HBM roofline.
+
+Prints one JSON line. Timing uses hipEvents recorded on the stream the library launches on;
+the in-place CE backward destroys its input, so the logits are restored from a pristine copy
+between steps, outside the timed events.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "FLCE fwd+bwd tokens/s (H4096,V128256) % MFMA peak; CE-only HBM GB/s % peak"
+
+FLCE_WORKLOAD = "flce_8192x4096x128256"
+CE_WORKLOAD = "ce_16384x128256"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "linear_cross_entropy_masked_amd", "csrc")
+
+
+def source_digest() -> str:
+    """Hash of the HIP sources: stored HBM-traffic counters are only valid for this digest."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if still current."""
+    path = os.path.join(PROFILE_DIR, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        table = json.load(f)
+    rec = table.get(f"{kernel}@{workload}")
+    if not rec or rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def ce_algorithmic_bytes(n, v, nvalid):
+    """Bytes the method must move: forward reads each labelled row once; the in-place backward
+    reads each labelled row and writes every row (ignored rows are zero-filled)."""
+    fwd = nvalid * v * 2
+    bwd_read = nvalid * v * 2
+    bwd_write = n * v * 2
+    return fwd, bwd_read + bwd_write
+
+
+def run_flce(args, torch, lce, workloads):
+    w = workloads.WORKLOADS[FLCE_WORKLOAD]
+    t0 = time.time()
+    inp = workloads.make_flce_inputs(w, seed=0)
+    gen_s = time.time() - t0
+    dev = torch.device("cuda:0")
+    import numpy as np
+    hid = torch.from_numpy(inp.hidden.view(np.int16)).view(torch.bfloat16).to(dev)
+    wt = torch.from_numpy(inp.weight.view(np.int16)).view(torch.bfloat16).to(dev)
+    lab = torch.from_numpy(inp.labels).to(dev)
+    gh = torch.empty((w.n, w.h), dtype=torch.bfloat16, device=dev)
+    gw = torch.empty((w.v, w.h), dtype=torch.float32, device=dev)
+    ws = torch.empty(lce.flce_workspace_size(w.n, w.h, w.v, w.chunk_size, 0), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev)
+    nvalid = int((inp.labels != -100).sum())
+
+    def step():
+        return lce.flce_fwd_bwd(hid, wt, lab, None, chunk_size=w.chunk_size, grad_hidden=gh,
+                                grad_weight=gw, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    mem_before = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        loss = step()[0]
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    peak_extra = torch.cuda.max_memory_allocated(dev) - mem_before + ws.numel()
+
+    # per-kernel breakdown (separate pass: events around every launch)
+    lce.lce_timing_enable(True)
+    lce.lce_timing_read()
+    kreps = max(1, min(3, args.steps))
+    for _ in range(kreps):
+        step()
+    torch.cuda.synchronize()
+    kernels = lce.lce_timing_read()
+    lce.lce_timing_enable(False)
+
+    flops = 6.0 * w.n * w.h * w.v
+    chunks = -(-w.n // w.chunk_size)
+    gemm_flops_per_launch = 2.0 * w.chunk_size * w.h * w.v  # every chunk is full here
+    gemms = [k for k in kernels if k[0].startswith("flce_gemm")]
+    dom = max(gemms, key=lambda k: k[1]) if gemms else None
+    roof = None
+    if dom:
+        avg_ms = dom[1] / dom[2]
+        achieved = gemm_flops_per_launch / (avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": dom[0], "achieved": round(achieved, 2),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "avg_launch_ms": round(avg_ms, 4),
+                "traffic": stored_traffic(dom[0], FLCE_WORKLOAD)}
+    return {
+        "workload": w, "ms": ms, "wall_s": wall, "tokens_per_s": w.n / (ms * 1e-3),
+        "tflops": flops / (ms * 1e-3) / 1e12, "loss": float(loss.item()), "roofline": roof,
+        "kernels": {k[0]: {"ms_per_step": round(k[1] / kreps, 4), "launches_per_step": k[2] // kreps}
+                    for k in kernels},
+        "peak_extra_bytes": int(peak_extra), "slice_budget_bytes": int(w.chunk_size * w.v * 4),
+        "nvalid": nvalid, "gen_s": gen_s, "chunks": chunks, "inputs": inp,
+    }
+
+
+def run_ce(args, torch, lce, workloads):
+    import numpy as np
+    w = workloads.WORKLOADS[CE_WORKLOAD]
+    t0 = time.time()
+    inp = workloads.make_ce_inputs(w, seed=0)
+    gen_s = time.time() - t0
+    dev = torch.device("cuda:0")
+    pristine = torch.from_numpy(inp.logits.view(np.int16)).view(torch.bfloat16).to(dev)
+    logits = torch.empty_like(pristine)
+    lab = torch.from_numpy(inp.labels).to(dev)
+    ws = torch.empty(lce.ce_chunked_workspace_size(w.n, w.v, w.chunk_size), dtype=torch.uint8,
+                     device=dev)
+    lse = torch.empty(w.n, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    nvalid = int((inp.labels != -100).sum())
+    fwd_bytes, bwd_bytes = ce_algorithmic_bytes(w.n, w.v, nvalid)
+
+    def step(timed):
+        logits.copy_(pristine)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if timed else None
+        if timed:
+            e[0].record(stream)
+        loss, l = lce.ce_chunked_fwd(logits, lab, chunk_size=w.chunk_size, workspace=ws)
+        if timed:
+            e[1].record(stream)
+        lce.ce_chunked_bwd_inplace(logits, lab, chunk_size=w.chunk_size, lse=l, workspace=ws)
+        if timed:
+            e[2].record(stream)
+        return loss, e
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    evs = []
+    wall0 = time.perf_counter()
+    for _ in range(args.steps):
+        loss, e = step(True)
+        evs.append(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ms = fwd_ms + bwd_ms
+
+    lce.lce_timing_enable(True)
+    lce.lce_timing_read()
+    kreps = max(1, min(3, args.steps))
+    for _ in range(kreps):
+        step(False)
+    torch.cuda.synchronize()
+    kernels = lce.lce_timing_read()
+    lce.lce_timing_enable(False)
+    kd = {k[0]: k for k in kernels}
+    roof = None
+    if "ce_bwd_rows" in kd:
+        k = kd["ce_bwd_rows"]
+        avg_ms = k[1] / k[2]
+        achieved = bwd_bytes / (avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "ce_bwd_rows", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "avg_launch_ms": round(avg_ms, 4),
+                "traffic": stored_traffic("ce_bwd_rows", CE_WORKLOAD)}
+    fwd_gbs = fwd_bytes / (fwd_ms * 1e-3) / 1e9
+    tot_gbs = (fwd_bytes + bwd_bytes) / (ms * 1e-3) / 1e9
+    return {
+        "workload": w, "ms": ms, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "wall_s": wall,
+        "tokens_per_s": w.n / (ms * 1e-3), "gbs": tot_gbs, "fwd_gbs": fwd_gbs,
+        "bwd_gbs": bwd_bytes / (bwd_ms * 1e-3) / 1e9, "loss": float(loss.item()),
+        "roofline": roof, "algorithmic_bytes": fwd_bytes + bwd_bytes, "gen_s": gen_s,
+        "kernels": {k[0]: {"ms_per_step": round(k[1] / kreps, 4), "launches_per_step": k[2] // kreps}
+                    for k in kernels},
+        "inputs": inp, "nvalid": nvalid,
+    }
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("internal_api") in ("openblas", "mkl", "blis")]
+        if info:
+            return int(info[0]["num_threads"])
+    except Exception:  # pragma: no cover
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline_flce(res):
+    """The fp64 oracle on the first 256 tokens of the same workload (all of the weight)."""
+    import oracle
+    inp = res["inputs"]
+    k = 256
+    t0 = time.perf_counter()
+    oracle.flce(inp.hidden[:k], inp.weight, inp.labels[:k], num_label_tokens=res["nvalid"],
+                row_block=256)
+    dt = time.perf_counter() - t0
+    return {"value": round(k / dt, 2), "unit": "tokens/s", "cores": blas_threads(),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"first {k} of {res['workload'].n} tokens, full weight "
+                      f"[{res['workload'].v}, {res['workload'].h}]: loss, grad_hidden, grad_weight in fp64"}
+
+
+def cpu_baseline_ce(res):
+    """The fp64 oracle on the first 2048 rows of the same logits."""
+    import oracle
+    inp = res["inputs"]
+    k = 2048
+    t0 = time.perf_counter()
+    oracle.ce_masked_sum_bits(inp.logits[:k], inp.labels[:k], num_label_tokens=res["nvalid"],
+                              row_block=256)
+    dt = time.perf_counter() - t0
+    return {"value": round(k / dt, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"first {k} of {res['workload'].n} rows of the [{res['workload'].n}, "
+                      f"{res['workload'].v}] logits: loss and full gradient rows in fp64"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["flce", "ce"], default=None,
+                    help="run one layer only (profiling)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+    if args.steps < 1:
+        print("--steps must be >= 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import linear_cross_entropy_masked_amd as lce
+    import workloads
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 2
+    lce.load_library()
+
+    out = {"metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": None,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded PCG64 normals rounded to bf16; labels uniform with ignore holes)"}
+    fl = ce = None
+    if args.only in (None, "flce"):
+        fl = run_flce(args, torch, lce, workloads)
+        w = fl["workload"]
+        print(f"# flce {w.name}: {fl['ms']:.3f} ms/step, {fl['tokens_per_s']:.0f} tokens/s, "
+              f"{fl['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        out.update({
+            "value": round(fl["tokens_per_s"], 1), "ms_per_step": round(fl["ms"], 4),
+            "config": {"workload": w.name, "tokens": w.n, "hidden": w.h, "vocab": w.v,
+                       "chunk_size": w.chunk_size, "bias": False, "ignored": w.n - fl["nvalid"],
+                       "outputs": "loss, grad_hidden bf16, grad_weight fp32"},
+            "tflops": round(fl["tflops"], 2),
+            "mfma_frac": round(fl["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+            "roofline": fl["roofline"],
+            "kernels": fl["kernels"],
+            "peak_extra_bytes": fl["peak_extra_bytes"],
+            "slice_budget_bytes": fl["slice_budget_bytes"],
+            "loss": fl["loss"],
+        })
+    if args.only in (None, "ce"):
+        ce = run_ce(args, torch, lce, workloads)
+        w = ce["workload"]
+        print(f"# ce {w.name}: {ce['ms']:.3f} ms/step, {ce['gbs']:.0f} GB/s", file=sys.stderr,
+              flush=True)
+        ce_obj = {
+            "workload": w.name, "ms_per_step": round(ce["ms"], 4),
+            "fwd_ms": round(ce["fwd_ms"], 4), "bwd_ms": round(ce["bwd_ms"], 4),
+            "tokens_per_s": round(ce["tokens_per_s"], 1), "GB_per_s": round(ce["gbs"], 1),
+            "hbm_frac": round(ce["gbs"] / HBM_PEAK_GBS, 4),
+            "fwd_GB_per_s": round(ce["fwd_gbs"], 1), "bwd_GB_per_s": round(ce["bwd_gbs"], 1),
+            "algorithmic_bytes": ce["algorithmic_bytes"], "roofline": ce["roofline"],
+            "kernels": ce["kernels"], "loss": ce["loss"],
+        }
+        if fl is None:
+            out.update({"value": round(ce["tokens_per_s"], 1), "ms_per_step": round(ce["ms"], 4),
+                        "config": {"workload": w.name, "tokens": w.n, "vocab": w.v,
+                                   "chunk_size": w.chunk_size},
+                        "roofline": ce["roofline"]})
+        out["ce_only"] = ce_obj
+    if not args.no_cpu_baseline:
+        if fl is not None:
+            out["cpu_baseline"] = cpu_baseline_flce(fl)
+        if ce is not None:
+            (out["ce_only"] if "ce_only" in out and fl is not None else out)["cpu_baseline"] = \
+                cpu_baseline_ce(ce)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -150,6 +150,21 @@ int flce_fwd_bwd(const uint16_t* hidden, const uint16_t* weight, const float* bi
                  uint16_t* grad_hidden, float* grad_weight, float* grad_bias,
                  int32_t* status_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------ measurement aid */
+
+/* Opt-in launch timing. While enabled, every kernel the library enqueues is bracketed by a
+ * pair of hipEvents recorded on the caller's stream (a few microseconds per launch; off by
+ * default; process-wide). Always returns LCE_OK. */
+int lce_timing_enable(int enable);
+
+/* Waits for the recorded event pairs, writes up to max_kernels rows (kernel name in static
+ * storage, total milliseconds, number of launches) for the kernels timed since the previous
+ * read, then resets the totals. *count_out receives the number of kernels seen, which may
+ * exceed max_kernels. LCE_ERR_NULL_ARG if count_out is NULL, or max_kernels > 0 and an
+ * output array is NULL; LCE_ERR_HIP if an event could not be read. */
+int lce_timing_read(int max_kernels, const char** names, double* total_ms, long long* launches,
+                    int* count_out);
+
 #ifdef __cplusplus
 }
 #endif

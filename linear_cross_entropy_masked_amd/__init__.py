@@ -20,6 +20,7 @@ __all__ = [
     "ce_chunked_workspace_size", "ce_chunked_fwd", "ce_chunked_bwd", "ce_chunked_bwd_inplace",
     "flce_workspace_size", "flce_fwd_bwd", "lce_status_str",
     "FLCE_RECOMPUTE", "FLCE_ACCUMULATE", "LCE_STATUS_BAD_LABEL",
+    "lce_timing_enable", "lce_timing_read",
 ]
 
 FLCE_RECOMPUTE = 1
@@ -62,6 +63,11 @@ def load_library() -> ctypes.CDLL:
         "flce_workspace_size": (ctypes.c_int, [i64, i64, i64, i64, u32, psz]),
         "flce_fwd_bwd": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, i64, i32, i64, i64, u32, vp, vp, vp,
                                         vp, vp, vp, vp, vp, sz, vp]),
+        "lce_timing_enable": (ctypes.c_int, [ctypes.c_int]),
+        "lce_timing_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
+                                           ctypes.POINTER(ctypes.c_double),
+                                           ctypes.POINTER(ctypes.c_longlong),
+                                           ctypes.POINTER(ctypes.c_int)]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(lib, name)
@@ -279,3 +285,20 @@ def flce_fwd_bwd(hidden, weight, labels, bias=None, *, ignore_index: int = -100,
         _ptr(gw), _ptr(gb), _ptr(status), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(dev)))
     return loss, gh, gw, gb, lse
+
+
+def lce_timing_enable(on: bool = True) -> None:
+    """Bracket every library launch with hipEvents (measurement aid; off by default)."""
+    _check("lce_timing_enable", load_library().lce_timing_enable(1 if on else 0))
+
+
+def lce_timing_read() -> list[tuple[str, float, int]]:
+    """(kernel name, total ms, launches) per kernel since the previous read; resets totals."""
+    lib = load_library()
+    cap = 32
+    names = (ctypes.c_char_p * cap)()
+    ms = (ctypes.c_double * cap)()
+    cnt = (ctypes.c_longlong * cap)()
+    k = ctypes.c_int()
+    _check("lce_timing_read", lib.lce_timing_read(cap, names, ms, cnt, ctypes.byref(k)))
+    return [(names[i].decode(), ms[i], cnt[i]) for i in range(min(k.value, cap))]

@@ -23,7 +23,7 @@ LIB_NAME = "liblce_masked.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["capi.hip", "ce_kernels.hip", "flce_kernels.hip"]
+SOURCES = ["capi.hip", "ce_kernels.hip", "flce_kernels.hip", "timing.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -294,6 +294,7 @@ CeWorkspace ce_workspace_carve(void* base, int64_t n) {
 
 hipError_t launch_label_prep(const int32_t* labels, int64_t n, int64_t v, int32_t ignore_index,
                              long long* count_out, int32_t* status_out, hipStream_t stream) {
+  TimedLaunch t(stream, K_LABEL_PREP);
   hipLaunchKernelGGL(label_prep_kernel, dim3(1), dim3(1024), 0, stream, labels, n, v,
                      ignore_index, count_out, status_out);
   return hipGetLastError();
@@ -303,6 +304,7 @@ hipError_t launch_ce_fwd_rows(const uint16_t* logits, int64_t n, int64_t v, int6
                               const int32_t* labels, int32_t ignore_index, float* row_loss,
                               float* lse_out, hipStream_t stream) {
   if (n == 0) return hipSuccess;
+  TimedLaunch t(stream, K_CE_FWD_ROWS);
   hipLaunchKernelGGL(ce_fwd_rows_kernel, dim3(unsigned(n)), dim3(kRowThreads), 0, stream,
                      logits, v, ld, labels, ignore_index, row_loss, lse_out);
   return hipGetLastError();
@@ -310,6 +312,7 @@ hipError_t launch_ce_fwd_rows(const uint16_t* logits, int64_t n, int64_t v, int6
 
 hipError_t launch_loss_reduce(const float* row_loss, int64_t n, const long long* count_dev,
                               long long count_host, float* loss_out, hipStream_t stream) {
+  TimedLaunch t(stream, K_LOSS_REDUCE);
   hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(1024), 0, stream, row_loss, n,
                      count_dev, count_host, loss_out);
   return hipGetLastError();
@@ -320,6 +323,7 @@ hipError_t launch_ce_bwd_rows(const uint16_t* logits, int64_t ld, uint16_t* grad
                               const float* lse, const long long* count_dev, long long count_host,
                               const float* grad_output, hipStream_t stream) {
   if (n == 0) return hipSuccess;
+  TimedLaunch t(stream, K_CE_BWD_ROWS);
   hipLaunchKernelGGL(ce_bwd_rows_kernel, dim3(unsigned(n)), dim3(kRowThreads), 0, stream,
                      logits, ld, grad, ldg, v, labels, ignore_index, lse, count_dev, count_host,
                      grad_output);

@@ -79,3 +79,38 @@ hipError_t launch_ce_bwd_rows(const uint16_t* logits, int64_t ld, uint16_t* grad
                               const float* grad_output, hipStream_t stream);
 
 }  // namespace lce
+
+// ---- opt-in launch timing (lce_timing_enable / lce_timing_read in the C ABI) ----
+namespace lce {
+
+enum KernelId {
+  K_LABEL_PREP = 0,
+  K_CE_FWD_ROWS,
+  K_LOSS_REDUCE,
+  K_CE_BWD_ROWS,
+  K_FLCE_GEMM_LOGITS,
+  K_FLCE_ROW_LSE,
+  K_FLCE_BIAS_GRAD,
+  K_FLCE_TO_PROBS,
+  K_FLCE_GEMM_GRAD_HIDDEN,
+  K_FLCE_GEMM_GRAD_WEIGHT,
+  K_FLCE_ONEHOT_FIX,
+  K_FILL,
+  K_COUNT
+};
+
+const char* kernel_name(int id);
+bool timing_on();
+// Record a start/stop event pair around a launch on `stream` (no-ops unless enabled).
+void timing_start(hipStream_t stream, int id);
+void timing_stop(hipStream_t stream, int id);
+
+// RAII helper: brackets one launch.
+struct TimedLaunch {
+  hipStream_t s;
+  int id;
+  TimedLaunch(hipStream_t s_, int id_) : s(s_), id(id_) { timing_start(s, id); }
+  ~TimedLaunch() { timing_stop(s, id); }
+};
+
+}  // namespace lce

@@ -374,7 +374,8 @@ FlceWs flce_carve(void* base, int64_t n, int64_t v, int64_t chunk) {
 
 template <int BM, int BN, bool AK, bool BKM, class Epi>
 hipError_t launch_gemm(const View& A, const View& B, int64_t M, int64_t N, int64_t K,
-                       const Epi& epi, hipStream_t s) {
+                       const Epi& epi, hipStream_t s, int kid) {
+  TimedLaunch t(s, kid);
   const dim3 grid(unsigned((N + BN - 1) / BN), unsigned((M + BM - 1) / BM));
   hipLaunchKernelGGL((gemm_kernel<BM, BN, 64, AK, BKM, Epi>), grid, dim3(256), 0, s, A, B, M,
                      N, K, epi);
@@ -413,10 +414,12 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     return e;
   if (n == 0 && !accumulate) {
     if (a.grad_weight) {
+      TimedLaunch t(s, K_FILL);
       hipLaunchKernelGGL(fill_zero_f32, dim3(1024), dim3(256), 0, s, a.grad_weight, v * h);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (a.grad_bias) {
+      TimedLaunch t(s, K_FILL);
       hipLaunchKernelGGL(fill_zero_f32, dim3(64), dim3(256), 0, s, a.grad_bias, v);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -432,16 +435,20 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     View Ah{hid, h, kGroup, rows, h};
     View Bw{a.weight, h, kGroup, v, h};
     EpiLogits el{ws.slice, ws.ldz, a.bias};
-    if ((e = launch_gemm<64, 64, true, true>(Ah, Bw, rows, v, h, el, s)) != hipSuccess) return e;
+    if ((e = launch_gemm<64, 64, true, true>(Ah, Bw, rows, v, h, el, s, K_FLCE_GEMM_LOGITS)) != hipSuccess) return e;
 
     // 2. row logsumexp and loss terms
-    hipLaunchKernelGGL(slice_row_lse_kernel, dim3(unsigned(rows)), dim3(kRowThreads), 0, s,
-                       ws.slice, ws.ldz, v, lab, a.ignore_index, ws.lse_c, ws.row_loss + c0,
-                       a.lse_out ? a.lse_out + c0 : nullptr);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+      TimedLaunch t(s, K_FLCE_ROW_LSE);
+      hipLaunchKernelGGL(slice_row_lse_kernel, dim3(unsigned(rows)), dim3(kRowThreads), 0, s,
+                         ws.slice, ws.ldz, v, lab, a.ignore_index, ws.lse_c, ws.row_loss + c0,
+                         a.lse_out ? a.lse_out + c0 : nullptr);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
 
     // 3. bias gradient from the fp32 logits
     if (a.grad_bias) {
+      TimedLaunch t(s, K_FLCE_BIAS_GRAD);
       hipLaunchKernelGGL(slice_bias_grad_kernel, dim3(unsigned((v + 255) / 256)), dim3(256), 0, s,
                          ws.slice, ws.ldz, rows, v, lab, a.ignore_index, ws.lse_c, a.grad_bias,
                          int(first && !accumulate), ws.count, th, a.grad_output);
@@ -451,9 +458,12 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
 
     // 4. probabilities in place
     const int64_t groups = ws.ldz / kGroup;
-    hipLaunchKernelGGL(slice_to_probs_kernel, dim3(unsigned((groups + 3) / 4), unsigned(rows)),
-                       dim3(256), 0, s, ws.slice, ws.ldz, v, lab, a.ignore_index, ws.lse_c);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+      TimedLaunch t(s, K_FLCE_TO_PROBS);
+      hipLaunchKernelGGL(slice_to_probs_kernel, dim3(unsigned((groups + 3) / 4), unsigned(rows)),
+                         dim3(256), 0, s, ws.slice, ws.ldz, v, lab, a.ignore_index, ws.lse_c);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     const uint16_t* P = reinterpret_cast<const uint16_t*>(ws.slice);
     const int64_t p_ld = 2 * ws.ldz, p_gs = 2 * kGroup;
 
@@ -463,14 +473,15 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
       View Bw2{a.weight, h, kGroup, v, h};  // rows = k (vocab), cols = n (hidden)
       EpiGradHidden eh{a.grad_hidden + c0 * h, h, lab, a.weight, h, v, a.ignore_index,
                        ws.count, th, a.grad_output, 0.f};
-      if ((e = launch_gemm<64, 64, true, false>(Ap, Bw2, rows, h, v, eh, s)) != hipSuccess) return e;
+      if ((e = launch_gemm<64, 64, true, false>(Ap, Bw2, rows, h, v, eh, s, K_FLCE_GEMM_GRAD_HIDDEN)) != hipSuccess) return e;
     }
     // 6./7. grad_weight
     if (a.grad_weight) {
       View Apt{P, p_ld, p_gs, rows, v};        // rows = k (chunk row), cols = m (vocab)
       View Bh{hid, h, kGroup, rows, h};       // rows = k, cols = n
       EpiGradWeight ew{a.grad_weight, h, int(first && !accumulate), ws.count, th, a.grad_output, 0.f};
-      if ((e = launch_gemm<64, 64, false, false>(Apt, Bh, v, h, rows, ew, s)) != hipSuccess) return e;
+      if ((e = launch_gemm<64, 64, false, false>(Apt, Bh, v, h, rows, ew, s, K_FLCE_GEMM_GRAD_WEIGHT)) != hipSuccess) return e;
+      TimedLaunch t(s, K_FLCE_ONEHOT_FIX);
       hipLaunchKernelGGL(onehot_weight_fix_kernel, dim3(unsigned(rows)), dim3(256), 0, s, hid, h,
                          rows, lab, a.ignore_index, v, a.grad_weight, ws.count, th, a.grad_output);
       if ((e = hipGetLastError()) != hipSuccess) return e;
