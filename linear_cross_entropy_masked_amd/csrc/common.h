@@ -96,6 +96,7 @@ enum KernelId {
   K_FLCE_GEMM_GRAD_WEIGHT,
   K_FLCE_ONEHOT_FIX,
   K_FILL,
+  K_FLCE_GRAD_HIDDEN_REDUCE,
   K_COUNT
 };
 

@@ -25,44 +25,18 @@
 // result (scaling or subtracting inside the bf16 operand would not).
 #include "common.h"
 #include "flce.h"
+#include "gemm_tile.h"
 #include "lce_masked.h"
 
 namespace lce {
 
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
 constexpr int kGroup = 64;  // column-group width of the logits slice / probability layout
 
 __host__ __device__ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-// Row-major bf16 matrix view whose contiguous dimension is split into 64-wide groups placed
-// `gs` elements apart (gs == 64 is a plain dense matrix).
-struct View {
-  const uint16_t* p;
-  int64_t ld;    // elements between consecutive rows
-  int64_t gs;    // elements between consecutive 64-column groups
-  int64_t rows;  // valid rows
-  int64_t cols;  // valid columns
-  __device__ __forceinline__ const uint16_t* at(int64_t r, int64_t c) const {
-    return p + r * ld + (c >> 6) * gs + (c & 63);
-  }
-  // 8 consecutive columns starting at c (c % 8 == 0), zero outside the valid range.
-  __device__ __forceinline__ uint4 load8(int64_t r, int64_t c) const {
-    if (r < rows && c + 8 <= cols) return *reinterpret_cast<const uint4*>(at(r, c));
-    uint16_t e[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = (r < rows && c + j < cols) ? *at(r, c + j) : uint16_t(0);
-    uint4 q;
-    q.x = uint32_t(e[0]) | (uint32_t(e[1]) << 16);
-    q.y = uint32_t(e[2]) | (uint32_t(e[3]) << 16);
-    q.z = uint32_t(e[4]) | (uint32_t(e[5]) << 16);
-    q.w = uint32_t(e[6]) | (uint32_t(e[7]) << 16);
-    return q;
-  }
-};
+using gemm::View;
 
 __device__ __forceinline__ float flce_coef(const long long* count_dev, long long count_host,
                                            const float* gout) {
@@ -75,104 +49,18 @@ __device__ __forceinline__ bool has_label(int32_t y, int64_t v, int32_t ignore_i
   return y != ignore_index && y >= 0 && int64_t(y) < v;
 }
 
-// ------------------------------------------------------------------ generic MFMA GEMM
-//
-// C[M, N] = Σ_k A(m, k) · B(k, n) on v_mfma_f32_16x16x32_bf16. A is K-major (row m holds
-// contiguous k) when AK, else M-major (row k holds contiguous m); likewise B with BK_.
-// 256 threads = 4 wavefronts in a 2 × 2 arrangement; both operands are staged in LDS
-// K-contiguous (an M/N-major operand is transposed on its way into LDS), so each lane feeds
-// the MFMA with one 16-byte LDS read per 16 × 32 fragment.
-template <int BM, int BN, int BKT, bool AK, bool BKM, class Epi>
-__global__ void __launch_bounds__(256) gemm_kernel(View A, View B, int64_t M, int64_t N,
-                                                   int64_t K, Epi epi) {
-  constexpr int PAD = 8;
-  constexpr int LDP = BKT + PAD;
-  constexpr int WTM = BM / 2, WTN = BN / 2;
-  constexpr int TM = WTM / 16, TN = WTN / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t sA[BM * LDP];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[BN * LDP];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = int64_t(blockIdx.y) * BM;
-  const int64_t n0 = int64_t(blockIdx.x) * BN;
-
-  f32x4_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  auto stage = [&](const View& X, bool kmajor, int64_t r0, int64_t k0, uint16_t* s, int R) {
-    if (kmajor) {
-      const int vecs = R * (BKT / 8);
-      for (int e = tid; e < vecs; e += 256) {
-        const int r = e / (BKT / 8);
-        const int kv = (e % (BKT / 8)) * 8;
-        *reinterpret_cast<uint4*>(&s[r * LDP + kv]) = X.load8(r0 + r, k0 + kv);
-      }
-    } else {
-      const int vecs = BKT * (R / 8);
-      for (int e = tid; e < vecs; e += 256) {
-        const int k = e / (R / 8);
-        const int rv = (e % (R / 8)) * 8;
-        const uint4 q = X.load8(k0 + k, r0 + rv);
-        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          s[(rv + 2 * j) * LDP + k] = uint16_t(w[j] & 0xffffu);
-          s[(rv + 2 * j + 1) * LDP + k] = uint16_t(w[j] >> 16);
-        }
-      }
-    }
-  };
-
-  for (int64_t k0 = 0; k0 < K; k0 += BKT) {
-    __syncthreads();
-    stage(A, AK, m0, k0, sA, BM);
-    stage(B, BKM, n0, k0, sB, BN);
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < BKT; ks += 32) {
-      bf16x8_t af[TM], bfr[TN];
-      const int kq = ks + 8 * (lane >> 4);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(&sA[(wm * WTM + i * 16 + (lane & 15)) * LDP + kq]);
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&sB[(wn * WTN + j * 16 + (lane & 15)) * LDP + kq]);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-  }
-
-  epi.begin();
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t gm = m0 + wm * WTM + i * 16 + 4 * (lane >> 4) + q;
-        const int64_t gn = n0 + wn * WTN + j * 16 + (lane & 15);
-        if (gm < M && gn < N) epi(gm, gn, acc[i][j][q]);
-      }
-}
-
 // Z[m, n] = acc + bias[n] into the fp32 slice.
 struct EpiLogits {
   float* z;
   int64_t ldz;
   const float* bias;
-  __device__ void begin() {}
+  __device__ void begin(int64_t) {}
   __device__ __forceinline__ void operator()(int64_t m, int64_t n, float a) {
     z[m * ldz + n] = bias ? a + bias[n] : a;
+  }
+  __device__ __forceinline__ void store4(int64_t m, int64_t n, gemm::f32x4_t a) {
+    if (bias) a += gemm::f32x4_t{bias[n], bias[n + 1], bias[n + 2], bias[n + 3]};
+    *reinterpret_cast<gemm::f32x4_t*>(z + m * ldz + n) = a;
   }
 };
 
@@ -188,12 +76,22 @@ struct EpiGradHidden {
   long long count_host;
   const float* gout;
   float coef;
-  __device__ void begin() { coef = flce_coef(count_dev, count_host, gout); }
+  __device__ void begin(int64_t) { coef = flce_coef(count_dev, count_host, gout); }
   __device__ __forceinline__ void operator()(int64_t m, int64_t n, float a) {
     const int32_t y = labels[m];
     float r = 0.f;
     if (has_label(y, v, ignore_index)) r = coef * (a - bf16_to_f32(w[int64_t(y) * ldw + n]));
     dh[m * ldh + n] = f32_to_bf16(r);
+  }
+  __device__ __forceinline__ void store4(int64_t m, int64_t n, gemm::f32x4_t a) {
+    const int32_t y = labels[m];
+    uint2 o = {0u, 0u};
+    if (has_label(y, v, ignore_index)) {
+      const uint2 wy = *reinterpret_cast<const uint2*>(w + int64_t(y) * ldw + n);
+      o.x = pack_bf16x2(coef * (a[0] - bf16_lo(wy.x)), coef * (a[1] - bf16_hi(wy.x)));
+      o.y = pack_bf16x2(coef * (a[2] - bf16_lo(wy.y)), coef * (a[3] - bf16_hi(wy.y)));
+    }
+    *reinterpret_cast<uint2*>(dh + m * ldh + n) = o;
   }
 };
 
@@ -206,12 +104,54 @@ struct EpiGradWeight {
   long long count_host;
   const float* gout;
   float coef;
-  __device__ void begin() { coef = flce_coef(count_dev, count_host, gout); }
+  __device__ void begin(int64_t) { coef = flce_coef(count_dev, count_host, gout); }
   __device__ __forceinline__ void operator()(int64_t m, int64_t n, float a) {
     float* p = dw + m * ldw + n;
     *p = overwrite ? coef * a : *p + coef * a;
   }
+  __device__ __forceinline__ void store4(int64_t m, int64_t n, gemm::f32x4_t a) {
+    gemm::f32x4_t* p = reinterpret_cast<gemm::f32x4_t*>(dw + m * ldw + n);
+    *p = overwrite ? coef * a : *p + coef * a;
+  }
 };
+
+// Split-K partial sums of grad_hidden live in the unused second half of every 64-column
+// group of the slice once it holds probabilities: flat element e sits at float offset
+// (e / 32) * 64 + 32 + e % 32.
+__device__ __forceinline__ int64_t gap_index(int64_t e) { return (e >> 5) * 64 + 32 + (e & 31); }
+
+struct EpiPartial {
+  float* slice;
+  int64_t M, N;
+  int64_t kz;
+  __device__ void begin(int64_t z) { kz = z; }
+  __device__ __forceinline__ void operator()(int64_t m, int64_t n, float a) {
+    slice[gap_index((kz * M + m) * N + n)] = a;
+  }
+  // N % 4 == 0 and n % 4 == 0 keep the 4 values inside one 32-float gap
+  __device__ __forceinline__ void store4(int64_t m, int64_t n, gemm::f32x4_t a) {
+    *reinterpret_cast<gemm::f32x4_t*>(slice + gap_index((kz * M + m) * N + n)) = a;
+  }
+};
+
+// dH[m, n] = coef · (Σ_z partial_z[m, n] − W[y_m, n]), summed in split order; bf16 out.
+__global__ void __launch_bounds__(256) grad_hidden_reduce_kernel(
+    const float* __restrict__ slice, int64_t M, int64_t N, int64_t splits,
+    uint16_t* __restrict__ dh, const int32_t* __restrict__ labels, const uint16_t* __restrict__ w,
+    int64_t v, int32_t ignore_index, const long long* count_dev, long long count_host,
+    const float* gout) {
+  const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= M * N) return;
+  const int64_t m = e / N, n = e % N;
+  const int32_t y = labels[m];
+  float r = 0.f;
+  if (has_label(y, v, ignore_index)) {
+    float acc = 0.f;
+    for (int64_t z = 0; z < splits; ++z) acc += slice[gap_index(z * M * N + e)];
+    r = flce_coef(count_dev, count_host, gout) * (acc - bf16_to_f32(w[int64_t(y) * N + n]));
+  }
+  dh[e] = f32_to_bf16(r);
+}
 
 // ------------------------------------------------------------------ row / column passes
 
@@ -372,16 +312,6 @@ FlceWs flce_carve(void* base, int64_t n, int64_t v, int64_t chunk) {
   return w;
 }
 
-template <int BM, int BN, bool AK, bool BKM, class Epi>
-hipError_t launch_gemm(const View& A, const View& B, int64_t M, int64_t N, int64_t K,
-                       const Epi& epi, hipStream_t s, int kid) {
-  TimedLaunch t(s, kid);
-  const dim3 grid(unsigned((N + BN - 1) / BN), unsigned((M + BM - 1) / BM));
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, 64, AK, BKM, Epi>), grid, dim3(256), 0, s, A, B, M,
-                     N, K, epi);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 int flce_check_shape(int64_t n, int64_t h, int64_t v, int64_t chunk_size, uint32_t flags) {
@@ -435,7 +365,12 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     View Ah{hid, h, kGroup, rows, h};
     View Bw{a.weight, h, kGroup, v, h};
     EpiLogits el{ws.slice, ws.ldz, a.bias};
-    if ((e = launch_gemm<64, 64, true, true>(Ah, Bw, rows, v, h, el, s, K_FLCE_GEMM_LOGITS)) != hipSuccess) return e;
+    {
+      TimedLaunch t(s, K_FLCE_GEMM_LOGITS);
+      e = (h % gemm::v2::BK2 == 0) ? gemm::v2::launch<true, true>(Ah, Bw, rows, v, h, 1, true, el, s)
+                                   : gemm::launch<true, true>(Ah, Bw, rows, v, h, 1, true, el, s);
+      if (e != hipSuccess) return e;
+    }
 
     // 2. row logsumexp and loss terms
     {
@@ -471,16 +406,41 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     if (a.grad_hidden) {
       View Ap{P, p_ld, p_gs, rows, v};
       View Bw2{a.weight, h, kGroup, v, h};  // rows = k (vocab), cols = n (hidden)
-      EpiGradHidden eh{a.grad_hidden + c0 * h, h, lab, a.weight, h, v, a.ignore_index,
-                       ws.count, th, a.grad_output, 0.f};
-      if ((e = launch_gemm<64, 64, true, false>(Ap, Bw2, rows, h, v, eh, s, K_FLCE_GEMM_GRAD_HIDDEN)) != hipSuccess) return e;
+      // split K = V so the few [rows, h] output tiles still fill the chip
+      const int64_t tiles = ((rows + gemm::BM - 1) / gemm::BM) * ((h + gemm::BN - 1) / gemm::BN);
+      int64_t splits = 256 / tiles;
+      const int64_t gap_cap = (rows * ws.ldz / 2) / (rows * h);  // partials that fit the gaps
+      if (splits > gap_cap) splits = gap_cap;
+      if (splits > (v + 2047) / 2048) splits = (v + 2047) / 2048;  // keep >= 2048 of K per split
+      if (splits < 1) splits = 1;
+      if (splits == 1) {
+        EpiGradHidden eh{a.grad_hidden + c0 * h, h, lab, a.weight, h, v, a.ignore_index,
+                         ws.count, th, a.grad_output, 0.f};
+        TimedLaunch t(s, K_FLCE_GEMM_GRAD_HIDDEN);
+        if ((e = gemm::v2::launch<true, false>(Ap, Bw2, rows, h, v, 1, true, eh, s)) != hipSuccess) return e;
+      } else {
+        EpiPartial ep{ws.slice, rows, h, 0};
+        {
+          TimedLaunch t(s, K_FLCE_GEMM_GRAD_HIDDEN);
+          if ((e = gemm::v2::launch<true, false>(Ap, Bw2, rows, h, v, splits, true, ep, s)) != hipSuccess)
+            return e;
+        }
+        TimedLaunch t(s, K_FLCE_GRAD_HIDDEN_REDUCE);
+        hipLaunchKernelGGL(grad_hidden_reduce_kernel, dim3(unsigned((rows * h + 255) / 256)),
+                           dim3(256), 0, s, ws.slice, rows, h, splits, a.grad_hidden + c0 * h, lab,
+                           a.weight, v, a.ignore_index, ws.count, th, a.grad_output);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
     }
     // 6./7. grad_weight
     if (a.grad_weight) {
       View Apt{P, p_ld, p_gs, rows, v};        // rows = k (chunk row), cols = m (vocab)
       View Bh{hid, h, kGroup, rows, h};       // rows = k, cols = n
       EpiGradWeight ew{a.grad_weight, h, int(first && !accumulate), ws.count, th, a.grad_output, 0.f};
-      if ((e = launch_gemm<64, 64, false, false>(Apt, Bh, v, h, rows, ew, s, K_FLCE_GEMM_GRAD_WEIGHT)) != hipSuccess) return e;
+      {
+        TimedLaunch t(s, K_FLCE_GEMM_GRAD_WEIGHT);
+        if ((e = gemm::v2::launch<false, false>(Apt, Bh, v, h, rows, 1, false, ew, s)) != hipSuccess) return e;
+      }
       TimedLaunch t(s, K_FLCE_ONEHOT_FIX);
       hipLaunchKernelGGL(onehot_weight_fix_kernel, dim3(unsigned(rows)), dim3(256), 0, s, hid, h,
                          rows, lab, a.ignore_index, v, a.grad_weight, ws.count, th, a.grad_output);

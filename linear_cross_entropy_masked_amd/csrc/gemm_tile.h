@@ -1,0 +1,486 @@
+// Block-tiled bf16 GEMM on gfx950 MFMA, shared by the three products of the fused linear CE.
+//
+//   C[M, N] = Σ_k A(m, k) · B(k, n),   fp32 accumulation, result handed to an epilogue.
+//
+// Tile: 256 × 256 outputs per workgroup, K advanced 64 at a time; 4 wavefronts in a 2 × 2
+// arrangement, each owning a 128 × 128 block of accumulators (8 × 8 fragments of
+// v_mfma_f32_16x16x32_bf16, 256 fp32 registers per lane). Both operands are staged in LDS in
+// the layout the MFMA wants — 64 contiguous k per row — so every fragment is one 16-byte LDS
+// read. 16-byte chunks within a row are XOR-swizzled by a function of the row so that the
+// 16 rows a fragment read touches, and the rows a transposing store touches, fall in
+// different banks.
+//
+// Operands come in two layouts:
+//   K-major  (row m holds contiguous k): copied straight into LDS;
+//   MN-major (row k holds contiguous m): each lane loads a 4 (k) × 8 (m) block with four
+//            16-byte loads and writes eight 4-element k-runs, transposing in registers.
+// The next K-tile is loaded into registers while the MFMAs work on the current one, and
+// LDS is double-buffered, so one barrier per K-tile suffices.
+#pragma once
+
+#include "common.h"
+
+namespace lce {
+namespace gemm {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kThreads = 256;
+constexpr int kTileBytes = 256 * BK * 2;  // one operand tile in LDS (32 KiB)
+
+// Row-major bf16 matrix whose contiguous dimension is split into 64-wide groups placed `gs`
+// elements apart (gs == 64: an ordinary dense matrix).
+struct View {
+  const uint16_t* p;
+  int64_t ld;    // elements between consecutive rows
+  int64_t gs;    // elements between consecutive 64-column groups
+  int64_t rows;  // valid rows
+  int64_t cols;  // valid columns
+};
+
+// Buffer resource over [base, base + bytes): loads at offsets past the end return zero, which
+// masks rows beyond the valid range without branches and can never fault.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xffffffffLL ? 0xffffffffu : uint32_t(bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(n), 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, int(voff), int(soff), 0);
+  return uint4{v.x, v.y, v.z, v.w};
+}
+
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+// Byte offset of 16-byte chunk c (k = 8c .. 8c+7) of row `row` in a [256][64] bf16 tile.
+__device__ __forceinline__ int lds_off(int row, int c) { return row * 128 + ((c ^ swz(row)) << 4); }
+
+// Per-lane byte offset of this lane's first 16-byte load within an operand tile.
+template <bool KMAJOR>
+__device__ __forceinline__ uint32_t lane_offset(const View& X) {
+  const int t = threadIdx.x;
+  if constexpr (KMAJOR) {
+    return uint32_t((int64_t(t >> 3) * X.ld + (t & 7) * 8) * 2);
+  } else {
+    const int m = 8 * (t & 31);
+    return uint32_t((int64_t(t >> 5) * 4 * X.ld + (m >> 6) * X.gs + (m & 63)) * 2);
+  }
+}
+
+// Global -> registers for one operand tile: rows r0 .. r0+255 (m or n), k0 .. k0+63 of a
+// contraction of length K. Rows past the valid range and k >= K read as zero.
+template <bool KMAJOR>
+__device__ __forceinline__ void load_tile(const View& X, int64_t r0, int64_t k0, int64_t K,
+                                          uint32_t voff, uint4 (&reg)[8]) {
+  const int t = threadIdx.x;
+  if constexpr (KMAJOR) {
+    const int64_t g = (k0 >> 6) * X.gs;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(X.p + r0 * X.ld + g, ((X.rows - r0) * X.ld - g) * 2);
+    const bool kin = k0 + (t & 7) * 8 < K;
+    const uint32_t step = uint32_t(32 * X.ld * 2);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint4 v = buf_load16(rs, voff, uint32_t(j) * step);
+      reg[j] = kin ? v : uint4{0u, 0u, 0u, 0u};
+    }
+  } else {
+    const int64_t kr = (X.rows < K ? X.rows : K) - k0;  // valid k rows from k0
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(X.p + k0 * X.ld + (r0 >> 6) * X.gs, kr * X.ld * 2);
+    const uint32_t row = uint32_t(X.ld * 2);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) reg[4 * b + q] = buf_load16(rs, voff, uint32_t(32 * b + q) * row);
+  }
+}
+
+// Registers -> LDS in the MFMA layout.
+template <bool KMAJOR>
+__device__ __forceinline__ void store_tile(char* lds, const uint4 (&reg)[8]) {
+  const int t = threadIdx.x;
+  if constexpr (KMAJOR) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<uint4*>(lds + lds_off((t >> 3) + 32 * j, t & 7)) = reg[j];
+  } else {
+    const int mc = t & 31;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int kq = (t >> 5) + 8 * b;  // k = 4 kq .. 4 kq + 3
+      const uint32_t w[4][4] = {
+          {reg[4 * b + 0].x, reg[4 * b + 0].y, reg[4 * b + 0].z, reg[4 * b + 0].w},
+          {reg[4 * b + 1].x, reg[4 * b + 1].y, reg[4 * b + 1].z, reg[4 * b + 1].w},
+          {reg[4 * b + 2].x, reg[4 * b + 2].y, reg[4 * b + 2].z, reg[4 * b + 2].w},
+          {reg[4 * b + 3].x, reg[4 * b + 3].y, reg[4 * b + 3].z, reg[4 * b + 3].w}};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int wd = j >> 1;
+        uint32_t lo, hi;
+        if (j & 1) {
+          lo = (w[0][wd] >> 16) | (w[1][wd] & 0xffff0000u);
+          hi = (w[2][wd] >> 16) | (w[3][wd] & 0xffff0000u);
+        } else {
+          lo = (w[0][wd] & 0xffffu) | (w[1][wd] << 16);
+          hi = (w[2][wd] & 0xffffu) | (w[3][wd] << 16);
+        }
+        const int m = 8 * mc + j;
+        *reinterpret_cast<uint2*>(lds + lds_off(m, kq >> 1) + (kq & 1) * 8) = uint2{lo, hi};
+      }
+    }
+  }
+}
+
+// Map a linear workgroup id to a tile id so that the tiles one XCD runs (ids congruent mod 8
+// are dispatched to the same XCD) are consecutive in tile order and share operands in its L2.
+__device__ __forceinline__ int64_t xcd_tile(int64_t w, int64_t total) {
+  const int64_t per = total / 8;
+  if (w >= per * 8) return w;
+  return (w % 8) * per + w / 8;
+}
+
+// Tile order: `inner` tiles along the fast dimension share the slow-dimension operand.
+struct TileMap {
+  int64_t m_tiles, n_tiles, splits;
+  bool m_fast;  // true: consecutive tiles walk m (sharing the B tile), else walk n
+};
+
+template <bool AK, bool BKM, class Epi>
+__global__ void __launch_bounds__(kThreads, 1)
+    gemm256_kernel(View A, View B, int64_t M, int64_t N, int64_t K, int64_t ksplit, TileMap tm,
+                   Epi epi) {
+  __shared__ __attribute__((aligned(16))) char lds[2][2][kTileBytes];
+
+  const int64_t total = tm.m_tiles * tm.n_tiles * tm.splits;
+  const int64_t tile = xcd_tile(blockIdx.x, total);
+  const int64_t mn = tm.m_tiles * tm.n_tiles;
+  const int64_t kz = tile / mn;
+  const int64_t rest = tile % mn;
+  const int64_t mt = tm.m_fast ? rest % tm.m_tiles : rest / tm.n_tiles;
+  const int64_t nt = tm.m_fast ? rest / tm.m_tiles : rest % tm.n_tiles;
+  const int64_t m0 = mt * BM, n0 = nt * BN;
+  const int64_t kbeg = kz * ksplit;
+  const int64_t kend = kbeg + ksplit < K ? kbeg + ksplit : K;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  f32x4_t acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  uint4 ra[8], rb[8];
+  const uint32_t va = lane_offset<AK>(A), vb = lane_offset<BKM>(B);
+  int buf = 0;
+  if (kbeg < kend) {
+    load_tile<AK>(A, m0, kbeg, K, va, ra);
+    load_tile<BKM>(B, n0, kbeg, K, vb, rb);
+    store_tile<AK>(lds[0][0], ra);
+    store_tile<BKM>(lds[0][1], rb);
+  }
+  __syncthreads();
+
+  for (int64_t k0 = kbeg; k0 < kend; k0 += BK) {
+    const bool more = k0 + BK < kend;
+    if (more) {
+      load_tile<AK>(A, m0, k0 + BK, K, va, ra);
+      load_tile<BKM>(B, n0, k0 + BK, K, vb, rb);
+    }
+    const char* la = lds[buf][0];
+    const char* lb = lds[buf][1];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c = kk * 4 + (lane >> 4);
+      bf16x8_t bfr[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(lb + lds_off(wn * 128 + j * 16 + (lane & 15), c));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bf16x8_t af =
+            *reinterpret_cast<const bf16x8_t*>(la + lds_off(wm * 128 + i * 16 + (lane & 15), c));
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    if (more) {
+      store_tile<AK>(lds[buf ^ 1][0], ra);
+      store_tile<BKM>(lds[buf ^ 1][1], rb);
+    }
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  epi.begin(kz);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t gm = m0 + wm * 128 + i * 16 + 4 * (lane >> 4) + q;
+        const int64_t gn = n0 + wn * 128 + j * 16 + (lane & 15);
+        if (gm < M && gn < N) epi(gm, gn, acc[i][j][q]);
+      }
+}
+
+template <bool AK, bool BKM, class Epi>
+hipError_t launch(const View& A, const View& B, int64_t M, int64_t N, int64_t K, int64_t splits,
+                  bool m_fast, const Epi& epi, hipStream_t s) {
+  TileMap tm{(M + BM - 1) / BM, (N + BN - 1) / BN, splits < 1 ? 1 : splits, m_fast};
+  int64_t ksplit = (K + tm.splits - 1) / tm.splits;
+  ksplit = (ksplit + BK - 1) / BK * BK;
+  const int64_t total = tm.m_tiles * tm.n_tiles * tm.splits;
+  hipLaunchKernelGGL((gemm256_kernel<AK, BKM, Epi>), dim3(unsigned(total)), dim3(kThreads), 0, s,
+                     A, B, M, N, K, ksplit, tm, epi);
+  return hipGetLastError();
+}
+
+
+// ============================================================================ pipelined variant
+//
+// Same 256 × 256 tile and 2 × 2 wavefront split, but operands go global -> LDS directly
+// (buffer_load ... lds, 16 bytes per lane, no registers involved) into a 4-stage ring of
+// K = 32 slices, three slices ahead of the MFMAs. LDS layouts:
+//   K-major operand : [256 rows][32 k]   (64 B rows, 16-byte chunks XOR-swizzled by row)
+//   MN-major operand: [32 k][256 rows]   (512 B rows, 32-byte pairs XOR-swizzled by k),
+//                     read back with ds_read_b64_tr_b16, which hands each lane 4
+//                     consecutive k of one row — the MFMA operand order.
+// The MFMA is issued with B as its first operand, so each lane ends up owning 4 consecutive
+// output columns of one row (16-byte epilogue accesses).
+// Requirement: for a K-major operand, K must be a multiple of 32 or the columns past K must
+// read as zero (true for the probability slice, whose padding is zero-filled).
+namespace v2 {
+
+constexpr int BK2 = 32;
+constexpr int kStages = 4;
+constexpr int kOpBytes = 256 * BK2 * 2;        // 16 KiB per operand per stage
+constexpr int kStageBytes2 = 2 * kOpBytes;     // A + B
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ int swz_k(int r) { return (r ^ (r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int swz_mn(int k) { return 2 * ((k & 3) | ((k >> 1) & 4)); }
+
+// Per-lane byte offsets (within one stage's global window) of the lane's 4 DMA loads.
+template <bool KMAJOR>
+__device__ __forceinline__ void dma_offsets(const View& X, uint32_t (&off)[4]) {
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (KMAJOR) {
+      const int r = 64 * w + 16 * j + (l >> 2);
+      const int c = (l & 3) ^ swz_k(r);
+      off[j] = uint32_t((int64_t(r) * X.ld + 8 * c) * 2);
+    } else {
+      const int k = 8 * w + 2 * j + (l >> 5);
+      const int c = (l & 31) ^ swz_mn(k);
+      const int m = 8 * c;
+      off[j] = uint32_t((int64_t(k) * X.ld + (m >> 6) * X.gs + (m & 63)) * 2);
+    }
+  }
+}
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource words (base, 32-bit record count, gfx9 data format) for inline asm.
+__device__ __forceinline__ i32x4_t rsrc_words(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xffffffffLL ? 0xffffffffu : uint32_t(bytes));
+  // every input is wave-uniform; readfirstlane lets the asm take the words from SGPRs
+  return i32x4_t{int(__builtin_amdgcn_readfirstlane(uint32_t(a))),
+                 int(__builtin_amdgcn_readfirstlane(uint32_t(a >> 32) & 0xffffu)),
+                 int(__builtin_amdgcn_readfirstlane(n)), 0x00020000};
+}
+
+// 16 bytes per lane from global straight into LDS at dst + 16 * lane. Issued as inline asm
+// on purpose: the compiler then leaves these loads to the explicit vmcnt waits below
+// instead of draining every in-flight slice before each LDS read.
+__device__ __forceinline__ void dma16(i32x4_t rs, uint32_t voff, char* dst) {
+  // the destination is wave-uniform (it depends only on the wavefront index)
+  const uint32_t la = __builtin_amdgcn_readfirstlane(
+      uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)dst)));
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(la), "v"(voff), "s"(rs)
+      : "memory");
+}
+
+// Issue one operand's loads for the K slice starting at k0 into `lds` (this stage's tile).
+template <bool KMAJOR>
+__device__ __forceinline__ void dma_issue(const View& X, int64_t r0, int64_t k0, int64_t K,
+                                          const uint32_t (&off)[4], char* lds) {
+  const int w = threadIdx.x >> 6;
+  i32x4_t rs;
+  if constexpr (KMAJOR) {
+    const int64_t g = (k0 >> 6) * X.gs + (k0 & 63);
+    rs = rsrc_words(X.p + r0 * X.ld + g, ((X.rows - r0) * X.ld - g) * 2);
+  } else {
+    const int64_t kr = (X.rows < K ? X.rows : K) - k0;
+    rs = rsrc_words(X.p + k0 * X.ld + (r0 >> 6) * X.gs, kr * X.ld * 2);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dma16(rs, off[j], lds + (4 * w + j) * 1024);
+}
+
+// One 16 × 32 MFMA operand fragment for rows rbase .. rbase+15 of the stage tile.
+template <bool KMAJOR>
+__device__ __forceinline__ bf16x8_t frag(const char* lds, int rbase) {
+  const int l = threadIdx.x & 63;
+  if constexpr (KMAJOR) {
+    const int r = rbase + (l & 15);
+    const int c = (l >> 4) ^ swz_k(r);
+    return *reinterpret_cast<const bf16x8_t*>(lds + r * 64 + c * 16);
+  } else {
+    const int g = l >> 4, L = l & 15;
+    const int m = rbase + 4 * (L & 3);
+    const int k0 = 8 * g + (L >> 2), k1 = k0 + 4;
+    const int c = m >> 3, h = ((m >> 2) & 1) * 8;
+    const char* p0 = lds + k0 * 512 + ((c ^ swz_mn(k0)) << 4) + h;
+    const char* p1 = lds + k1 * 512 + ((c ^ swz_mn(k1)) << 4) + h;
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p0);
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p1);
+    typedef short v8s __attribute__((ext_vector_type(8)));
+    const v8s v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+  }
+}
+
+// s_waitcnt vmcnt(n) (other counters untouched), n < 64.
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70 | 0); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F70 | 8); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70 | 0x4000 | 0); break;  // 16
+  }
+}
+
+// The four ring slots are separate LDS arrays and the loop is unrolled over them, so the
+// compiler's tracking of in-flight LDS DMA can tell which slot a read depends on and does
+// not drain the slots still being filled.
+__shared__ __attribute__((aligned(1024))) char g_ring0[kStageBytes2];
+__shared__ __attribute__((aligned(1024))) char g_ring1[kStageBytes2];
+__shared__ __attribute__((aligned(1024))) char g_ring2[kStageBytes2];
+__shared__ __attribute__((aligned(1024))) char g_ring3[kStageBytes2];
+
+template <int S>
+__device__ __forceinline__ char* ring() {
+  if constexpr (S == 0) return g_ring0;
+  else if constexpr (S == 1) return g_ring1;
+  else if constexpr (S == 2) return g_ring2;
+  else return g_ring3;
+}
+
+template <bool AK, bool BKM, class Epi>
+__global__ void __launch_bounds__(kThreads, 1)
+    gemm256p_kernel(View A, View B, int64_t M, int64_t N, int64_t K, int64_t ksplit, TileMap tm,
+                    Epi epi) {
+  const int64_t total = tm.m_tiles * tm.n_tiles * tm.splits;
+  const int64_t tile = xcd_tile(blockIdx.x, total);
+  const int64_t mn = tm.m_tiles * tm.n_tiles;
+  const int64_t kz = tile / mn;
+  const int64_t rest = tile % mn;
+  const int64_t mt = tm.m_fast ? rest % tm.m_tiles : rest / tm.n_tiles;
+  const int64_t nt = tm.m_fast ? rest / tm.m_tiles : rest % tm.n_tiles;
+  const int64_t m0 = mt * BM, n0 = nt * BN;
+  const int64_t kbeg = kz * ksplit;
+  const int64_t kend = kbeg + ksplit < K ? kbeg + ksplit : K;
+  const int nk = kend > kbeg ? int((kend - kbeg + BK2 - 1) / BK2) : 0;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  uint32_t offa[4], offb[4];
+  dma_offsets<AK>(A, offa);
+  dma_offsets<BKM>(B, offb);
+
+  f32x4_t acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto issue = [&](char* st, int s) {
+    const int64_t k0 = kbeg + int64_t(s) * BK2;
+    dma_issue<AK>(A, m0, k0, K, offa, st);
+    dma_issue<BKM>(B, n0, k0, K, offb, st + kOpBytes);
+  };
+
+  if (0 < nk) issue(ring<0>(), 0);
+  if (1 < nk) issue(ring<1>(), 1);
+  if (2 < nk) issue(ring<2>(), 2);
+
+  // one K slice: wait for its DMA, read fragments, refill the slot three slices ahead, MFMA
+  auto step = [&](const char* st, char* refill, int kt) {
+    const int later = (nk - 1 - kt) < (kStages - 2) ? (nk - 1 - kt) : (kStages - 2);
+    wait_vm(8 * later);
+    // bare barrier: the vmcnt wait above covers this slice's DMA; a __syncthreads() fence
+    // would also drain the slices still in flight
+    __builtin_amdgcn_s_barrier();
+    bf16x8_t bf[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bf[j] = frag<BKM>(st + kOpBytes, wn * 128 + 16 * j);
+    bf16x8_t af[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) af[i] = frag<AK>(st, wm * 128 + 16 * i);
+    if (kt + kStages - 1 < nk) issue(refill, kt + kStages - 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+  };
+
+  for (int kt = 0; kt < nk; kt += kStages) {
+    step(ring<0>(), ring<3>(), kt);
+    if (kt + 1 < nk) step(ring<1>(), ring<0>(), kt + 1);
+    if (kt + 2 < nk) step(ring<2>(), ring<1>(), kt + 2);
+    if (kt + 3 < nk) step(ring<3>(), ring<2>(), kt + 3);
+  }
+
+  epi.begin(kz);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t gm = m0 + wm * 128 + 16 * i + (lane & 15);
+    if (gm >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t gn = n0 + wn * 128 + 16 * j + 4 * (lane >> 4);
+      if (gn + 4 <= N) {
+        epi.store4(gm, gn, acc[i][j]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (gn + q < N) epi(gm, gn + q, acc[i][j][q]);
+      }
+    }
+  }
+}
+
+template <bool AK, bool BKM, class Epi>
+hipError_t launch(const View& A, const View& B, int64_t M, int64_t N, int64_t K, int64_t splits,
+                  bool m_fast, const Epi& epi, hipStream_t s) {
+  TileMap tm{(M + BM - 1) / BM, (N + BN - 1) / BN, splits < 1 ? 1 : splits, m_fast};
+  int64_t ksplit = (K + tm.splits - 1) / tm.splits;
+  ksplit = (ksplit + BK2 - 1) / BK2 * BK2;
+  const int64_t total = tm.m_tiles * tm.n_tiles * tm.splits;
+  hipLaunchKernelGGL((gemm256p_kernel<AK, BKM, Epi>), dim3(unsigned(total)), dim3(kThreads), 0, s,
+                     A, B, M, N, K, ksplit, tm, epi);
+  return hipGetLastError();
+}
+
+}  // namespace v2
+}  // namespace gemm
+}  // namespace lce

@@ -51,10 +51,10 @@ def run_flce(dev, inp, chunk, count=None, g=None, recompute=False, accumulate_in
 def rounding_bounds(inp, ref, g):
     """Elementwise error budget of the bf16 probability operand.
 
-    The gradient products take P rounded to bf16 (relative error at most 2^-9, round to
-    nearest even); the one-hot term and the scale g/T stay in fp32. So, up to fp32
-    accumulation, |ΔdW| <= 2^-9 · |g/T| · |P|ᵀ|H| and |ΔdH| <= 2^-9 · |g/T| · |P||W| plus
-    the final bf16 rounding of dH (half an ulp).
+    The gradient products take P rounded to bf16 (8 significant bits, round to nearest even:
+    relative error at most u = 2^-8); the one-hot term and the scale g/T stay in fp32. So,
+    up to fp32 accumulation, |ΔdW| <= u · |g/T| · |P|ᵀ|H| and |ΔdH| <= u · |g/T| · |P||W|
+    plus the final bf16 rounding of dH (half an ulp).
     """
     h = oracle.bf16_bits_to_f64(inp.hidden)
     w = oracle.bf16_bits_to_f64(inp.weight)
@@ -62,7 +62,7 @@ def rounding_bounds(inp, ref, g):
     p = np.exp(z - ref.lse[:, None])
     ok, _ = oracle.labelled_rows(inp.labels, w.shape[0])
     p[~ok] = 0.0
-    c = abs(g) * ref.scale * 2.0 ** -9
+    c = abs(g) * ref.scale * 2.0 ** -8
     return c * (p.T @ np.abs(h)), c * (p @ np.abs(w))
 
 
