@@ -119,13 +119,16 @@ def run_flce(args, torch, lce, workloads):
 
     flops = 6.0 * w.n * w.h * w.v
     chunks = -(-w.n // w.chunk_size)
-    gemm_flops_per_launch = 2.0 * w.chunk_size * w.h * w.v  # every chunk is full here
-    gemms = [k for k in kernels if k[0].startswith("flce_gemm")]
+    one = 2.0 * w.chunk_size * w.h * w.v  # one chunk's product (every chunk is full here)
+    # algorithmic flops per launch of each MFMA kernel: the paired launch runs two products
+    per_launch = {"flce_gemm_logits": one, "flce_gemm_grad_hidden": one,
+                  "flce_gemm_grad_weight": one, "flce_gemm_grad_hidden_and_weight": 2 * one}
+    gemms = [k for k in kernels if k[0] in per_launch]
     dom = max(gemms, key=lambda k: k[1]) if gemms else None
     roof = None
     if dom:
         avg_ms = dom[1] / dom[2]
-        achieved = gemm_flops_per_launch / (avg_ms * 1e-3) / 1e12
+        achieved = per_launch[dom[0]] / (avg_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": dom[0], "achieved": round(achieved, 2),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),

@@ -58,9 +58,12 @@ struct EpiLogits {
   __device__ __forceinline__ void operator()(int64_t m, int64_t n, float a) {
     z[m * ldz + n] = bias ? a + bias[n] : a;
   }
-  __device__ __forceinline__ void store4(int64_t m, int64_t n, gemm::f32x4_t a) {
-    if (bias) a += gemm::f32x4_t{bias[n], bias[n + 1], bias[n + 2], bias[n + 3]};
-    *reinterpret_cast<gemm::f32x4_t*>(z + m * ldz + n) = a;
+  using Aux = gemm::f32x4_t;
+  __device__ __forceinline__ Aux load4(int64_t, int64_t n) const {
+    return bias ? Aux{bias[n], bias[n + 1], bias[n + 2], bias[n + 3]} : Aux{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ __forceinline__ void store4(int64_t m, int64_t n, gemm::f32x4_t a, Aux b) {
+    *reinterpret_cast<gemm::f32x4_t*>(z + m * ldz + n) = a + b;
   }
 };
 
@@ -83,13 +86,21 @@ struct EpiGradHidden {
     if (has_label(y, v, ignore_index)) r = coef * (a - bf16_to_f32(w[int64_t(y) * ldw + n]));
     dh[m * ldh + n] = f32_to_bf16(r);
   }
-  __device__ __forceinline__ void store4(int64_t m, int64_t n, gemm::f32x4_t a) {
+  // aux: the 4 weights W[y_m, n .. n+3] as two bf16 pairs; ok = 0 for a row without label
+  struct Aux {
+    uint32_t a, b, ok;
+  };
+  __device__ __forceinline__ Aux load4(int64_t m, int64_t n) const {
     const int32_t y = labels[m];
+    if (!has_label(y, v, ignore_index)) return Aux{0u, 0u, 0u};
+    const uint2 wy = *reinterpret_cast<const uint2*>(w + int64_t(y) * ldw + n);
+    return Aux{wy.x, wy.y, 1u};
+  }
+  __device__ __forceinline__ void store4(int64_t m, int64_t n, gemm::f32x4_t a, Aux x) {
     uint2 o = {0u, 0u};
-    if (has_label(y, v, ignore_index)) {
-      const uint2 wy = *reinterpret_cast<const uint2*>(w + int64_t(y) * ldw + n);
-      o.x = pack_bf16x2(coef * (a[0] - bf16_lo(wy.x)), coef * (a[1] - bf16_hi(wy.x)));
-      o.y = pack_bf16x2(coef * (a[2] - bf16_lo(wy.y)), coef * (a[3] - bf16_hi(wy.y)));
+    if (x.ok) {
+      o.x = pack_bf16x2(coef * (a[0] - bf16_lo(x.a)), coef * (a[1] - bf16_hi(x.a)));
+      o.y = pack_bf16x2(coef * (a[2] - bf16_lo(x.b)), coef * (a[3] - bf16_hi(x.b)));
     }
     *reinterpret_cast<uint2*>(dh + m * ldh + n) = o;
   }
@@ -109,9 +120,13 @@ struct EpiGradWeight {
     float* p = dw + m * ldw + n;
     *p = overwrite ? coef * a : *p + coef * a;
   }
-  __device__ __forceinline__ void store4(int64_t m, int64_t n, gemm::f32x4_t a) {
-    gemm::f32x4_t* p = reinterpret_cast<gemm::f32x4_t*>(dw + m * ldw + n);
-    *p = overwrite ? coef * a : *p + coef * a;
+  using Aux = gemm::f32x4_t;
+  __device__ __forceinline__ Aux load4(int64_t m, int64_t n) const {
+    if (overwrite) return Aux{0.f, 0.f, 0.f, 0.f};
+    return *reinterpret_cast<const gemm::f32x4_t*>(dw + m * ldw + n);
+  }
+  __device__ __forceinline__ void store4(int64_t m, int64_t n, gemm::f32x4_t a, Aux old) {
+    *reinterpret_cast<gemm::f32x4_t*>(dw + m * ldw + n) = old + coef * a;
   }
 };
 
@@ -128,8 +143,10 @@ struct EpiPartial {
   __device__ __forceinline__ void operator()(int64_t m, int64_t n, float a) {
     slice[gap_index((kz * M + m) * N + n)] = a;
   }
+  struct Aux {};
+  __device__ __forceinline__ Aux load4(int64_t, int64_t) const { return Aux{}; }
   // N % 4 == 0 and n % 4 == 0 keep the 4 values inside one 32-float gap
-  __device__ __forceinline__ void store4(int64_t m, int64_t n, gemm::f32x4_t a) {
+  __device__ __forceinline__ void store4(int64_t m, int64_t n, gemm::f32x4_t a, Aux) {
     *reinterpret_cast<gemm::f32x4_t*>(slice + gap_index((kz * M + m) * N + n)) = a;
   }
 };
@@ -157,7 +174,9 @@ __global__ void __launch_bounds__(256) grad_hidden_reduce_kernel(
 
 constexpr int kRowThreads = 256;
 
-// lse of one fp32 slice row; loss term and lse written for labelled rows.
+// lse of one fp32 slice row; loss term and lse written for labelled rows. 16-byte loads,
+// four in flight per lane; rows are 256-byte aligned (ldz % 64 == 0), so only the last
+// vector of a row can be partial.
 __global__ void __launch_bounds__(kRowThreads) slice_row_lse_kernel(
     const float* __restrict__ z, int64_t ldz, int64_t v, const int32_t* __restrict__ labels,
     int32_t ignore_index, float* __restrict__ lse_c, float* __restrict__ row_loss,
@@ -173,12 +192,39 @@ __global__ void __launch_bounds__(kRowThreads) slice_row_lse_kernel(
     return;
   }
   const float* row = z + i * ldz;
+  const float4* r4 = reinterpret_cast<const float4*>(row);
+  const int64_t nfull = v >> 2;
   float m = -INFINITY, s = 0.f;
-  for (int64_t c = threadIdx.x; c < v; c += kRowThreads) {
-    const float x = row[c];
-    const float mn = fmaxf(m, x);
-    s = (mn == m ? s : s * fast_exp2((m - mn) * kLog2e)) + fast_exp2((x - mn) * kLog2e);
+  auto absorb = [&](const float* x, int cnt) {
+    float mx = x[0];
+    for (int k = 1; k < cnt; ++k) mx = fmaxf(mx, x[k]);
+    const float mn = fmaxf(m, mx);
+    const float c = mn * kLog2e;
+    float acc = (m == mn) ? s : s * fast_exp2(fmaf(m, kLog2e, -c));
+    for (int k = 0; k < cnt; ++k) acc += fast_exp2(fmaf(x[k], kLog2e, -c));
+    s = acc;
     m = mn;
+  };
+  int64_t j = threadIdx.x;
+  for (; j + 3 * kRowThreads < nfull; j += 4 * kRowThreads) {
+    float4 q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) q[u] = r4[j + u * kRowThreads];
+    float x[16];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      x[4 * u] = q[u].x; x[4 * u + 1] = q[u].y; x[4 * u + 2] = q[u].z; x[4 * u + 3] = q[u].w;
+    }
+    absorb(x, 16);
+  }
+  for (; j < nfull; j += kRowThreads) {
+    const float4 q = r4[j];
+    const float x[4] = {q.x, q.y, q.z, q.w};
+    absorb(x, 4);
+  }
+  if (threadIdx.x < (v & 3)) {
+    const float x = row[nfull * 4 + threadIdx.x];
+    absorb(&x, 1);
   }
   __shared__ float sm[kRowThreads / 64], ss[kRowThreads / 64];
   wave_lse_reduce(m, s);
@@ -219,27 +265,35 @@ __global__ void __launch_bounds__(256) slice_bias_grad_kernel(
 }
 
 // In place: the fp32 logits of row i, column group g (bytes [256 g, 256 g + 256) of the row)
-// become 64 bf16 probabilities in the group's first 128 bytes. One wavefront owns one
-// group, and each lane's store depends on its own load, so no lane can overwrite bytes
-// another lane has yet to read.
+// become 64 bf16 probabilities in the group's first 128 bytes. Sixteen lanes of one
+// wavefront own a group: each loads 4 floats (16 B) and stores 4 bf16 (8 B) at a lower
+// address inside the same group; the wavefront's load completes for every lane before its
+// dependent store issues, so no lane overwrites bytes another lane has yet to read.
 __global__ void __launch_bounds__(256) slice_to_probs_kernel(float* z, int64_t ldz, int64_t v,
                                                              const int32_t* __restrict__ labels,
                                                              int32_t ignore_index,
                                                              const float* __restrict__ lse_c) {
   const int64_t i = blockIdx.y;
-  const int64_t g = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int64_t groups = ldz / kGroup;
-  if (g >= groups) return;
+  const int64_t g = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int L = threadIdx.x & 15;
+  if (g >= ldz / kGroup) return;
   const int32_t y = labels[i];
   const bool ok = has_label(y, v, ignore_index);
-  const int64_t col = g * kGroup + lane;
   float* row = z + i * ldz;
-  const float x = row[col];
-  float p = 0.f;
-  if (ok && col < v) p = fast_exp2((x - lse_c[i]) * kLog2e);
-  uint16_t* out = reinterpret_cast<uint16_t*>(row) + g * (2 * kGroup) + lane;
-  *out = f32_to_bf16(p);
+  const int64_t col = g * kGroup + 4 * L;
+  const float4 x = *reinterpret_cast<const float4*>(row + col);
+  const float c = ok ? lse_c[i] * kLog2e : 0.f;
+  float p[4] = {0.f, 0.f, 0.f, 0.f};
+  if (ok) {
+    const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (col + k < v) p[k] = fast_exp2(fmaf(xs[k], kLog2e, -c));
+  }
+  uint2 o;
+  o.x = pack_bf16x2(p[0], p[1]);
+  o.y = pack_bf16x2(p[2], p[3]);
+  *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(row) + g * (2 * kGroup) + 4 * L) = o;
 }
 
 // dW[y] −= coef · Σ_{i in chunk, y_i = y} h_i. The first chunk row carrying label y owns that
@@ -395,52 +449,47 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     const int64_t groups = ws.ldz / kGroup;
     {
       TimedLaunch t(s, K_FLCE_TO_PROBS);
-      hipLaunchKernelGGL(slice_to_probs_kernel, dim3(unsigned((groups + 3) / 4), unsigned(rows)),
+      hipLaunchKernelGGL(slice_to_probs_kernel, dim3(unsigned((groups + 15) / 16), unsigned(rows)),
                          dim3(256), 0, s, ws.slice, ws.ldz, v, lab, a.ignore_index, ws.lse_c);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const uint16_t* P = reinterpret_cast<const uint16_t*>(ws.slice);
     const int64_t p_ld = 2 * ws.ldz, p_gs = 2 * kGroup;
 
-    // 5. grad_hidden = coef (P W − W[y])
+    // 5.-7. gradients. grad_hidden splits K = V so that its few [rows, h] output tiles still
+    // fill the chip; its fp32 partials live in the free half of every slice group.
+    View Ap{P, p_ld, p_gs, rows, v};         // P: rows = chunk rows, cols = vocab (K-major)
+    View Bw2{a.weight, h, kGroup, v, h};      // W: rows = k (vocab), cols = n (hidden)
+    View Bh{hid, h, kGroup, rows, h};         // hidden chunk: rows = k, cols = n
+    const int64_t tiles = ((rows + gemm::BM - 1) / gemm::BM) * ((h + gemm::BN - 1) / gemm::BN);
+    const int64_t gap_cap = (rows * ws.ldz / 2) / (rows * h);  // partial sets that fit the gaps
+    int64_t splits = 256 / tiles;
+    if (splits > gap_cap) splits = gap_cap;
+    if (splits > (v + 2047) / 2048) splits = (v + 2047) / 2048;  // keep >= 2048 of K per split
+    if (splits < 1) splits = 1;
+    EpiGradHidden eh{a.grad_hidden + c0 * h, h, lab, a.weight, h, v, a.ignore_index,
+                     ws.count, th, a.grad_output, 0.f};
+    EpiPartial ep{ws.slice, rows, h, 0};
+    EpiGradWeight ew{a.grad_weight, h, int(first && !accumulate), ws.count, th, a.grad_output, 0.f};
     if (a.grad_hidden) {
-      View Ap{P, p_ld, p_gs, rows, v};
-      View Bw2{a.weight, h, kGroup, v, h};  // rows = k (vocab), cols = n (hidden)
-      // split K = V so the few [rows, h] output tiles still fill the chip
-      const int64_t tiles = ((rows + gemm::BM - 1) / gemm::BM) * ((h + gemm::BN - 1) / gemm::BN);
-      int64_t splits = 256 / tiles;
-      const int64_t gap_cap = (rows * ws.ldz / 2) / (rows * h);  // partials that fit the gaps
-      if (splits > gap_cap) splits = gap_cap;
-      if (splits > (v + 2047) / 2048) splits = (v + 2047) / 2048;  // keep >= 2048 of K per split
-      if (splits < 1) splits = 1;
-      if (splits == 1) {
-        EpiGradHidden eh{a.grad_hidden + c0 * h, h, lab, a.weight, h, v, a.ignore_index,
-                         ws.count, th, a.grad_output, 0.f};
-        TimedLaunch t(s, K_FLCE_GEMM_GRAD_HIDDEN);
-        if ((e = gemm::v2::launch<true, false>(Ap, Bw2, rows, h, v, 1, true, eh, s)) != hipSuccess) return e;
-      } else {
-        EpiPartial ep{ws.slice, rows, h, 0};
-        {
-          TimedLaunch t(s, K_FLCE_GEMM_GRAD_HIDDEN);
-          if ((e = gemm::v2::launch<true, false>(Ap, Bw2, rows, h, v, splits, true, ep, s)) != hipSuccess)
-            return e;
-        }
-        TimedLaunch t(s, K_FLCE_GRAD_HIDDEN_REDUCE);
-        hipLaunchKernelGGL(grad_hidden_reduce_kernel, dim3(unsigned((rows * h + 255) / 256)),
-                           dim3(256), 0, s, ws.slice, rows, h, splits, a.grad_hidden + c0 * h, lab,
-                           a.weight, v, a.ignore_index, ws.count, th, a.grad_output);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-      }
+      TimedLaunch t(s, K_FLCE_GEMM_GRAD_HIDDEN);
+      e = splits == 1 ? gemm::v2::launch<true, false>(Ap, Bw2, rows, h, v, 1, true, eh, s)
+                      : gemm::v2::launch<true, false>(Ap, Bw2, rows, h, v, splits, true, ep, s);
+      if (e != hipSuccess) return e;
     }
-    // 6./7. grad_weight
     if (a.grad_weight) {
-      View Apt{P, p_ld, p_gs, rows, v};        // rows = k (chunk row), cols = m (vocab)
-      View Bh{hid, h, kGroup, rows, h};       // rows = k, cols = n
-      EpiGradWeight ew{a.grad_weight, h, int(first && !accumulate), ws.count, th, a.grad_output, 0.f};
-      {
-        TimedLaunch t(s, K_FLCE_GEMM_GRAD_WEIGHT);
-        if ((e = gemm::v2::launch<false, false>(Apt, Bh, v, h, rows, 1, false, ew, s)) != hipSuccess) return e;
-      }
+      TimedLaunch t(s, K_FLCE_GEMM_GRAD_WEIGHT);
+      if ((e = gemm::v2::launch<false, false>(Ap, Bh, v, h, rows, 1, false, ew, s)) != hipSuccess)
+        return e;
+    }
+    if (a.grad_hidden && splits > 1) {
+      TimedLaunch t(s, K_FLCE_GRAD_HIDDEN_REDUCE);
+      hipLaunchKernelGGL(grad_hidden_reduce_kernel, dim3(unsigned((rows * h + 255) / 256)),
+                         dim3(256), 0, s, ws.slice, rows, h, splits, a.grad_hidden + c0 * h, lab,
+                         a.weight, v, a.ignore_index, ws.count, th, a.grad_output);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (a.grad_weight) {
       TimedLaunch t(s, K_FLCE_ONEHOT_FIX);
       hipLaunchKernelGGL(onehot_weight_fix_kernel, dim3(unsigned(rows)), dim3(256), 0, s, hid, h,
                          rows, lab, a.ignore_index, v, a.grad_weight, ws.count, th, a.grad_output);
