@@ -257,13 +257,21 @@ hipError_t launch(const View& A, const View& B, int64_t M, int64_t N, int64_t K,
 // read as zero (true for the probability slice, whose padding is zero-filled).
 namespace v2 {
 
-constexpr int BK2 = 32;
+// K per pipeline stage. 64 makes every DMA row segment of a K-major operand a full 128-byte
+// line (32 leaves 64-byte segments, which measured at half the L2->LDS throughput).
+#ifndef LCE_GEMM_BK
+#define LCE_GEMM_BK 64
+#endif
+constexpr int BK2 = LCE_GEMM_BK;
 #ifndef LCE_GEMM_STAGES
-#define LCE_GEMM_STAGES 4
+#define LCE_GEMM_STAGES (LCE_GEMM_BK == 64 ? 2 : 4)
 #endif
 constexpr int kStages = LCE_GEMM_STAGES;
-constexpr int kOpBytes = 256 * BK2 * 2;        // 16 KiB per operand per stage
+constexpr int kOpBytes = 256 * BK2 * 2;        // one operand per stage
 constexpr int kStageBytes2 = 2 * kOpBytes;     // A + B
+constexpr int kRowBytes = BK2 * 2;             // K-major row in LDS
+constexpr int kChunks = BK2 / 8;               // 16-byte chunks per K-major row
+constexpr int kIPS = kOpBytes / 1024;          // 1 KiB DMA instructions per operand per stage
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -272,20 +280,23 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // (lanes 0-15 = 16 consecutive rows, one 16-byte chunk each) XOR with (row >> 1) & 3 is
 // conflict-free, while XOR with row & 3 or no swizzle costs about 2x in LDS cycles. It does
 // not depend on the fragment's 16-row block, so fragment addresses differ by constants only.
-__device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 3; }
+__device__ __forceinline__ int swz_k(int r) {
+  // 128-byte rows: XOR with row & 7 (measured conflict-free as well)
+  return kChunks == 8 ? (r & 7) : ((r >> 1) & 3);
+}
 __device__ __forceinline__ int swz_mn(int k) { return 2 * ((k & 3) | ((k >> 1) & 4)); }
 
 // Per-lane byte offsets (within one stage's global window) of the lane's DMA loads. One
-// operand slice is 16 instructions of 1 KiB; with NW wavefronts each issues 16 / NW of them.
+// operand stage is kIPS instructions of 1 KiB; with NW wavefronts each issues kIPS / NW.
 template <bool KMAJOR, int NW>
-__device__ __forceinline__ void dma_offsets(const View& X, uint32_t (&off)[16 / NW]) {
+__device__ __forceinline__ void dma_offsets(const View& X, uint32_t (&off)[kIPS / NW]) {
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-  for (int j = 0; j < 16 / NW; ++j) {
-    const int g = w * (16 / NW) + j;  // instruction index within the slice
+  for (int j = 0; j < kIPS / NW; ++j) {
+    const int g = w * (kIPS / NW) + j;  // instruction index within the stage
     if constexpr (KMAJOR) {
-      const int r = 16 * g + (l >> 2);
-      const int c = (l & 3) ^ swz_k(r);
+      const int r = (64 / kChunks) * g + l / kChunks;  // 64 / kChunks rows per instruction
+      const int c = (l % kChunks) ^ swz_k(r);
       off[j] = uint32_t((int64_t(r) * X.ld + 8 * c) * 2);
     } else {
       const int k = 2 * g + (l >> 5);
@@ -329,7 +340,7 @@ __device__ __forceinline__ void dma16(i32x4_t rs, uint32_t voff, char* dst) {
 // Issue one operand's loads for the K slice starting at k0 into `lds` (this stage's tile).
 template <bool KMAJOR, int NW>
 __device__ __forceinline__ void dma_issue(const View& X, int64_t r0, int64_t k0, int64_t K,
-                                          const uint32_t (&off)[16 / NW], char* lds) {
+                                          const uint32_t (&off)[kIPS / NW], char* lds) {
   const int w = threadIdx.x >> 6;
   i32x4_t rs;
   if constexpr (KMAJOR) {
@@ -340,21 +351,22 @@ __device__ __forceinline__ void dma_issue(const View& X, int64_t r0, int64_t k0,
     rs = rsrc_words(X.p + k0 * X.ld + (r0 >> 6) * X.gs, kr * X.ld * 2);
   }
 #pragma unroll
-  for (int j = 0; j < 16 / NW; ++j) dma16(rs, off[j], lds + (w * (16 / NW) + j) * 1024);
+  for (int j = 0; j < kIPS / NW; ++j) dma16(rs, off[j], lds + (w * (kIPS / NW) + j) * 1024);
 }
 
-// One 16 × 32 MFMA operand fragment for rows rbase .. rbase+15 of the stage tile.
+// One 16 × 32 MFMA operand fragment for rows rbase .. rbase+15 and k = 32 kk .. 32 kk + 31 of
+// the stage tile.
 template <bool KMAJOR>
-__device__ __forceinline__ bf16x8_t frag(const char* lds, int rbase) {
+__device__ __forceinline__ bf16x8_t frag(const char* lds, int rbase, int kk = 0) {
   const int l = threadIdx.x & 63;
   if constexpr (KMAJOR) {
     const int r = rbase + (l & 15);
-    const int c = (l >> 4) ^ swz_k(r);
-    return *reinterpret_cast<const bf16x8_t*>(lds + r * 64 + c * 16);
+    const int c = (4 * kk + (l >> 4)) ^ swz_k(r);
+    return *reinterpret_cast<const bf16x8_t*>(lds + r * kRowBytes + c * 16);
   } else {
     const int g = l >> 4, L = l & 15;
     const int m = rbase + 4 * (L & 3);
-    const int k0 = 8 * g + (L >> 2), k1 = k0 + 4;
+    const int k0 = 32 * kk + 8 * g + (L >> 2), k1 = k0 + 4;
     const int c = m >> 3, h = ((m >> 2) & 1) * 8;
     const char* p0 = lds + k0 * 512 + ((c ^ swz_mn(k0)) << 4) + h;
     const char* p1 = lds + k1 * 512 + ((c ^ swz_mn(k1)) << 4) + h;
@@ -366,31 +378,6 @@ __device__ __forceinline__ bf16x8_t frag(const char* lds, int rbase) {
   }
 }
 
-// Operand fragment of v_mfma_f32_32x32x16_bf16: rows rbase .. rbase+31, k = 16 kh .. 16 kh + 15
-// of the stage tile; lane l holds row rbase + l % 32, k = 16 kh + 8 (l / 32) .. + 7.
-template <bool KMAJOR>
-__device__ __forceinline__ bf16x8_t frag32(const char* lds, int rbase, int kh) {
-  const int l = threadIdx.x & 63;
-  if constexpr (KMAJOR) {
-    const int r = rbase + (l & 31);
-    const int c = (2 * kh + (l >> 5)) ^ swz_k(r);
-    return *reinterpret_cast<const bf16x8_t*>(lds + r * 64 + c * 16);
-  } else {
-    const int g = l >> 4, L = l & 15;
-    const int m = rbase + 16 * (g & 1) + 4 * (L & 3);
-    const int k0 = 16 * kh + 8 * (g >> 1) + (L >> 2), k1 = k0 + 4;
-    const int c = m >> 3, h = ((m >> 2) & 1) * 8;
-    const char* p0 = lds + k0 * 512 + ((c ^ swz_mn(k0)) << 4) + h;
-    const char* p1 = lds + k1 * 512 + ((c ^ swz_mn(k1)) << 4) + h;
-    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p0);
-    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p1);
-    typedef short v8s __attribute__((ext_vector_type(8)));
-    const v8s v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8_t, v);
-  }
-}
-
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // s_waitcnt vmcnt(n) with the other counters untouched; n is a multiple of the per-slice
 // instruction count and at most 4 slices.
@@ -415,7 +402,7 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
                                          int64_t tile, Epi& epi, char* lds) {
   constexpr int NW = WM * WN;
   constexpr int TM = 256 / WM / 16, TN = 256 / WN / 16;
-  constexpr int PER = 2 * (16 / NW);  // DMA instructions per slice per wavefront
+  constexpr int PER = 2 * (kIPS / NW);  // DMA instructions per stage per wavefront
   const int64_t mn = tm.m_tiles * tm.n_tiles;
   const int64_t kz = tile / mn;
   const int64_t rest = tile % mn;
@@ -430,7 +417,7 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
   const int wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
-  uint32_t offa[16 / NW], offb[16 / NW];
+  uint32_t offa[kIPS / NW], offb[kIPS / NW];
   dma_offsets<AK, NW>(A, offa);
   dma_offsets<BKM, NW>(B, offb);
 
@@ -464,19 +451,22 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
     // reads below from the MFMAs that wait on them one by one
     if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
     const char* st = slot(kt);
-    bf16x8_t bf[TN], af[TM];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bf[j] = frag<BKM>(st + kOpBytes, wn * (256 / WN) + 16 * j);
+    for (int kk = 0; kk < BK2 / 32; ++kk) {
+      bf16x8_t bf[TN], af[TM];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) af[i] = frag<AK>(st, wm * (256 / WM) + 16 * i);
-    // all fragment reads are in flight before the first MFMA; the MFMAs then wait on them
-    // one by one instead of the scheduler trading registers for exposed LDS latency
-    __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < TN; ++j) bf[j] = frag<BKM>(st + kOpBytes, wn * (256 / WN) + 16 * j, kk);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i) af[i] = frag<AK>(st, wm * (256 / WM) + 16 * i, kk);
+      // all fragment reads are in flight before the first MFMA; the MFMAs then wait on them
+      // one by one instead of the scheduler trading registers for exposed LDS latency
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+    }
   }
 
   // Epilogue in batches of two 16-row blocks: every load a batch needs (old accumulator
@@ -523,111 +513,6 @@ __global__ void __launch_bounds__(64 * WM * WN, 1)
   run_tile<WM, WN, AK, BKM>(A, B, M, N, K, ksplit, tm, xcd_tile(blockIdx.x, total), epi, lds);
 }
 
-template <int WM, int WN, bool AK, bool BKM, class Epi>
-__global__ void __launch_bounds__(64 * WM * WN, 1)
-    gemm256p32_kernel(View A, View B, int64_t M, int64_t N, int64_t K, int64_t ksplit, TileMap tm,
-                    Epi epi) {
-  constexpr int NW = WM * WN;
-  constexpr int TM = 256 / WM / 32, TN = 256 / WN / 32;
-  constexpr int PER = 2 * (16 / NW);  // DMA instructions per slice per wavefront
-  __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageBytes2];
-
-  const int64_t total = tm.m_tiles * tm.n_tiles * tm.splits;
-  const int64_t tile = xcd_tile(blockIdx.x, total);
-  const int64_t mn = tm.m_tiles * tm.n_tiles;
-  const int64_t kz = tile / mn;
-  const int64_t rest = tile % mn;
-  const int64_t mt = tm.m_fast ? rest % tm.m_tiles : rest / tm.n_tiles;
-  const int64_t nt = tm.m_fast ? rest / tm.m_tiles : rest % tm.n_tiles;
-  const int64_t m0 = mt * BM, n0 = nt * BN;
-  const int64_t kbeg = kz * ksplit;
-  const int64_t kend = kbeg + ksplit < K ? kbeg + ksplit : K;
-  const int nk = kend > kbeg ? int((kend - kbeg + BK2 - 1) / BK2) : 0;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-
-  uint32_t offa[16 / NW], offb[16 / NW];
-  dma_offsets<AK, NW>(A, offa);
-  dma_offsets<BKM, NW>(B, offb);
-
-  f32x16_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  int issued = 0;  // slices whose DMA has been issued (the same count in every wavefront)
-  auto slot = [&](int s) { return lds + (s % kStages) * kStageBytes2; };
-  auto issue = [&](int s) {
-    char* st = slot(s);
-    const int64_t k0 = kbeg + int64_t(s) * BK2;
-    dma_issue<AK, NW>(A, m0, k0, K, offa, st);
-    dma_issue<BKM, NW>(B, n0, k0, K, offb, st + kOpBytes);
-    ++issued;
-  };
-
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < nk) issue(s);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    // slice kt has landed once at most the later slices' DMA is pending; then sync the block
-    // with a bare barrier (a __syncthreads() fence would drain the later slices too)
-    wait_vm(PER * (issued - 1 - kt));
-    __builtin_amdgcn_s_barrier();
-    const char* st = slot(kt);
-    bf16x8_t bf[2][TN], af[2][TM];
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bf[kh][j] = frag32<BKM>(st + kOpBytes, wn * (256 / WN) + 32 * j, kh);
-#pragma unroll
-      for (int i = 0; i < TM; ++i) af[kh][i] = frag32<AK>(st, wm * (256 / WM) + 32 * i, kh);
-    }
-    // refill the slot of slice kt-1: every wavefront's reads of it were consumed by its
-    // MFMAs before it reached this barrier
-    if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[kh][j], af[kh][i], acc[i][j], 0, 0, 0);
-  }
-
-  epi.begin(kz);
-  // lane l, register 4 g + q holds output row 32 i + l % 32, column 32 j + 8 g + 4 (l / 32) + q
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int64_t gm = m0 + wm * (256 / WM) + 32 * i + (lane & 31);
-    if (gm >= M) continue;
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t gn = n0 + wn * (256 / WN) + 32 * j + 8 * g + 4 * (lane >> 5);
-        const f32x4_t v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                           acc[i][j][4 * g + 3]};
-        if (gn + 4 <= N) {
-          epi.store4(gm, gn, v, epi.load4(gm, gn));
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (gn + q < N) epi(gm, gn + q, v[q]);
-        }
-      }
-  }
-}
-
-#ifndef LCE_GEMM_MFMA32
-#define LCE_GEMM_MFMA32 0
-#endif
-
 #ifndef LCE_GEMM_WM
 #define LCE_GEMM_WM 2
 #endif
@@ -643,17 +528,11 @@ hipError_t launch(const View& A, const View& B, int64_t M, int64_t N, int64_t K,
   ksplit = (ksplit + BK2 - 1) / BK2 * BK2;
   const int64_t total = tm.m_tiles * tm.n_tiles * tm.splits;
   constexpr int WM = LCE_GEMM_WM, WN = LCE_GEMM_WN;
-#if LCE_GEMM_MFMA32
-  hipLaunchKernelGGL((gemm256p32_kernel<WM, WN, AK, BKM, Epi>), dim3(unsigned(total)),
-                     dim3(64 * WM * WN), 0, s, A, B, M, N, K, ksplit, tm, epi);
-#else
   hipLaunchKernelGGL((gemm256p_kernel<WM, WN, AK, BKM, Epi>), dim3(unsigned(total)),
                      dim3(64 * WM * WN), 0, s, A, B, M, N, K, ksplit, tm, epi);
-#endif
   return hipGetLastError();
 }
 
 }  // namespace v2
 }  // namespace gemm
 }  // namespace lce
-
