@@ -60,6 +60,93 @@ def stored_traffic(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
+# rocprofv3 kernel names -> the library's launch-timing names (first match wins)
+KERNEL_NAMES = [
+    ("EpiLogits", "flce_gemm_logits"), ("EpiGradHidden", "flce_gemm_grad_hidden"),
+    ("EpiPartial", "flce_gemm_grad_hidden"), ("EpiGradWeight", "flce_gemm_grad_weight"),
+    ("slice_row_lse_kernel", "flce_row_lse"), ("slice_bias_grad_kernel", "flce_bias_grad"),
+    ("slice_to_probs_kernel", "flce_to_probs"), ("onehot_weight_fix_kernel", "flce_onehot_fix"),
+    ("grad_hidden_reduce_kernel", "flce_grad_hidden_reduce"), ("fill_zero", "fill_zero"),
+    ("label_prep_kernel", "label_prep"), ("loss_reduce_kernel", "loss_reduce"),
+    ("ce_fwd_rows_kernel", "ce_fwd_rows"), ("ce_bwd_rows_kernel", "ce_bwd_rows"),
+]
+CALIB_BYTES = 1 << 30  # bytes read and bytes written by one launch of the calibration copy
+
+
+def copy_calibration(torch):
+    """Three launches of a plain elementwise copy (negation) of 1 GiB of bf16: what FETCH_SIZE
+    and WRITE_SIZE read for it converts the counters of the library's kernels to bytes."""
+    dev = torch.device("cuda:0")
+    src = torch.ones(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def _counter_means(run_dir, counter):
+    """Mean of `counter` per dispatch, per kernel name, over every counter_collection.csv."""
+    import csv
+    import glob
+    tot, disp = {}, {}
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                k = r["Kernel_Name"]
+                tot[k] = tot.get(k, 0.0) + float(r["Counter_Value"])
+                disp.setdefault(k, set()).add(r["Dispatch_Id"])
+    return {k: tot[k] / len(disp[k]) for k in tot}
+
+
+def record_traffic(workload, fetch_dir, write_dir):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch) of
+    `bench.py --only <layer> --copy-calibration` into HBM bytes per launch of each library
+    kernel, scaled by the calibration copy's readings, and store them in profiles/traffic.json
+    under the current source digest."""
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+
+    def calib(m):
+        ks = [k for k in m if "neg_kernel" in k]
+        if not ks:
+            raise SystemExit("calibration copy kernel not found in the counter run")
+        return CALIB_BYTES / (max(m[k] for k in ks) * 1024.0)
+
+    f_scale, w_scale = calib(fetch), calib(write)
+    out = {}
+    for m, scale, key in ((fetch, f_scale, "read_bytes"), (write, w_scale, "write_bytes")):
+        for k, kib in m.items():
+            name = next((n for sub, n in KERNEL_NAMES if sub in k), None)
+            if name is None:
+                continue
+            rec = out.setdefault(name, {"raw_kib": {}})
+            rec[key] = rec.get(key, 0.0) + kib * 1024.0 * scale
+            rec["raw_kib"][key] = rec["raw_kib"].get(key, 0.0) + kib
+    path = os.path.join(PROFILE_DIR, "traffic.json")
+    table = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            table = json.load(f)
+    digest = source_digest()
+    for name, rec in out.items():
+        rd, wr = rec.get("read_bytes", 0.0), rec.get("write_bytes", 0.0)
+        table[f"{name}@{workload}"] = {
+            "bytes_per_launch": int(round(rd + wr)), "read_bytes": int(round(rd)),
+            "write_bytes": int(round(wr)), "raw_kib_per_dispatch": rec["raw_kib"],
+            "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
+            "source_digest": digest}
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+    print(json.dumps({k: v for k, v in table.items() if k.endswith("@" + workload)}, indent=1))
+
+
 def ce_algorithmic_bytes(n, v, nvalid):
     """Bytes the method must move: forward reads each labelled row once; the in-place backward
     reads each labelled row and writes every row (ignored rows are zero-filled)."""
@@ -67,6 +154,23 @@ def ce_algorithmic_bytes(n, v, nvalid):
     bwd_read = nvalid * v * 2
     bwd_write = n * v * 2
     return fwd, bwd_read + bwd_write
+
+
+def timed_kernels(torch, lce, stream, step, steps):
+    """Run `steps` more steps with the library's per-launch hipEvents on; returns (steps,
+    instrumented ms/step, [(kernel, total ms, launches)])."""
+    lce.lce_timing_enable(True)
+    lce.lce_timing_read()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(steps):
+        step()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    kernels = lce.lce_timing_read()
+    lce.lce_timing_enable(False)
+    return steps, ev[0].elapsed_time(ev[1]) / steps, kernels
 
 
 def run_flce(args, torch, lce, workloads):
@@ -107,22 +211,16 @@ def run_flce(args, torch, lce, workloads):
     ms = ev[0].elapsed_time(ev[1]) / args.steps
     peak_extra = torch.cuda.max_memory_allocated(dev) - mem_before + ws.numel()
 
-    # per-kernel breakdown (separate pass: events around every launch)
-    lce.lce_timing_enable(True)
-    lce.lce_timing_read()
-    kreps = max(1, min(3, args.steps))
-    for _ in range(kreps):
-        step()
-    torch.cuda.synchronize()
-    kernels = lce.lce_timing_read()
-    lce.lce_timing_enable(False)
+    # per-kernel breakdown: the same K steps again with a hipEvent pair around every launch,
+    # recorded by the library on the stream it launches on
+    kreps, inst_ms, kernels = timed_kernels(torch, lce, stream, step, args.steps)
 
     flops = 6.0 * w.n * w.h * w.v
     chunks = -(-w.n // w.chunk_size)
     one = 2.0 * w.chunk_size * w.h * w.v  # one chunk's product (every chunk is full here)
-    # algorithmic flops per launch of each MFMA kernel: the paired launch runs two products
+    # algorithmic flops per launch of each MFMA kernel (one chunk's product)
     per_launch = {"flce_gemm_logits": one, "flce_gemm_grad_hidden": one,
-                  "flce_gemm_grad_weight": one, "flce_gemm_grad_hidden_and_weight": 2 * one}
+                  "flce_gemm_grad_weight": one}
     gemms = [k for k in kernels if k[0] in per_launch]
     dom = max(gemms, key=lambda k: k[1]) if gemms else None
     roof = None
@@ -137,6 +235,7 @@ def run_flce(args, torch, lce, workloads):
     return {
         "workload": w, "ms": ms, "wall_s": wall, "tokens_per_s": w.n / (ms * 1e-3),
         "tflops": flops / (ms * 1e-3) / 1e12, "loss": float(loss.item()), "roofline": roof,
+        "instrumented_ms": inst_ms,
         "kernels": {k[0]: {"ms_per_step": round(k[1] / kreps, 4), "launches_per_step": k[2] // kreps}
                     for k in kernels},
         "peak_extra_bytes": int(peak_extra), "slice_budget_bytes": int(w.chunk_size * w.v * 4),
@@ -188,14 +287,7 @@ def run_ce(args, torch, lce, workloads):
     bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     ms = fwd_ms + bwd_ms
 
-    lce.lce_timing_enable(True)
-    lce.lce_timing_read()
-    kreps = max(1, min(3, args.steps))
-    for _ in range(kreps):
-        step(False)
-    torch.cuda.synchronize()
-    kernels = lce.lce_timing_read()
-    lce.lce_timing_enable(False)
+    kreps, inst_ms, kernels = timed_kernels(torch, lce, stream, lambda: step(False), args.steps)
     kd = {k[0]: k for k in kernels}
     roof = None
     if "ce_bwd_rows" in kd:
@@ -213,6 +305,7 @@ def run_ce(args, torch, lce, workloads):
         "tokens_per_s": w.n / (ms * 1e-3), "gbs": tot_gbs, "fwd_gbs": fwd_gbs,
         "bwd_gbs": bwd_bytes / (bwd_ms * 1e-3) / 1e9, "loss": float(loss.item()),
         "roofline": roof, "algorithmic_bytes": fwd_bytes + bwd_bytes, "gen_s": gen_s,
+        "instrumented_ms": inst_ms,
         "kernels": {k[0]: {"ms_per_step": round(k[1] / kreps, 4), "launches_per_step": k[2] // kreps}
                     for k in kernels},
         "inputs": inp, "nvalid": nvalid,
@@ -231,10 +324,10 @@ def blas_threads():
 
 
 def cpu_baseline_flce(res):
-    """The fp64 oracle on the first 256 tokens of the same workload (all of the weight)."""
+    """The fp64 oracle on the first 4096 tokens of the same workload (all of the weight)."""
     import oracle
     inp = res["inputs"]
-    k = 256
+    k = 4096
     t0 = time.perf_counter()
     oracle.flce(inp.hidden[:k], inp.weight, inp.labels[:k], num_label_tokens=res["nvalid"],
                 row_block=256)
@@ -246,10 +339,10 @@ def cpu_baseline_flce(res):
 
 
 def cpu_baseline_ce(res):
-    """The fp64 oracle on the first 2048 rows of the same logits."""
+    """The fp64 oracle on all 16384 rows of the same logits."""
     import oracle
     inp = res["inputs"]
-    k = 2048
+    k = res["workload"].n
     t0 = time.perf_counter()
     oracle.ce_masked_sum_bits(inp.logits[:k], inp.labels[:k], num_label_tokens=res["nvalid"],
                               row_block=256)
@@ -268,7 +361,16 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["flce", "ce"], default=None,
                     help="run one layer only (profiling)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a 1 GiB copy whose HBM counters calibrate the others")
+    ap.add_argument("--record-traffic", nargs=3, metavar=("LAYER", "FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: store HBM bytes per launch from two rocprofv3 --pmc runs "
+                         "(FETCH_SIZE, WRITE_SIZE) of --only LAYER --copy-calibration")
     args = ap.parse_args(argv)
+    if args.record_traffic:
+        layer, fdir, wdir = args.record_traffic
+        record_traffic({"flce": FLCE_WORKLOAD, "ce": CE_WORKLOAD}[layer], fdir, wdir)
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -284,6 +386,8 @@ def main(argv=None) -> int:
         print("no GPU visible", file=sys.stderr)
         return 2
     lce.load_library()
+    if args.copy_calibration:
+        copy_calibration(torch)
 
     out = {"metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": None,
