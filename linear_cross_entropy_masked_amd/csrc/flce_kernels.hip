@@ -37,6 +37,8 @@ constexpr int kGroup = 64;  // column-group width of the logits slice / probabil
 __host__ __device__ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 using gemm::View;
+using Wide = gemm::v2::CfgWide;  // the two large-K products
+using Pair = gemm::v2::CfgPair;  // grad_weight: fp32 read-modify-write epilogue
 
 __device__ __forceinline__ float flce_coef(const long long* count_dev, long long count_host,
                                            const float* gout) {
@@ -421,8 +423,8 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     EpiLogits el{ws.slice, ws.ldz, a.bias};
     {
       TimedLaunch t(s, K_FLCE_GEMM_LOGITS);
-      e = (h % gemm::v2::BK2 == 0) ? gemm::v2::launch<true, true>(Ah, Bw, rows, v, h, 1, true, el, s)
-                                   : gemm::launch<true, true>(Ah, Bw, rows, v, h, 1, true, el, s);
+      e = (h % Wide::BK == 0) ? gemm::v2::launch<Wide, true, true>(Ah, Bw, rows, v, h, 1, true, el, s)
+                              : gemm::launch<true, true>(Ah, Bw, rows, v, h, 1, true, el, s);
       if (e != hipSuccess) return e;
     }
 
@@ -461,7 +463,7 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     View Ap{P, p_ld, p_gs, rows, v};         // P: rows = chunk rows, cols = vocab (K-major)
     View Bw2{a.weight, h, kGroup, v, h};      // W: rows = k (vocab), cols = n (hidden)
     View Bh{hid, h, kGroup, rows, h};         // hidden chunk: rows = k, cols = n
-    const int64_t tiles = ((rows + gemm::BM - 1) / gemm::BM) * ((h + gemm::BN - 1) / gemm::BN);
+    const int64_t tiles = ((rows + Wide::BM - 1) / Wide::BM) * ((h + Wide::BN - 1) / Wide::BN);
     const int64_t gap_cap = (rows * ws.ldz / 2) / (rows * h);  // partial sets that fit the gaps
     int64_t splits = 256 / tiles;
     if (splits > gap_cap) splits = gap_cap;
@@ -473,13 +475,13 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     EpiGradWeight ew{a.grad_weight, h, int(first && !accumulate), ws.count, th, a.grad_output, 0.f};
     if (a.grad_hidden) {
       TimedLaunch t(s, K_FLCE_GEMM_GRAD_HIDDEN);
-      e = splits == 1 ? gemm::v2::launch<true, false>(Ap, Bw2, rows, h, v, 1, true, eh, s)
-                      : gemm::v2::launch<true, false>(Ap, Bw2, rows, h, v, splits, true, ep, s);
+      e = splits == 1 ? gemm::v2::launch<Wide, true, false>(Ap, Bw2, rows, h, v, 1, true, eh, s)
+                      : gemm::v2::launch<Wide, true, false>(Ap, Bw2, rows, h, v, splits, true, ep, s);
       if (e != hipSuccess) return e;
     }
     if (a.grad_weight) {
       TimedLaunch t(s, K_FLCE_GEMM_GRAD_WEIGHT);
-      if ((e = gemm::v2::launch<false, false>(Ap, Bh, v, h, rows, 1, false, ew, s)) != hipSuccess)
+      if ((e = gemm::v2::launch<Pair, false, false>(Ap, Bh, v, h, rows, 1, false, ew, s)) != hipSuccess)
         return e;
     }
     if (a.grad_hidden && splits > 1) {

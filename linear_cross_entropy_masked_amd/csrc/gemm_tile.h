@@ -87,7 +87,10 @@ __device__ __forceinline__ void load_tile(const View& X, int64_t r0, int64_t k0,
     }
   } else {
     const int64_t kr = (X.rows < K ? X.rows : K) - k0;  // valid k rows from k0
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(X.p + k0 * X.ld + (r0 >> 6) * X.gs, kr * X.ld * 2);
+    const int64_t shift = (r0 >> 6) * X.gs;              // window ends with the matrix too
+    const int64_t avail = (X.rows - k0) * X.ld - shift;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(X.p + k0 * X.ld + shift, (kr * X.ld < avail ? kr * X.ld : avail) * 2);
     const uint32_t row = uint32_t(X.ld * 2);
 #pragma unroll
     for (int b = 0; b < 2; ++b)
@@ -244,63 +247,80 @@ hipError_t launch(const View& A, const View& B, int64_t M, int64_t N, int64_t K,
 
 // ============================================================================ pipelined variant
 //
-// Same 256 × 256 tile and 2 × 2 wavefront split, but operands go global -> LDS directly
-// (buffer_load ... lds, 16 bytes per lane, no registers involved) into a 4-stage ring of
-// K = 32 slices, three slices ahead of the MFMAs. LDS layouts:
-//   K-major operand : [256 rows][32 k]   (64 B rows, 16-byte chunks XOR-swizzled by row)
-//   MN-major operand: [32 k][256 rows]   (512 B rows, 32-byte pairs XOR-swizzled by k),
+// Operands go global -> LDS directly (buffer_load ... lds, 16 bytes per lane, no registers
+// involved) into a ring of STAGES K-slices of depth BK, STAGES - 1 slices ahead of the MFMAs.
+// LDS layouts of one slice:
+//   K-major operand : [R rows][BK k]   (2·BK-byte rows, 16-byte chunks XOR-swizzled by row)
+//   MN-major operand: [BK k][R rows]   (2·R-byte rows, 32-byte pairs XOR-swizzled by k),
 //                     read back with ds_read_b64_tr_b16, which hands each lane 4
 //                     consecutive k of one row — the MFMA operand order.
 // The MFMA is issued with B as its first operand, so each lane ends up owning 4 consecutive
 // output columns of one row (16-byte epilogue accesses).
-// Requirement: for a K-major operand, K must be a multiple of 32 or the columns past K must
+// Requirement: for a K-major operand, K must be a multiple of BK or the columns past K must
 // read as zero (true for the probability slice, whose padding is zero-filled).
 namespace v2 {
 
-// K per pipeline stage. 64 makes every DMA row segment of a K-major operand a full 128-byte
-// line (32 leaves 64-byte segments, which measured at half the L2->LDS throughput).
-#ifndef LCE_GEMM_BK
-#define LCE_GEMM_BK 64
-#endif
-constexpr int BK2 = LCE_GEMM_BK;
-#ifndef LCE_GEMM_STAGES
-#define LCE_GEMM_STAGES (LCE_GEMM_BK == 64 ? 2 : 4)
-#endif
-constexpr int kStages = LCE_GEMM_STAGES;
-constexpr int kOpBytes = 256 * BK2 * 2;        // one operand per stage
-constexpr int kStageBytes2 = 2 * kOpBytes;     // A + B
-constexpr int kRowBytes = BK2 * 2;             // K-major row in LDS
-constexpr int kChunks = BK2 / 8;               // 16-byte chunks per K-major row
-constexpr int kIPS = kOpBytes / 1024;          // 1 KiB DMA instructions per operand per stage
+// Tile shape and pipeline of one instantiation.
+//   BM × BN outputs per workgroup, WM × WN wavefronts (each owns (BM/WM) × (BN/WN)),
+//   K slices of BK (64 makes every DMA row segment of a K-major operand a full 128-byte line;
+//   32 leaves 64-byte segments, which measured at half the L2->LDS throughput), STAGES slices
+//   in the LDS ring, OCC workgroups meant to share one CU (register and LDS budgets).
+template <int BM_, int BN_, int BK_, int STAGES_, int WM_, int WN_, int OCC_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, WM = WM_, WN = WN_;
+  static constexpr int OCC = OCC_, NW = WM * WN, THREADS = 64 * NW;
+  static constexpr int ABytes = BM * BK * 2, BBytes = BN * BK * 2;
+  static constexpr int StageBytes = ABytes + BBytes, LdsBytes = STAGES * StageBytes;
+  static constexpr int PA = ABytes / 1024 / NW, PB = BBytes / 1024 / NW;  // DMA per wave
+  static constexpr int PER = PA + PB;
+  static constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
+  static_assert(BK == 32 || BK == 64, "BK");
+  static_assert(PA * NW * 1024 == ABytes && PB * NW * 1024 == BBytes, "DMA split");
+  static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile");
+  static_assert(BM == 128 || BM == 256, "MN-major rows are 256 or 512 bytes");
+  static_assert(BN == 128 || BN == 256, "MN-major rows are 256 or 512 bytes");
+  static_assert(LdsBytes * OCC <= 160 * 1024, "LDS");
+  static_assert(PER * (STAGES - 1) <= 63, "vmcnt");
+};
+
+// Large-K products: one 256 × 256 workgroup per CU, 8 wavefronts, K = 64 slices, 2 stages.
+using CfgWide = Cfg<256, 256, 64, 2, 2, 4, 1>;
+// Products whose epilogue streams HBM (fp32 read-modify-write): two 256 × 128 workgroups per
+// CU, so one's epilogue overlaps the other's MFMAs; K = 32 slices, 3 stages.
+using CfgPair = Cfg<256, 128, 32, 3, 2, 2, 2>;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Chunk swizzle of the K-major [256][32] tile. Measured on gfx950: for 16-row fragment reads
-// (lanes 0-15 = 16 consecutive rows, one 16-byte chunk each) XOR with (row >> 1) & 3 is
-// conflict-free, while XOR with row & 3 or no swizzle costs about 2x in LDS cycles. It does
-// not depend on the fragment's 16-row block, so fragment addresses differ by constants only.
+// Chunk swizzle of K-major rows. Measured on gfx950 for 16-row fragment reads (lanes 0-15 =
+// 16 consecutive rows, one 16-byte chunk each): with 64-byte rows XOR with (row >> 1) & 3 is
+// conflict-free (row & 3 or no swizzle cost about 2x in LDS cycles); with 128-byte rows
+// XOR with row & 7 is. Neither depends on the fragment's 16-row block.
+template <int BK>
 __device__ __forceinline__ int swz_k(int r) {
-  // 128-byte rows: XOR with row & 7 (measured conflict-free as well)
-  return kChunks == 8 ? (r & 7) : ((r >> 1) & 3);
+  return BK == 64 ? (r & 7) : ((r >> 1) & 3);
 }
+// 32-byte-pair swizzle of MN-major k rows: the 8 k rows one half-wavefront of a transposing
+// read touches ({0..3, 8..11} + 16j) land on 8 different 32-byte bank groups.
 __device__ __forceinline__ int swz_mn(int k) { return 2 * ((k & 3) | ((k >> 1) & 4)); }
 
-// Per-lane byte offsets (within one stage's global window) of the lane's DMA loads. One
-// operand stage is kIPS instructions of 1 KiB; with NW wavefronts each issues kIPS / NW.
-template <bool KMAJOR, int NW>
-__device__ __forceinline__ void dma_offsets(const View& X, uint32_t (&off)[kIPS / NW]) {
+// Per-lane byte offsets (within one slice's global window) of the lane's P DMA loads for an
+// operand with R rows (K-major) or R columns (MN-major). One slice of the operand is
+// R·BK·2 / 1024 instructions of 1 KiB; wavefront w issues instructions w·P .. w·P + P − 1.
+template <bool KMAJOR, int R, int BK, int P>
+__device__ __forceinline__ void dma_offsets(const View& X, uint32_t (&off)[P]) {
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-  for (int j = 0; j < kIPS / NW; ++j) {
-    const int g = w * (kIPS / NW) + j;  // instruction index within the stage
+  for (int j = 0; j < P; ++j) {
+    const int g = w * P + j;  // instruction index within the slice
     if constexpr (KMAJOR) {
-      const int r = (64 / kChunks) * g + l / kChunks;  // 64 / kChunks rows per instruction
-      const int c = (l % kChunks) ^ swz_k(r);
+      constexpr int kc = BK / 8;                // 16-byte chunks per row
+      const int r = (64 / kc) * g + l / kc;     // 64 / kc rows per instruction
+      const int c = (l % kc) ^ swz_k<BK>(r);
       off[j] = uint32_t((int64_t(r) * X.ld + 8 * c) * 2);
     } else {
-      const int k = 2 * g + (l >> 5);
-      const int c = (l & 31) ^ swz_mn(k);
+      constexpr int rc = R / 8;                 // 16-byte chunks per k row
+      const int k = (64 / rc) * g + l / rc;     // 64 / rc k rows per instruction
+      const int c = (l % rc) ^ swz_mn(k);
       const int m = 8 * c;
       off[j] = uint32_t((int64_t(k) * X.ld + (m >> 6) * X.gs + (m & 63)) * 2);
     }
@@ -309,23 +329,11 @@ __device__ __forceinline__ void dma_offsets(const View& X, uint32_t (&off)[kIPS 
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
-// Raw buffer resource words (base, 32-bit record count, gfx9 data format) for inline asm.
-__device__ __forceinline__ i32x4_t rsrc_words(const void* base, int64_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xffffffffLL ? 0xffffffffu : uint32_t(bytes));
-  // every input is wave-uniform; readfirstlane lets the asm take the words from SGPRs
-  return i32x4_t{int(__builtin_amdgcn_readfirstlane(uint32_t(a))),
-                 int(__builtin_amdgcn_readfirstlane(uint32_t(a >> 32) & 0xffffu)),
-                 int(__builtin_amdgcn_readfirstlane(n)), 0x00020000};
-}
-
-// 16 bytes per lane from global straight into LDS at dst + 16 * lane. Issued as inline asm
-// on purpose: the compiler then leaves these loads to the explicit vmcnt waits below
-// instead of draining every in-flight slice before each LDS read.
-__device__ __forceinline__ void dma16(i32x4_t rs, uint32_t voff, char* dst) {
-  // the destination is wave-uniform (it depends only on the wavefront index)
-  const uint32_t la = __builtin_amdgcn_readfirstlane(
-      uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)dst)));
+// 16 bytes per lane from global straight into LDS at byte address m0 + 16 * lane. Issued as
+// inline asm on purpose: the compiler then leaves these loads to the explicit vmcnt waits
+// below instead of draining every in-flight slice before each LDS read. `rs` (buffer
+// resource) and `m0` are wave-uniform and live in SGPRs.
+__device__ __forceinline__ void dma16(i32x4_t rs, uint32_t voff, uint32_t m0) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -333,43 +341,83 @@ __device__ __forceinline__ void dma16(i32x4_t rs, uint32_t voff, char* dst) {
       "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(la), "v"(voff), "s"(rs)
+      : "s"(m0), "v"(voff), "s"(rs)
       : "memory");
 }
 
-// Issue one operand's loads for the K slice starting at k0 into `lds` (this stage's tile).
-template <bool KMAJOR, int NW>
-__device__ __forceinline__ void dma_issue(const View& X, int64_t r0, int64_t k0, int64_t K,
-                                          const uint32_t (&off)[kIPS / NW], char* lds) {
-  const int w = threadIdx.x >> 6;
-  i32x4_t rs;
+// Wave-uniform DMA window of one operand: byte address of the current K slice, bytes
+// readable from there (loads past them return zero; <= 0 reads nothing) and the advance per
+// slice. Built once per tile, so a slice costs a 64-bit add instead of address arithmetic.
+struct Stream {
+  uint64_t base;
+  int64_t recs;
+  int64_t step;
+};
+
+// Window of the K slice starting at k0 for rows / columns r0 .. r0 + R − 1. For a K-major
+// operand the slice start moves by a constant per slice when slices are whole 64-column
+// groups (BK == 64) or the groups are dense (gs == 64); the launcher only builds such views.
+template <bool KMAJOR, int BK>
+__device__ __forceinline__ Stream stream_at(const View& X, int64_t r0, int64_t k0, int64_t K) {
+  Stream st;
   if constexpr (KMAJOR) {
     const int64_t g = (k0 >> 6) * X.gs + (k0 & 63);
-    rs = rsrc_words(X.p + r0 * X.ld + g, ((X.rows - r0) * X.ld - g) * 2);
+    st.base = reinterpret_cast<uint64_t>(X.p + r0 * X.ld + g);
+    st.recs = ((X.rows - r0) * X.ld - g) * 2;
+    st.step = (BK == 64 ? X.gs : int64_t(BK)) * 2;
   } else {
+    // k rows past min(rows, K) read as zero; the window also stops at the end of the matrix
+    // (the shifted base would otherwise let the last row's columns past `cols` run over it)
     const int64_t kr = (X.rows < K ? X.rows : K) - k0;
-    rs = rsrc_words(X.p + k0 * X.ld + (r0 >> 6) * X.gs, kr * X.ld * 2);
+    const int64_t shift = (r0 >> 6) * X.gs;
+    const int64_t avail = (X.rows - k0) * X.ld - shift;
+    st.base = reinterpret_cast<uint64_t>(X.p + k0 * X.ld + shift);
+    st.recs = (kr * X.ld < avail ? kr * X.ld : avail) * 2;
+    st.step = int64_t(BK) * X.ld * 2;
   }
+  // every input is wave-uniform; saying so keeps the window in SGPRs for the whole K loop.
+  // readfirstlane returns a signed int: each half goes through uint32_t before widening, or
+  // a low word with bit 31 set would be sign-extended into the high word.
+  auto u64 = [](uint64_t x) {
+    const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(x)));
+    const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(x >> 32)));
+    return uint64_t(lo) | (uint64_t(hi) << 32);
+  };
+  st.base = u64(st.base);
+  st.recs = int64_t(u64(uint64_t(st.recs)));
+  st.step = int64_t(u64(uint64_t(st.step)));
+  return st;
+}
+
+// Issue one operand's P loads of the current slice (LDS bytes m0 .. m0 + P KiB), then advance.
+template <int P>
+__device__ __forceinline__ void dma_issue(Stream& st, const uint32_t (&off)[P], uint32_t m0) {
+  const int64_t r = st.recs;
+  const uint32_t n = r <= 0 ? 0u : (r >= 0xffffffffLL ? 0xffffffffu : uint32_t(r));
+  const i32x4_t rs = {int(uint32_t(st.base)), int(uint32_t(st.base >> 32) & 0xffffu), int(n),
+                      0x00020000};
 #pragma unroll
-  for (int j = 0; j < kIPS / NW; ++j) dma16(rs, off[j], lds + (w * (kIPS / NW) + j) * 1024);
+  for (int j = 0; j < P; ++j) dma16(rs, off[j], m0 + uint32_t(j) * 1024u);
+  st.base += uint64_t(st.step);
+  st.recs -= st.step;
 }
 
 // One 16 × 32 MFMA operand fragment for rows rbase .. rbase+15 and k = 32 kk .. 32 kk + 31 of
-// the stage tile.
-template <bool KMAJOR>
-__device__ __forceinline__ bf16x8_t frag(const char* lds, int rbase, int kk = 0) {
+// the slice tile (R rows / columns, depth BK).
+template <bool KMAJOR, int R, int BK>
+__device__ __forceinline__ bf16x8_t frag(const char* lds, int rbase, int kk) {
   const int l = threadIdx.x & 63;
   if constexpr (KMAJOR) {
     const int r = rbase + (l & 15);
-    const int c = (4 * kk + (l >> 4)) ^ swz_k(r);
-    return *reinterpret_cast<const bf16x8_t*>(lds + r * kRowBytes + c * 16);
+    const int c = (4 * kk + (l >> 4)) ^ swz_k<BK>(r);
+    return *reinterpret_cast<const bf16x8_t*>(lds + r * (2 * BK) + c * 16);
   } else {
     const int g = l >> 4, L = l & 15;
     const int m = rbase + 4 * (L & 3);
     const int k0 = 32 * kk + 8 * g + (L >> 2), k1 = k0 + 4;
     const int c = m >> 3, h = ((m >> 2) & 1) * 8;
-    const char* p0 = lds + k0 * 512 + ((c ^ swz_mn(k0)) << 4) + h;
-    const char* p1 = lds + k1 * 512 + ((c ^ swz_mn(k1)) << 4) + h;
+    const char* p0 = lds + k0 * (2 * R) + ((c ^ swz_mn(k0)) << 4) + h;
+    const char* p1 = lds + k1 * (2 * R) + ((c ^ swz_mn(k1)) << 4) + h;
     const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p0);
     const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p1);
     typedef short v8s __attribute__((ext_vector_type(8)));
@@ -378,48 +426,52 @@ __device__ __forceinline__ bf16x8_t frag(const char* lds, int rbase, int kk = 0)
   }
 }
 
-
-// s_waitcnt vmcnt(n) with the other counters untouched; n is a multiple of the per-slice
-// instruction count and at most 4 slices.
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    case 4: __builtin_amdgcn_s_waitcnt(0x0F70 | 4); break;
-    case 8: __builtin_amdgcn_s_waitcnt(0x0F70 | 8); break;
-    case 12: __builtin_amdgcn_s_waitcnt(0x0F70 | 12); break;
-    case 16: __builtin_amdgcn_s_waitcnt(0x0F70 | 0x4000); break;
-    case 24: __builtin_amdgcn_s_waitcnt(0x0F70 | 0x4000 | 8); break;
-    case 32: __builtin_amdgcn_s_waitcnt(0x0F70 | 0x8000); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;  // never taken; safe fallback
+// s_waitcnt vmcnt(PER · s) for the runtime s in [0, S], other counters untouched.
+template <int PER, int S>
+__device__ __forceinline__ void wait_slices(int s) {
+  if constexpr (S < 0) {
+    (void)s;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // never reached: s is always in range
+  } else {
+    if (s == S) {
+      constexpr int n = PER * S;
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+    } else {
+      wait_slices<PER, S - 1>(s);
+    }
   }
 }
 
-// One 256 × 256 output tile (`tile` indexes m-tiles, n-tiles and K splits as in `tm`).
-// WM × WN wavefronts; each owns a (256/WM) × (256/WN) block of accumulators.
-template <int WM, int WN, bool AK, bool BKM, class Epi>
+// One BM × BN output tile (`tile` indexes m-tiles, n-tiles and K splits as in `tm`).
+template <class C, bool AK, bool BKM, class Epi>
 __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M, int64_t N,
                                          int64_t K, int64_t ksplit, const TileMap& tm,
                                          int64_t tile, Epi& epi, char* lds) {
-  constexpr int NW = WM * WN;
-  constexpr int TM = 256 / WM / 16, TN = 256 / WN / 16;
-  constexpr int PER = 2 * (kIPS / NW);  // DMA instructions per stage per wavefront
+  constexpr int TM = C::TM, TN = C::TN, BK = C::BK, STAGES = C::STAGES;
   const int64_t mn = tm.m_tiles * tm.n_tiles;
   const int64_t kz = tile / mn;
   const int64_t rest = tile % mn;
   const int64_t mt = tm.m_fast ? rest % tm.m_tiles : rest / tm.n_tiles;
   const int64_t nt = tm.m_fast ? rest / tm.m_tiles : rest % tm.n_tiles;
-  const int64_t m0 = mt * BM, n0 = nt * BN;
+  const int64_t m0 = mt * C::BM, n0 = nt * C::BN;
   const int64_t kbeg = kz * ksplit;
   const int64_t kend = kbeg + ksplit < K ? kbeg + ksplit : K;
-  const int nk = kend > kbeg ? int((kend - kbeg + BK2 - 1) / BK2) : 0;
+  const int nk = kend > kbeg ? int((kend - kbeg + BK - 1) / BK) : 0;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  const int wm = wave / C::WN, wn = wave % C::WN;
 
-  uint32_t offa[kIPS / NW], offb[kIPS / NW];
-  dma_offsets<AK, NW>(A, offa);
-  dma_offsets<BKM, NW>(B, offb);
+  uint32_t offa[C::PA], offb[C::PB];
+  dma_offsets<AK, C::BM, BK, C::PA>(A, offa);
+  dma_offsets<BKM, C::BN, BK, C::PB>(B, offb);
+  Stream sa = stream_at<AK, BK>(A, m0, kbeg, K);
+  Stream sb = stream_at<BKM, BK>(B, n0, kbeg, K);
+  // LDS byte addresses of this wavefront's DMA destinations in slot 0
+  const uint32_t wv = __builtin_amdgcn_readfirstlane(uint32_t(threadIdx.x >> 6));
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds));
+  const uint32_t ma0 = lds0 + wv * uint32_t(C::PA * 1024);
+  const uint32_t mb0 = lds0 + uint32_t(C::ABytes) + wv * uint32_t(C::PB * 1024);
 
   f32x4_t acc[TM][TN];
 #pragma unroll
@@ -428,36 +480,39 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   int issued = 0;  // slices whose DMA has been issued (the same count in every wavefront)
-  auto slot = [&](int s) { return lds + (s % kStages) * kStageBytes2; };
-  auto issue = [&](int s) {
-    char* st = slot(s);
-    const int64_t k0 = kbeg + int64_t(s) * BK2;
-    dma_issue<AK, NW>(A, m0, k0, K, offa, st);
-    dma_issue<BKM, NW>(B, n0, k0, K, offb, st + kOpBytes);
+  int wslot = 0;   // ring slot the next issue fills
+  auto issue = [&]() {
+    const uint32_t o = uint32_t(wslot * C::StageBytes);
+    dma_issue<C::PA>(sa, offa, ma0 + o);
+    dma_issue<C::PB>(sb, offb, mb0 + o);
+    wslot = wslot + 1 == STAGES ? 0 : wslot + 1;
     ++issued;
   };
 
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < nk) issue(s);
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue();
+  int rslot = 0;  // ring slot of slice kt
 
   for (int kt = 0; kt < nk; ++kt) {
     // slice kt has landed once at most the later slices' DMA is pending; then sync the block
     // with a bare barrier (a __syncthreads() fence would drain the later slices too)
-    wait_vm(PER * (issued - 1 - kt));
+    wait_slices<C::PER, STAGES - 2>(issued - 1 - kt);
     __builtin_amdgcn_s_barrier();
     // refill the slot of slice kt-1 first (every wavefront's reads of it were consumed by
     // its MFMAs before it reached this barrier), so that nothing separates the fragment
     // reads below from the MFMAs that wait on them one by one
-    if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
-    const char* st = slot(kt);
+    if (kt + STAGES - 1 < nk) issue();
+    const char* st = lds + rslot * C::StageBytes;
+    rslot = rslot + 1 == STAGES ? 0 : rslot + 1;
 #pragma unroll
-    for (int kk = 0; kk < BK2 / 32; ++kk) {
+    for (int kk = 0; kk < BK / 32; ++kk) {
       bf16x8_t bf[TN], af[TM];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bf[j] = frag<BKM>(st + kOpBytes, wn * (256 / WN) + 16 * j, kk);
+      for (int j = 0; j < TN; ++j)
+        bf[j] = frag<BKM, C::BN, BK>(st + C::ABytes, wn * (C::BN / C::WN) + 16 * j, kk);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = frag<AK>(st, wm * (256 / WM) + 16 * i, kk);
+      for (int i = 0; i < TM; ++i) af[i] = frag<AK, C::BM, BK>(st, wm * (C::BM / C::WM) + 16 * i, kk);
       // all fragment reads are in flight before the first MFMA; the MFMAs then wait on them
       // one by one instead of the scheduler trading registers for exposed LDS latency
       __builtin_amdgcn_sched_barrier(0);
@@ -478,20 +533,20 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
     typename Epi::Aux aux[2][TN];
 #pragma unroll
     for (int di = 0; di < 2; ++di) {
-      const int64_t gm = m0 + wm * (256 / WM) + 16 * (i0 + di) + (lane & 15);
+      const int64_t gm = m0 + wm * (C::BM / C::WM) + 16 * (i0 + di) + (lane & 15);
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int64_t gn = n0 + wn * (256 / WN) + 16 * j + 4 * (lane >> 4);
+        const int64_t gn = n0 + wn * (C::BN / C::WN) + 16 * j + 4 * (lane >> 4);
         if (gm < M && gn + 4 <= N) aux[di][j] = epi.load4(gm, gn);
       }
     }
 #pragma unroll
     for (int di = 0; di < 2; ++di) {
-      const int64_t gm = m0 + wm * (256 / WM) + 16 * (i0 + di) + (lane & 15);
+      const int64_t gm = m0 + wm * (C::BM / C::WM) + 16 * (i0 + di) + (lane & 15);
       if (gm >= M) continue;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int64_t gn = n0 + wn * (256 / WN) + 16 * j + 4 * (lane >> 4);
+        const int64_t gn = n0 + wn * (C::BN / C::WN) + 16 * j + 4 * (lane >> 4);
         if (gn + 4 <= N) {
           epi.store4(gm, gn, acc[i0 + di][j], aux[di][j]);
         } else {
@@ -504,32 +559,29 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
   }
 }
 
-template <int WM, int WN, bool AK, bool BKM, class Epi>
-__global__ void __launch_bounds__(64 * WM * WN, 1)
-    gemm256p_kernel(View A, View B, int64_t M, int64_t N, int64_t K, int64_t ksplit, TileMap tm,
-                    Epi epi) {
-  __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageBytes2];
+template <class C, bool AK, bool BKM, class Epi>
+__global__ void __launch_bounds__(C::THREADS, C::OCC)
+    gemm_pipe_kernel(View A, View B, int64_t M, int64_t N, int64_t K, int64_t ksplit,
+                     TileMap tm, Epi epi) {
+  __shared__ __attribute__((aligned(1024))) char lds[C::LdsBytes];
   const int64_t total = tm.m_tiles * tm.n_tiles * tm.splits;
-  run_tile<WM, WN, AK, BKM>(A, B, M, N, K, ksplit, tm, xcd_tile(blockIdx.x, total), epi, lds);
+  run_tile<C, AK, BKM>(A, B, M, N, K, ksplit, tm, xcd_tile(blockIdx.x, total), epi, lds);
 }
 
-#ifndef LCE_GEMM_WM
-#define LCE_GEMM_WM 2
-#endif
-#ifndef LCE_GEMM_WN
-#define LCE_GEMM_WN 4
-#endif
-
-template <bool AK, bool BKM, class Epi>
+// C[M, N] = A · B over K with configuration C; `splits` > 1 cuts K into that many ranges
+// (multiples of C::BK), each its own tile set handed to the epilogue with its index.
+template <class C, bool AK, bool BKM, class Epi>
 hipError_t launch(const View& A, const View& B, int64_t M, int64_t N, int64_t K, int64_t splits,
                   bool m_fast, const Epi& epi, hipStream_t s) {
-  TileMap tm{(M + BM - 1) / BM, (N + BN - 1) / BN, splits < 1 ? 1 : splits, m_fast};
+  // a K-major operand's slice window must move by a constant per slice (see stream_at)
+  if ((AK && C::BK != 64 && A.gs != 64) || (BKM && C::BK != 64 && B.gs != 64))
+    return hipErrorInvalidValue;
+  TileMap tm{(M + C::BM - 1) / C::BM, (N + C::BN - 1) / C::BN, splits < 1 ? 1 : splits, m_fast};
   int64_t ksplit = (K + tm.splits - 1) / tm.splits;
-  ksplit = (ksplit + BK2 - 1) / BK2 * BK2;
+  ksplit = (ksplit + C::BK - 1) / C::BK * C::BK;
   const int64_t total = tm.m_tiles * tm.n_tiles * tm.splits;
-  constexpr int WM = LCE_GEMM_WM, WN = LCE_GEMM_WN;
-  hipLaunchKernelGGL((gemm256p_kernel<WM, WN, AK, BKM, Epi>), dim3(unsigned(total)),
-                     dim3(64 * WM * WN), 0, s, A, B, M, N, K, ksplit, tm, epi);
+  hipLaunchKernelGGL((gemm_pipe_kernel<C, AK, BKM, Epi>), dim3(unsigned(total)),
+                     dim3(C::THREADS), 0, s, A, B, M, N, K, ksplit, tm, epi);
   return hipGetLastError();
 }
 
