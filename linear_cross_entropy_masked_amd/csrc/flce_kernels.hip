@@ -481,7 +481,8 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     }
     if (a.grad_weight) {
       TimedLaunch t(s, K_FLCE_GEMM_GRAD_WEIGHT);
-      if ((e = gemm::v2::launch<Pair, false, false>(Ap, Bh, v, h, rows, 1, false, ew, s)) != hipSuccess)
+      if ((e = gemm::v2::launch<Pair, false, false>(Ap, Bh, v, h, rows, 1, false, ew, s, true)) !=
+          hipSuccess)
         return e;
     }
     if (a.grad_hidden && splits > 1) {

@@ -147,6 +147,8 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t w, int64_t total) {
 struct TileMap {
   int64_t m_tiles, n_tiles, splits;
   bool m_fast;  // true: consecutive tiles walk m (sharing the B tile), else walk n
+  int xn = 0;   // > 0 (pipelined kernel, one split): the 8 XCDs own a (8 / xn) × xn grid of
+                // m × n tile blocks, so each XCD's L2 sees 1 / xn of the B operand
 };
 
 template <bool AK, bool BKM, class Epi>
@@ -284,6 +286,8 @@ struct Cfg {
 };
 
 // Large-K products: one 256 × 256 workgroup per CU, 8 wavefronts, K = 64 slices, 2 stages.
+// (Measured: a 5-slot ring of single-operand slots, 1.5 slices ahead in 160 KiB, streams
+// faster alone but costs more than it gains once the MFMAs run.)
 using CfgWide = Cfg<256, 256, 64, 2, 2, 4, 1>;
 // Products whose epilogue streams HBM (fp32 read-modify-write): two 256 × 128 workgroups per
 // CU, so one's epilogue overlaps the other's MFMAs; K = 32 slices, 3 stages.
@@ -442,18 +446,39 @@ __device__ __forceinline__ void wait_slices(int s) {
   }
 }
 
-// One BM × BN output tile (`tile` indexes m-tiles, n-tiles and K splits as in `tm`).
+// Tile coordinates (m-tile, n-tile, K split) of workgroup w; false for a workgroup with no
+// tile (the XCD-block mapping pads every XCD to the largest block).
+struct TileCoord {
+  int64_t mt, nt, kz;
+};
+__device__ __forceinline__ bool tile_coord(const TileMap& tm, int64_t w, TileCoord& t) {
+  if (tm.xn > 0) {
+    // workgroups are dispatched to XCDs round-robin: XCD x runs w = x, x + 8, x + 16, ...
+    const int64_t x = w & 7, li = w >> 3, gm = 8 / tm.xn;
+    const int64_t xm = x / tm.xn, xq = x % tm.xn;
+    const int64_t m_lo = xm * tm.m_tiles / gm, m_hi = (xm + 1) * tm.m_tiles / gm;
+    const int64_t n_lo = xq * tm.n_tiles / tm.xn, n_hi = (xq + 1) * tm.n_tiles / tm.xn;
+    const int64_t nn = n_hi - n_lo;
+    if (nn <= 0 || li >= (m_hi - m_lo) * nn) return false;
+    t = TileCoord{m_lo + li / nn, n_lo + li % nn, 0};
+    return true;
+  }
+  const int64_t mn = tm.m_tiles * tm.n_tiles;
+  const int64_t tile = xcd_tile(w, mn * tm.splits);
+  const int64_t rest = tile % mn;
+  t = TileCoord{tm.m_fast ? rest % tm.m_tiles : rest / tm.n_tiles,
+                tm.m_fast ? rest / tm.m_tiles : rest % tm.n_tiles, tile / mn};
+  return true;
+}
+
+// One BM × BN output tile at tile coordinates `tc`.
 template <class C, bool AK, bool BKM, class Epi>
 __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M, int64_t N,
-                                         int64_t K, int64_t ksplit, const TileMap& tm,
-                                         int64_t tile, Epi& epi, char* lds) {
+                                         int64_t K, int64_t ksplit, const TileCoord& tc,
+                                         Epi& epi, char* lds) {
   constexpr int TM = C::TM, TN = C::TN, BK = C::BK, STAGES = C::STAGES;
-  const int64_t mn = tm.m_tiles * tm.n_tiles;
-  const int64_t kz = tile / mn;
-  const int64_t rest = tile % mn;
-  const int64_t mt = tm.m_fast ? rest % tm.m_tiles : rest / tm.n_tiles;
-  const int64_t nt = tm.m_fast ? rest / tm.m_tiles : rest % tm.n_tiles;
-  const int64_t m0 = mt * C::BM, n0 = nt * C::BN;
+  const int64_t kz = tc.kz;
+  const int64_t m0 = tc.mt * C::BM, n0 = tc.nt * C::BN;
   const int64_t kbeg = kz * ksplit;
   const int64_t kend = kbeg + ksplit < K ? kbeg + ksplit : K;
   const int nk = kend > kbeg ? int((kend - kbeg + BK - 1) / BK) : 0;
@@ -479,40 +504,16 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  int issued = 0;  // slices whose DMA has been issued (the same count in every wavefront)
-  int wslot = 0;   // ring slot the next issue fills
-  auto issue = [&]() {
-    const uint32_t o = uint32_t(wslot * C::StageBytes);
-    dma_issue<C::PA>(sa, offa, ma0 + o);
-    dma_issue<C::PB>(sb, offb, mb0 + o);
-    wslot = wslot + 1 == STAGES ? 0 : wslot + 1;
-    ++issued;
-  };
-
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) issue();
-  int rslot = 0;  // ring slot of slice kt
-
-  for (int kt = 0; kt < nk; ++kt) {
-    // slice kt has landed once at most the later slices' DMA is pending; then sync the block
-    // with a bare barrier (a __syncthreads() fence would drain the later slices too)
-    wait_slices<C::PER, STAGES - 2>(issued - 1 - kt);
-    __builtin_amdgcn_s_barrier();
-    // refill the slot of slice kt-1 first (every wavefront's reads of it were consumed by
-    // its MFMAs before it reached this barrier), so that nothing separates the fragment
-    // reads below from the MFMAs that wait on them one by one
-    if (kt + STAGES - 1 < nk) issue();
-    const char* st = lds + rslot * C::StageBytes;
-    rslot = rslot + 1 == STAGES ? 0 : rslot + 1;
+  // MFMAs over one slice whose A and B tiles sit at sA and sB
+  auto compute = [&](const char* sA, const char* sB) {
 #pragma unroll
     for (int kk = 0; kk < BK / 32; ++kk) {
       bf16x8_t bf[TN], af[TM];
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        bf[j] = frag<BKM, C::BN, BK>(st + C::ABytes, wn * (C::BN / C::WN) + 16 * j, kk);
+        bf[j] = frag<BKM, C::BN, BK>(sB, wn * (C::BN / C::WN) + 16 * j, kk);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = frag<AK, C::BM, BK>(st, wm * (C::BM / C::WM) + 16 * i, kk);
+      for (int i = 0; i < TM; ++i) af[i] = frag<AK, C::BM, BK>(sA, wm * (C::BM / C::WM) + 16 * i, kk);
       // all fragment reads are in flight before the first MFMA; the MFMAs then wait on them
       // one by one instead of the scheduler trading registers for exposed LDS latency
       __builtin_amdgcn_sched_barrier(0);
@@ -522,6 +523,33 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
     }
+  };
+
+  int issued = 0;  // slices whose DMA has been issued (the same count in every wavefront)
+  int wslot = 0;   // ring slot the next issue fills
+  auto issue = [&]() {
+    const uint32_t o = uint32_t(wslot * C::StageBytes);
+    dma_issue<C::PA>(sa, offa, ma0 + o);
+    dma_issue<C::PB>(sb, offb, mb0 + o);
+    wslot = wslot + 1 == STAGES ? 0 : wslot + 1;
+    ++issued;
+  };
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue();
+  int rslot = 0;  // ring slot of slice kt
+  for (int kt = 0; kt < nk; ++kt) {
+    // slice kt has landed once at most the later slices' DMA is pending; then sync the
+    // block with a bare barrier (a __syncthreads() fence would drain the later slices too)
+    wait_slices<C::PER, STAGES - 2>(issued - 1 - kt);
+    __builtin_amdgcn_s_barrier();
+    // refill the slot of slice kt-1 first (every wavefront's reads of it were consumed by
+    // its MFMAs before it reached this barrier), so that nothing separates the fragment
+    // reads below from the MFMAs that wait on them one by one
+    if (kt + STAGES - 1 < nk) issue();
+    const char* st = lds + rslot * C::StageBytes;
+    rslot = rslot + 1 == STAGES ? 0 : rslot + 1;
+    compute(st, st + C::ABytes);
   }
 
   // Epilogue in batches of two 16-row blocks: every load a batch needs (old accumulator
@@ -564,23 +592,33 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC)
     gemm_pipe_kernel(View A, View B, int64_t M, int64_t N, int64_t K, int64_t ksplit,
                      TileMap tm, Epi epi) {
   __shared__ __attribute__((aligned(1024))) char lds[C::LdsBytes];
-  const int64_t total = tm.m_tiles * tm.n_tiles * tm.splits;
-  run_tile<C, AK, BKM>(A, B, M, N, K, ksplit, tm, xcd_tile(blockIdx.x, total), epi, lds);
+  TileCoord tc;
+  if (!tile_coord(tm, blockIdx.x, tc)) return;  // uniform over the workgroup
+  run_tile<C, AK, BKM>(A, B, M, N, K, ksplit, tc, epi, lds);
 }
 
 // C[M, N] = A · B over K with configuration C; `splits` > 1 cuts K into that many ranges
 // (multiples of C::BK), each its own tile set handed to the epilogue with its index.
+// xcd_blocks (splits == 1, at least 8 m-tiles) hands each XCD a block of the m × n tile
+// grid instead of a run of consecutive tiles: with n split xn ways (xn = 4, 2 or 1, the
+// first that divides the n-tile count) an XCD reads 1 / xn of B and xn / 8 of A; worth it
+// when B is re-read by every m-tile and too large for one L2.
 template <class C, bool AK, bool BKM, class Epi>
 hipError_t launch(const View& A, const View& B, int64_t M, int64_t N, int64_t K, int64_t splits,
-                  bool m_fast, const Epi& epi, hipStream_t s) {
+                  bool m_fast, const Epi& epi, hipStream_t s, bool xcd_blocks = false) {
   // a K-major operand's slice window must move by a constant per slice (see stream_at)
   if ((AK && C::BK != 64 && A.gs != 64) || (BKM && C::BK != 64 && B.gs != 64))
     return hipErrorInvalidValue;
   TileMap tm{(M + C::BM - 1) / C::BM, (N + C::BN - 1) / C::BN, splits < 1 ? 1 : splits, m_fast};
   int64_t ksplit = (K + tm.splits - 1) / tm.splits;
   ksplit = (ksplit + C::BK - 1) / C::BK * C::BK;
-  const int64_t total = tm.m_tiles * tm.n_tiles * tm.splits;
-  hipLaunchKernelGGL((gemm_pipe_kernel<C, AK, BKM, Epi>), dim3(unsigned(total)),
+  int64_t grid = tm.m_tiles * tm.n_tiles * tm.splits;
+  if (xcd_blocks && tm.splits == 1 && tm.m_tiles >= 8) {
+    tm.xn = tm.n_tiles % 4 == 0 ? 4 : (tm.n_tiles % 2 == 0 ? 2 : 1);
+    const int64_t gm = 8 / tm.xn;
+    grid = 8 * ((tm.m_tiles + gm - 1) / gm) * (tm.n_tiles / tm.xn);
+  }
+  hipLaunchKernelGGL((gemm_pipe_kernel<C, AK, BKM, Epi>), dim3(unsigned(grid)),
                      dim3(C::THREADS), 0, s, A, B, M, N, K, ksplit, tm, epi);
   return hipGetLastError();
 }
