@@ -286,8 +286,11 @@ struct Cfg {
 };
 
 // Large-K products: one 256 × 256 workgroup per CU, 8 wavefronts, K = 64 slices, 2 stages.
-// (Measured: a 5-slot ring of single-operand slots, 1.5 slices ahead in 160 KiB, streams
-// faster alone but costs more than it gains once the MFMAs run.)
+// Measured on the logits product's access pattern, direct-to-LDS streaming reaches about
+// 12 TB/s with one 64-deep slice in flight per CU and about 16 TB/s with two, while 32-deep
+// slices (64-byte row segments) stay near 12 TB/s at any depth. Two slices in flight do not
+// fit next to the one being multiplied; the variants that approximate it (a 5-slot ring of
+// single operands; refilling a slot mid-slice after a second barrier) measured slower.
 using CfgWide = Cfg<256, 256, 64, 2, 2, 4, 1>;
 // Products whose epilogue streams HBM (fp32 read-modify-write): two 256 × 128 workgroups per
 // CU, so one's epilogue overlaps the other's MFMAs; K = 32 slices, 3 stages.
@@ -355,12 +358,12 @@ __device__ __forceinline__ void dma16(i32x4_t rs, uint32_t voff, uint32_t m0) {
 struct Stream {
   uint64_t base;
   int64_t recs;
-  int64_t step;
+  int64_t step;   // advance after the next slice
+  int64_t step2;  // advance after the one after (differs from step only for 32-deep slices
+                  // of a grouped K-major operand: 32 elements, then the gap to the next group)
 };
 
-// Window of the K slice starting at k0 for rows / columns r0 .. r0 + R − 1. For a K-major
-// operand the slice start moves by a constant per slice when slices are whole 64-column
-// groups (BK == 64) or the groups are dense (gs == 64); the launcher only builds such views.
+// Window of the K slice starting at k0 (a multiple of BK) for rows / columns r0 .. r0 + R − 1.
 template <bool KMAJOR, int BK>
 __device__ __forceinline__ Stream stream_at(const View& X, int64_t r0, int64_t k0, int64_t K) {
   Stream st;
@@ -368,7 +371,13 @@ __device__ __forceinline__ Stream stream_at(const View& X, int64_t r0, int64_t k
     const int64_t g = (k0 >> 6) * X.gs + (k0 & 63);
     st.base = reinterpret_cast<uint64_t>(X.p + r0 * X.ld + g);
     st.recs = ((X.rows - r0) * X.ld - g) * 2;
-    st.step = (BK == 64 ? X.gs : int64_t(BK)) * 2;
+    if (BK == 64) {
+      st.step = st.step2 = X.gs * 2;
+    } else {  // 32 within a group, then on to the next group's start
+      const int64_t in = 64, across = (X.gs - 32) * 2;
+      st.step = (k0 & 32) ? across : in;
+      st.step2 = (k0 & 32) ? in : across;
+    }
   } else {
     // k rows past min(rows, K) read as zero; the window also stops at the end of the matrix
     // (the shifted base would otherwise let the last row's columns past `cols` run over it)
@@ -377,7 +386,7 @@ __device__ __forceinline__ Stream stream_at(const View& X, int64_t r0, int64_t k
     const int64_t avail = (X.rows - k0) * X.ld - shift;
     st.base = reinterpret_cast<uint64_t>(X.p + k0 * X.ld + shift);
     st.recs = (kr * X.ld < avail ? kr * X.ld : avail) * 2;
-    st.step = int64_t(BK) * X.ld * 2;
+    st.step = st.step2 = int64_t(BK) * X.ld * 2;
   }
   // every input is wave-uniform; saying so keeps the window in SGPRs for the whole K loop.
   // readfirstlane returns a signed int: each half goes through uint32_t before widening, or
@@ -390,6 +399,7 @@ __device__ __forceinline__ Stream stream_at(const View& X, int64_t r0, int64_t k
   st.base = u64(st.base);
   st.recs = int64_t(u64(uint64_t(st.recs)));
   st.step = int64_t(u64(uint64_t(st.step)));
+  st.step2 = int64_t(u64(uint64_t(st.step2)));
   return st;
 }
 
@@ -404,6 +414,9 @@ __device__ __forceinline__ void dma_issue(Stream& st, const uint32_t (&off)[P], 
   for (int j = 0; j < P; ++j) dma16(rs, off[j], m0 + uint32_t(j) * 1024u);
   st.base += uint64_t(st.step);
   st.recs -= st.step;
+  const int64_t t = st.step;
+  st.step = st.step2;
+  st.step2 = t;
 }
 
 // One 16 × 32 MFMA operand fragment for rows rbase .. rbase+15 and k = 32 kk .. 32 kk + 31 of
@@ -534,6 +547,7 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
     wslot = wslot + 1 == STAGES ? 0 : wslot + 1;
     ++issued;
   };
+
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < nk) issue();
@@ -606,9 +620,8 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC)
 template <class C, bool AK, bool BKM, class Epi>
 hipError_t launch(const View& A, const View& B, int64_t M, int64_t N, int64_t K, int64_t splits,
                   bool m_fast, const Epi& epi, hipStream_t s, bool xcd_blocks = false) {
-  // a K-major operand's slice window must move by a constant per slice (see stream_at)
-  if ((AK && C::BK != 64 && A.gs != 64) || (BKM && C::BK != 64 && B.gs != 64))
-    return hipErrorInvalidValue;
+  // grouped K-major operands keep whole groups of 64 (see stream_at)
+  if ((AK && A.gs < 64) || (BKM && B.gs < 64)) return hipErrorInvalidValue;
   TileMap tm{(M + C::BM - 1) / C::BM, (N + C::BN - 1) / C::BN, splits < 1 ? 1 : splits, m_fast};
   int64_t ksplit = (K + tm.splits - 1) / tm.splits;
   ksplit = (ksplit + C::BK - 1) / C::BK * C::BK;
