@@ -125,9 +125,10 @@ int ce_chunked_bwd_inplace(uint16_t* logits_inout, int64_t n, int64_t v, int64_t
 
 /* ------------------------------------------------------------------ fused linear CE */
 
-/* Workspace bytes for flce_fwd_bwd: one fp32 [chunk, V] logits slice (rows padded to the
- * kernels' tile width) plus O(n + chunk) bookkeeping; with FLCE_RECOMPUTE the slice holds
- * bf16 probabilities only (half the bytes). Host-only; safe without a GPU. */
+/* Workspace bytes for flce_fwd_bwd: one fp32 [chunk, V] logits slice (rows padded to a
+ * multiple of 64) plus bookkeeping below 1% of it: n per-row loss terms, chunk lse values and
+ * one (max, sum) pair per chunk row and 256-column tile of the logits. Host-only; safe
+ * without a GPU. */
 int flce_workspace_size(int64_t n, int64_t h, int64_t v, int64_t chunk_size, uint32_t flags,
                         size_t* bytes);
 

@@ -51,11 +51,16 @@ __device__ __forceinline__ bool has_label(int32_t y, int64_t v, int32_t ignore_i
   return y != ignore_index && y >= 0 && int64_t(y) < v;
 }
 
-// Z[m, n] = acc + bias[n] into the fp32 slice.
+// Z[m, n] = acc + bias[n] into the fp32 slice. With the pipelined GEMM it also leaves, per row
+// m and 256-column tile t, part[m · part_ld + t] = (max_n z, Σ_n exp(z − max)) over the tile:
+// the logsumexp of each row is then a merge of ⌈V / 256⌉ pairs instead of a pass over Z.
 struct EpiLogits {
   float* z;
   int64_t ldz;
   const float* bias;
+  float2* part;
+  int64_t part_ld;
+  static constexpr bool kRowStats = true;
   __device__ void begin(int64_t) {}
   __device__ __forceinline__ void operator()(int64_t m, int64_t n, float a) {
     z[m * ldz + n] = bias ? a + bias[n] : a;
@@ -67,10 +72,16 @@ struct EpiLogits {
   __device__ __forceinline__ void store4(int64_t m, int64_t n, gemm::f32x4_t a, Aux b) {
     *reinterpret_cast<gemm::f32x4_t*>(z + m * ldz + n) = a + b;
   }
+  __device__ __forceinline__ gemm::f32x4_t value4(gemm::f32x4_t a, Aux b) const { return a + b; }
+  __device__ __forceinline__ float value1(int64_t n, float a) const { return bias ? a + bias[n] : a; }
+  __device__ __forceinline__ void row_stats(int64_t m, int64_t t, float mx, float sum) {
+    part[m * part_ld + t] = float2{mx, sum};
+  }
 };
 
 // dH[m, n] = coef · (acc − W[y_m, n]) for labelled rows, 0 otherwise; bf16 out.
 struct EpiGradHidden {
+  static constexpr bool kRowStats = false;
   uint16_t* dh;
   int64_t ldh;
   const int32_t* labels;  // chunk rows
@@ -110,6 +121,7 @@ struct EpiGradHidden {
 
 // dW[m, n] = (overwrite ? 0 : dW[m, n]) + coef · acc.
 struct EpiGradWeight {
+  static constexpr bool kRowStats = false;
   float* dw;
   int64_t ldw;
   int overwrite;
@@ -138,6 +150,7 @@ struct EpiGradWeight {
 __device__ __forceinline__ int64_t gap_index(int64_t e) { return (e >> 5) * 64 + 32 + (e & 31); }
 
 struct EpiPartial {
+  static constexpr bool kRowStats = false;
   float* slice;
   int64_t M, N;
   int64_t kz;
@@ -245,6 +258,39 @@ __global__ void __launch_bounds__(kRowThreads) slice_row_lse_kernel(
   }
 }
 
+// lse of each labelled row from the logits GEMM's per-tile (max, Σ exp) pairs, merged in a
+// fixed order; loss term lse − z[y] (z read back from the slice) and lse_out. One wavefront
+// per row.
+__global__ void __launch_bounds__(256) lse_merge_rows_kernel(
+    const float2* __restrict__ part, int64_t tiles, const float* __restrict__ z, int64_t ldz,
+    int64_t rows, int64_t v, const int32_t* __restrict__ labels, int32_t ignore_index,
+    float* __restrict__ lse_c, float* __restrict__ row_loss, float* __restrict__ lse_out) {
+  const int64_t i = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (i >= rows) return;
+  const int32_t y = labels[i];
+  if (!has_label(y, v, ignore_index)) {
+    if (lane == 0) {
+      lse_c[i] = 0.f;
+      row_loss[i] = 0.f;
+      if (lse_out) lse_out[i] = 0.f;
+    }
+    return;
+  }
+  float m = -INFINITY, sum = 0.f;
+  for (int64_t t = lane; t < tiles; t += 64) {
+    const float2 p = part[i * tiles + t];
+    lse_merge(m, sum, p.x, p.y);
+  }
+  wave_lse_reduce(m, sum);
+  if (lane == 0) {
+    const float lse = m + fast_log2(sum) * kLn2;
+    lse_c[i] = lse;
+    row_loss[i] = lse - z[i * ldz + y];
+    if (lse_out) lse_out[i] = lse;
+  }
+}
+
 // grad_bias[v] (=|+=) coef · (Σ_{labelled i} p_iv − #{i: y_i = v}) from the fp32 slice.
 __global__ void __launch_bounds__(256) slice_bias_grad_kernel(
     const float* __restrict__ z, int64_t ldz, int64_t rows, int64_t v,
@@ -348,11 +394,15 @@ struct FlceWs {
   long long* count;
   float* row_loss;  // [n]
   float* lse_c;     // [C]
+  float2* part;     // [C, tiles] per-tile (max, Σ exp) of the logits rows
+  int64_t tiles;
   float* slice;     // [C, ldz] fp32
   int64_t ldz;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int64_t lse_tiles(int64_t v) { return (v + Wide::BN - 1) / Wide::BN; }
 
 FlceWs flce_carve(void* base, int64_t n, int64_t v, int64_t chunk) {
   char* b = static_cast<char*>(base);
@@ -363,6 +413,9 @@ FlceWs flce_carve(void* base, int64_t n, int64_t v, int64_t chunk) {
   off += align256(size_t(n) * 4);
   w.lse_c = reinterpret_cast<float*>(b + off);
   off += align256(size_t(chunk) * 4);
+  w.tiles = lse_tiles(v);
+  w.part = reinterpret_cast<float2*>(b + off);
+  off += align256(size_t(chunk) * size_t(w.tiles) * 8);
   w.slice = reinterpret_cast<float*>(b + off);
   w.ldz = round_up(v, kGroup);
   return w;
@@ -385,7 +438,7 @@ size_t flce_workspace_bytes(int64_t n, int64_t h, int64_t v, int64_t chunk_size,
   const int64_t c = chunk_size < n ? chunk_size : (n > 0 ? n : 1);
   const int64_t ldz = round_up(v, kGroup);
   return 256 + align256(size_t(n) * 4) + align256(size_t(c) * 4) +
-         align256(size_t(c) * size_t(ldz) * 4);
+         align256(size_t(c) * size_t(lse_tiles(v)) * 8) + align256(size_t(c) * size_t(ldz) * 4);
 }
 
 hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
@@ -417,23 +470,31 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     const int32_t* lab = a.labels + c0;
     const uint16_t* hid = a.hidden + c0 * h;
 
-    // 1. logits slice
+    // 1. logits slice (the pipelined GEMM also leaves per-tile logsumexp pairs; the register-
+    //    staged one, used when h is not a multiple of 64, does not)
     View Ah{hid, h, kGroup, rows, h};
     View Bw{a.weight, h, kGroup, v, h};
-    EpiLogits el{ws.slice, ws.ldz, a.bias};
+    EpiLogits el{ws.slice, ws.ldz, a.bias, ws.part, ws.tiles};
+    const bool fused_lse = h % Wide::BK == 0;
     {
       TimedLaunch t(s, K_FLCE_GEMM_LOGITS);
-      e = (h % Wide::BK == 0) ? gemm::v2::launch<Wide, true, true>(Ah, Bw, rows, v, h, 1, true, el, s)
-                              : gemm::launch<true, true>(Ah, Bw, rows, v, h, 1, true, el, s);
+      e = fused_lse ? gemm::v2::launch<Wide, true, true>(Ah, Bw, rows, v, h, 1, true, el, s)
+                    : gemm::launch<true, true>(Ah, Bw, rows, v, h, 1, true, el, s);
       if (e != hipSuccess) return e;
     }
 
     // 2. row logsumexp and loss terms
     {
       TimedLaunch t(s, K_FLCE_ROW_LSE);
-      hipLaunchKernelGGL(slice_row_lse_kernel, dim3(unsigned(rows)), dim3(kRowThreads), 0, s,
-                         ws.slice, ws.ldz, v, lab, a.ignore_index, ws.lse_c, ws.row_loss + c0,
-                         a.lse_out ? a.lse_out + c0 : nullptr);
+      float* lo = a.lse_out ? a.lse_out + c0 : nullptr;
+      if (fused_lse)
+        hipLaunchKernelGGL(lse_merge_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s,
+                           ws.part, ws.tiles, ws.slice, ws.ldz, rows, v, lab, a.ignore_index,
+                           ws.lse_c, ws.row_loss + c0, lo);
+      else
+        hipLaunchKernelGGL(slice_row_lse_kernel, dim3(unsigned(rows)), dim3(kRowThreads), 0, s,
+                           ws.slice, ws.ldz, v, lab, a.ignore_index, ws.lse_c, ws.row_loss + c0,
+                           lo);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
 

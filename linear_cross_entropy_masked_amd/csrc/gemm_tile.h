@@ -569,7 +569,15 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
   // Epilogue in batches of two 16-row blocks: every load a batch needs (old accumulator
   // values, bias, label rows) is issued before any of its stores, so the loads overlap
   // instead of each waiting behind a store the compiler cannot prove disjoint.
+  // Epilogues with kRowStats also get, per output row, the (max, sum of exp(x - max)) of the
+  // values they store over this tile's valid columns (value4 says what those values are).
   epi.begin(kz);
+  float rm[TM], rs[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    rm[i] = -INFINITY;
+    rs[i] = 0.f;
+  }
 #pragma unroll
   for (int i0 = 0; i0 < TM; i0 += 2) {
     typename Epi::Aux aux[2][TN];
@@ -591,12 +599,58 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
         const int64_t gn = n0 + wn * (C::BN / C::WN) + 16 * j + 4 * (lane >> 4);
         if (gn + 4 <= N) {
           epi.store4(gm, gn, acc[i0 + di][j], aux[di][j]);
+          if constexpr (Epi::kRowStats) {
+            const f32x4_t z = epi.value4(acc[i0 + di][j], aux[di][j]);
+            const float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+            const float mn = fmaxf(rm[i0 + di], mx), c = mn * kLog2e;
+            float t = rm[i0 + di] == mn ? rs[i0 + di]
+                                        : rs[i0 + di] * fast_exp2(fmaf(rm[i0 + di], kLog2e, -c));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) t += fast_exp2(fmaf(z[q], kLog2e, -c));
+            rm[i0 + di] = mn;
+            rs[i0 + di] = t;
+          }
         } else {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            if (gn + q < N) epi(gm, gn + q, acc[i0 + di][j][q]);
+            if (gn + q < N) {
+              epi(gm, gn + q, acc[i0 + di][j][q]);
+              if constexpr (Epi::kRowStats) {
+                const float z = epi.value1(gn + q, acc[i0 + di][j][q]);
+                float m1 = rm[i0 + di], s1 = rs[i0 + di];
+                lse_merge(m1, s1, z, 1.f);
+                rm[i0 + di] = m1;
+                rs[i0 + di] = s1;
+              }
+            }
         }
       }
+    }
+  }
+  if constexpr (Epi::kRowStats) {
+    // lanes l, l ^ 16, l ^ 32 and l ^ 48 hold the same rows: merge them, then merge the WN
+    // wavefronts that share each row through LDS, in wavefront order
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int off = 16; off <= 32; off <<= 1) {
+        const float m2 = __shfl_xor(rm[i], off, 64), s2 = __shfl_xor(rs[i], off, 64);
+        lse_merge(rm[i], rs[i], m2, s2);
+      }
+    }
+    __syncthreads();  // every wavefront is past the main loop: the LDS ring is free
+    float2* red = reinterpret_cast<float2*>(lds);  // [WN][BM]
+    if ((lane >> 4) == 0) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        red[wn * C::BM + wm * (C::BM / C::WM) + 16 * i + lane] = float2{rm[i], rs[i]};
+    }
+    __syncthreads();
+    for (int r = threadIdx.x; r < C::BM; r += C::THREADS) {
+      float m = red[r].x, sum = red[r].y;
+#pragma unroll
+      for (int w = 1; w < C::WN; ++w) lse_merge(m, sum, red[w * C::BM + r].x, red[w * C::BM + r].y);
+      if (m0 + r < M) epi.row_stats(m0 + r, tc.nt, m, sum);
     }
   }
 }
