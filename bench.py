@@ -62,7 +62,8 @@ def stored_traffic(kernel: str, workload: str):
 
 # rocprofv3 kernel names -> the library's launch-timing names (first match wins)
 KERNEL_NAMES = [
-    ("EpiLogits", "flce_gemm_logits"), ("EpiGradHidden", "flce_gemm_grad_hidden"),
+    ("EpiLogits", "flce_gemm_logits"), ("EpiLseOnly", "flce_gemm_logits"),
+    ("EpiProbs", "flce_gemm_probs"), ("EpiGradHidden", "flce_gemm_grad_hidden"),
     ("EpiPartial", "flce_gemm_grad_hidden"), ("EpiGradWeight", "flce_gemm_grad_weight"),
     ("slice_row_lse_kernel", "flce_row_lse"), ("slice_bias_grad_kernel", "flce_bias_grad"),
     ("slice_to_probs_kernel", "flce_to_probs"), ("onehot_weight_fix_kernel", "flce_onehot_fix"),
@@ -219,8 +220,8 @@ def run_flce(args, torch, lce, workloads):
     chunks = -(-w.n // w.chunk_size)
     one = 2.0 * w.chunk_size * w.h * w.v  # one chunk's product (every chunk is full here)
     # algorithmic flops per launch of each MFMA kernel (one chunk's product)
-    per_launch = {"flce_gemm_logits": one, "flce_gemm_grad_hidden": one,
-                  "flce_gemm_grad_weight": one}
+    per_launch = {"flce_gemm_logits": one, "flce_gemm_probs": one,
+                  "flce_gemm_grad_hidden": one, "flce_gemm_grad_weight": one}
     gemms = [k for k in kernels if k[0] in per_launch]
     dom = max(gemms, key=lambda k: k[1]) if gemms else None
     roof = None

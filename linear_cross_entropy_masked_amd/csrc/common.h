@@ -97,6 +97,7 @@ enum KernelId {
   K_FLCE_ONEHOT_FIX,
   K_FILL,
   K_FLCE_GRAD_HIDDEN_REDUCE,
+  K_FLCE_GEMM_PROBS,
   K_COUNT
 };
 

@@ -55,6 +55,7 @@ __device__ __forceinline__ bool has_label(int32_t y, int64_t v, int32_t ignore_i
 // m and 256-column tile t, part[m · part_ld + t] = (max_n z, Σ_n exp(z − max)) over the tile:
 // the logsumexp of each row is then a merge of ⌈V / 256⌉ pairs instead of a pass over Z.
 struct EpiLogits {
+  static constexpr bool kColSums = false;
   float* z;
   int64_t ldz;
   const float* bias;
@@ -79,8 +80,98 @@ struct EpiLogits {
   }
 };
 
+// Pass 1 of the recomputing schedule: the logits tile is only reduced, never stored. Leaves
+// the per-tile (max, Σ exp) pairs like EpiLogits, and zy[m] = z[m, y_m] for the tile holding
+// the label column.
+struct EpiLseOnly {
+  const float* bias;
+  float2* part;
+  int64_t part_ld;
+  const int32_t* labels;
+  float* zy;
+  static constexpr bool kRowStats = true;
+  static constexpr bool kColSums = false;
+  __device__ void begin(int64_t) {}
+  __device__ __forceinline__ void operator()(int64_t m, int64_t n, float a) {
+    if (int64_t(labels[m]) == n) zy[m] = bias ? a + bias[n] : a;
+  }
+  using Aux = gemm::f32x4_t;
+  __device__ __forceinline__ Aux load4(int64_t, int64_t n) const {
+    return bias ? Aux{bias[n], bias[n + 1], bias[n + 2], bias[n + 3]} : Aux{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ __forceinline__ void store4(int64_t m, int64_t n, gemm::f32x4_t a, Aux b) {
+    const int64_t d = int64_t(labels[m]) - n;
+    if (d >= 0 && d < 4) {
+      const gemm::f32x4_t z = a + b;
+      zy[m] = d == 0 ? z[0] : d == 1 ? z[1] : d == 2 ? z[2] : z[3];
+    }
+  }
+  __device__ __forceinline__ gemm::f32x4_t value4(gemm::f32x4_t a, Aux b) const { return a + b; }
+  __device__ __forceinline__ float value1(int64_t n, float a) const { return bias ? a + bias[n] : a; }
+  __device__ __forceinline__ void row_stats(int64_t m, int64_t t, float mx, float sum) {
+    part[m * part_ld + t] = float2{mx, sum};
+  }
+};
+
+// Pass 2 of the recomputing schedule: the recomputed logits tile becomes bf16 probabilities
+// P = exp(z − lse) in the slice's probability layout (first half of every 64-column group),
+// 0 for rows without a label and for the padding columns v .. ldz − 1 (the GEMM runs over
+// N = ldz; weight rows past v read as zero). With grad_bias it also leaves, per 256-row tile
+// mt and column n, colsum[mt · v + n] = Σ_m p (the fp32 values, before rounding).
+struct EpiProbs {
+  uint16_t* p;
+  int64_t p_ld;  // elements between rows (2 · ldz)
+  const float* bias;
+  const float* lse;
+  const int32_t* labels;
+  int64_t v;
+  int32_t ignore_index;
+  float* colsum;  // NULL: no column sums
+  static constexpr bool kRowStats = false;
+  static constexpr bool kColSums = true;
+  __device__ void begin(int64_t) {}
+  __device__ __forceinline__ int64_t at(int64_t m, int64_t n) const {
+    return m * p_ld + (n >> 6) * (2 * kGroup) + (n & 63);
+  }
+  struct Aux {
+    gemm::f32x4_t b;
+    float c;  // lse · log2 e, or NaN for a row without a label
+  };
+  __device__ __forceinline__ Aux load4(int64_t m, int64_t n) const {
+    Aux x;
+    x.b = gemm::f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (bias) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (n + q < v) x.b[q] = bias[n + q];
+    }
+    x.c = has_label(labels[m], v, ignore_index) ? lse[m] * kLog2e : __builtin_nanf("");
+    return x;
+  }
+  __device__ __forceinline__ gemm::f32x4_t colvalue4(gemm::f32x4_t a, Aux x) const {
+    gemm::f32x4_t r{0.f, 0.f, 0.f, 0.f};
+    if (x.c == x.c) {  // labelled row
+#pragma unroll
+      for (int q = 0; q < 4; ++q) r[q] = fast_exp2(fmaf(a[q] + x.b[q], kLog2e, -x.c));
+    }
+    return r;
+  }
+  __device__ __forceinline__ void store4(int64_t m, int64_t n, gemm::f32x4_t a, Aux x) {
+    gemm::f32x4_t r = colvalue4(a, x);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (n + q >= v) r[q] = 0.f;
+    *reinterpret_cast<uint2*>(p + at(m, n)) = uint2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+  }
+  __device__ __forceinline__ void operator()(int64_t, int64_t, float) {}  // N % 4 == 0: unused
+  __device__ __forceinline__ void col_sums(int64_t mt, int64_t n, float sum) {
+    if (colsum && n < v) colsum[mt * v + n] = sum;
+  }
+};
+
 // dH[m, n] = coef · (acc − W[y_m, n]) for labelled rows, 0 otherwise; bf16 out.
 struct EpiGradHidden {
+  static constexpr bool kColSums = false;
   static constexpr bool kRowStats = false;
   uint16_t* dh;
   int64_t ldh;
@@ -121,6 +212,7 @@ struct EpiGradHidden {
 
 // dW[m, n] = (overwrite ? 0 : dW[m, n]) + coef · acc.
 struct EpiGradWeight {
+  static constexpr bool kColSums = false;
   static constexpr bool kRowStats = false;
   float* dw;
   int64_t ldw;
@@ -150,6 +242,7 @@ struct EpiGradWeight {
 __device__ __forceinline__ int64_t gap_index(int64_t e) { return (e >> 5) * 64 + 32 + (e & 31); }
 
 struct EpiPartial {
+  static constexpr bool kColSums = false;
   static constexpr bool kRowStats = false;
   float* slice;
   int64_t M, N;
@@ -259,12 +352,13 @@ __global__ void __launch_bounds__(kRowThreads) slice_row_lse_kernel(
 }
 
 // lse of each labelled row from the logits GEMM's per-tile (max, Σ exp) pairs, merged in a
-// fixed order; loss term lse − z[y] (z read back from the slice) and lse_out. One wavefront
-// per row.
+// fixed order; loss term lse − z[y] and lse_out. z[y] comes from zy when given, else from the
+// fp32 slice. One wavefront per row.
 __global__ void __launch_bounds__(256) lse_merge_rows_kernel(
     const float2* __restrict__ part, int64_t tiles, const float* __restrict__ z, int64_t ldz,
-    int64_t rows, int64_t v, const int32_t* __restrict__ labels, int32_t ignore_index,
-    float* __restrict__ lse_c, float* __restrict__ row_loss, float* __restrict__ lse_out) {
+    const float* __restrict__ zy, int64_t rows, int64_t v, const int32_t* __restrict__ labels,
+    int32_t ignore_index, float* __restrict__ lse_c, float* __restrict__ row_loss,
+    float* __restrict__ lse_out) {
   const int64_t i = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (i >= rows) return;
@@ -286,7 +380,7 @@ __global__ void __launch_bounds__(256) lse_merge_rows_kernel(
   if (lane == 0) {
     const float lse = m + fast_log2(sum) * kLn2;
     lse_c[i] = lse;
-    row_loss[i] = lse - z[i * ldz + y];
+    row_loss[i] = lse - (zy ? zy[i] : z[i * ldz + y]);
     if (lse_out) lse_out[i] = lse;
   }
 }
@@ -309,6 +403,25 @@ __global__ void __launch_bounds__(256) slice_bias_grad_kernel(
   }
   const float coef = flce_coef(count_dev, count_host, gout);
   const float d = coef * (sp - float(cnt));
+  grad_bias[col] = overwrite ? d : grad_bias[col] + d;
+}
+
+// grad_bias[v] (=|+=) coef · (Σ_mt colsum[mt, v] − #{labelled i: y_i = v}), the column sums
+// added in row-tile order.
+__global__ void __launch_bounds__(256) bias_from_colsums_kernel(
+    const float* __restrict__ colsum, int64_t mtiles, int64_t rows, int64_t v,
+    const int32_t* __restrict__ labels, int32_t ignore_index, float* __restrict__ grad_bias,
+    int overwrite, const long long* count_dev, long long count_host, const float* gout) {
+  const int64_t col = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (col >= v) return;
+  float sp = 0.f;
+  for (int64_t t = 0; t < mtiles; ++t) sp += colsum[t * v + col];
+  int cnt = 0;
+  for (int64_t i = 0; i < rows; ++i) {
+    const int32_t y = labels[i];
+    cnt += (has_label(y, v, ignore_index) && int64_t(y) == col);
+  }
+  const float d = flce_coef(count_dev, count_host, gout) * (sp - float(cnt));
   grad_bias[col] = overwrite ? d : grad_bias[col] + d;
 }
 
@@ -396,6 +509,8 @@ struct FlceWs {
   float* lse_c;     // [C]
   float2* part;     // [C, tiles] per-tile (max, Σ exp) of the logits rows
   int64_t tiles;
+  float* zy;        // [C] label logits (recomputing schedule)
+  float* colsum;    // [C / 256, V] probability column sums (recomputing schedule, bias)
   float* slice;     // [C, ldz] fp32
   int64_t ldz;
 };
@@ -403,6 +518,7 @@ struct FlceWs {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int64_t lse_tiles(int64_t v) { return (v + Wide::BN - 1) / Wide::BN; }
+int64_t row_tiles(int64_t c) { return (c + Wide::BM - 1) / Wide::BM; }
 
 FlceWs flce_carve(void* base, int64_t n, int64_t v, int64_t chunk) {
   char* b = static_cast<char*>(base);
@@ -416,6 +532,10 @@ FlceWs flce_carve(void* base, int64_t n, int64_t v, int64_t chunk) {
   w.tiles = lse_tiles(v);
   w.part = reinterpret_cast<float2*>(b + off);
   off += align256(size_t(chunk) * size_t(w.tiles) * 8);
+  w.zy = reinterpret_cast<float*>(b + off);
+  off += align256(size_t(chunk) * 4);
+  w.colsum = reinterpret_cast<float*>(b + off);
+  off += align256(size_t(row_tiles(chunk)) * size_t(v) * 4);
   w.slice = reinterpret_cast<float*>(b + off);
   w.ldz = round_up(v, kGroup);
   return w;
@@ -438,7 +558,8 @@ size_t flce_workspace_bytes(int64_t n, int64_t h, int64_t v, int64_t chunk_size,
   const int64_t c = chunk_size < n ? chunk_size : (n > 0 ? n : 1);
   const int64_t ldz = round_up(v, kGroup);
   return 256 + align256(size_t(n) * 4) + align256(size_t(c) * 4) +
-         align256(size_t(c) * size_t(lse_tiles(v)) * 8) + align256(size_t(c) * size_t(ldz) * 4);
+         align256(size_t(c) * size_t(lse_tiles(v)) * 8) + align256(size_t(c) * 4) +
+         align256(size_t(row_tiles(c)) * size_t(v) * 4) + align256(size_t(c) * size_t(ldz) * 4);
 }
 
 hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
@@ -447,6 +568,9 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
   FlceWs ws = flce_carve(a.workspace, n, v, chunk);
   const long long th = a.num_label_tokens >= 0 ? a.num_label_tokens : -1;
   const bool accumulate = (a.flags & FLCE_ACCUMULATE) != 0;
+  // the recomputing schedule needs the pipelined GEMM's epilogue hooks (h % 64 == 0); for other
+  // h the flag runs the stored-slice schedule, whose results are the same
+  const bool recompute = (a.flags & FLCE_RECOMPUTE) != 0 && h % Wide::BK == 0;
   hipError_t e;
 
   if ((e = launch_label_prep(a.labels, n, v, a.ignore_index, ws.count, a.status_out, s)) != hipSuccess)
@@ -470,51 +594,91 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     const int32_t* lab = a.labels + c0;
     const uint16_t* hid = a.hidden + c0 * h;
 
-    // 1. logits slice (the pipelined GEMM also leaves per-tile logsumexp pairs; the register-
-    //    staged one, used when h is not a multiple of 64, does not)
     View Ah{hid, h, kGroup, rows, h};
     View Bw{a.weight, h, kGroup, v, h};
-    EpiLogits el{ws.slice, ws.ldz, a.bias, ws.part, ws.tiles};
     const bool fused_lse = h % Wide::BK == 0;
-    {
-      TimedLaunch t(s, K_FLCE_GEMM_LOGITS);
-      e = fused_lse ? gemm::v2::launch<Wide, true, true>(Ah, Bw, rows, v, h, 1, true, el, s)
-                    : gemm::launch<true, true>(Ah, Bw, rows, v, h, 1, true, el, s);
-      if (e != hipSuccess) return e;
-    }
+    float* lo = a.lse_out ? a.lse_out + c0 : nullptr;
+    if (!recompute) {
+      // 1. logits slice (the pipelined GEMM also leaves per-tile logsumexp pairs; the
+      //    register-staged one, used when h is not a multiple of 64, does not)
+      EpiLogits el{ws.slice, ws.ldz, a.bias, ws.part, ws.tiles};
+      {
+        TimedLaunch t(s, K_FLCE_GEMM_LOGITS);
+        e = fused_lse ? gemm::v2::launch<Wide, true, true>(Ah, Bw, rows, v, h, 1, true, el, s)
+                      : gemm::launch<true, true>(Ah, Bw, rows, v, h, 1, true, el, s);
+        if (e != hipSuccess) return e;
+      }
 
-    // 2. row logsumexp and loss terms
-    {
-      TimedLaunch t(s, K_FLCE_ROW_LSE);
-      float* lo = a.lse_out ? a.lse_out + c0 : nullptr;
-      if (fused_lse)
+      // 2. row logsumexp and loss terms
+      {
+        TimedLaunch t(s, K_FLCE_ROW_LSE);
+        if (fused_lse)
+          hipLaunchKernelGGL(lse_merge_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0,
+                             s, ws.part, ws.tiles, ws.slice, ws.ldz, nullptr, rows, v, lab,
+                             a.ignore_index, ws.lse_c, ws.row_loss + c0, lo);
+        else
+          hipLaunchKernelGGL(slice_row_lse_kernel, dim3(unsigned(rows)), dim3(kRowThreads), 0, s,
+                             ws.slice, ws.ldz, v, lab, a.ignore_index, ws.lse_c,
+                             ws.row_loss + c0, lo);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
+
+      // 3. bias gradient from the fp32 logits
+      if (a.grad_bias) {
+        TimedLaunch t(s, K_FLCE_BIAS_GRAD);
+        hipLaunchKernelGGL(slice_bias_grad_kernel, dim3(unsigned((v + 255) / 256)), dim3(256), 0,
+                           s, ws.slice, ws.ldz, rows, v, lab, a.ignore_index, ws.lse_c,
+                           a.grad_bias, int(first && !accumulate), ws.count, th, a.grad_output);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
+      if (!a.grad_hidden && !a.grad_weight) continue;
+
+      // 4. probabilities in place
+      const int64_t groups = ws.ldz / kGroup;
+      {
+        TimedLaunch t(s, K_FLCE_TO_PROBS);
+        hipLaunchKernelGGL(slice_to_probs_kernel,
+                           dim3(unsigned((groups + 15) / 16), unsigned(rows)), dim3(256), 0, s,
+                           ws.slice, ws.ldz, v, lab, a.ignore_index, ws.lse_c);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
+    } else {
+      // 1'. pass 1: the logits are reduced to per-tile logsumexp pairs and the label logit,
+      //     never stored
+      EpiLseOnly e1{a.bias, ws.part, ws.tiles, lab, ws.zy};
+      {
+        TimedLaunch t(s, K_FLCE_GEMM_LOGITS);
+        if ((e = gemm::v2::launch<Wide, true, true>(Ah, Bw, rows, v, h, 1, true, e1, s)) !=
+            hipSuccess)
+          return e;
+      }
+      // 2'. row logsumexp and loss terms
+      {
+        TimedLaunch t(s, K_FLCE_ROW_LSE);
         hipLaunchKernelGGL(lse_merge_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s,
-                           ws.part, ws.tiles, ws.slice, ws.ldz, rows, v, lab, a.ignore_index,
+                           ws.part, ws.tiles, nullptr, 0, ws.zy, rows, v, lab, a.ignore_index,
                            ws.lse_c, ws.row_loss + c0, lo);
-      else
-        hipLaunchKernelGGL(slice_row_lse_kernel, dim3(unsigned(rows)), dim3(kRowThreads), 0, s,
-                           ws.slice, ws.ldz, v, lab, a.ignore_index, ws.lse_c, ws.row_loss + c0,
-                           lo);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-
-    // 3. bias gradient from the fp32 logits
-    if (a.grad_bias) {
-      TimedLaunch t(s, K_FLCE_BIAS_GRAD);
-      hipLaunchKernelGGL(slice_bias_grad_kernel, dim3(unsigned((v + 255) / 256)), dim3(256), 0, s,
-                         ws.slice, ws.ldz, rows, v, lab, a.ignore_index, ws.lse_c, a.grad_bias,
-                         int(first && !accumulate), ws.count, th, a.grad_output);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    if (!a.grad_hidden && !a.grad_weight) continue;
-
-    // 4. probabilities in place
-    const int64_t groups = ws.ldz / kGroup;
-    {
-      TimedLaunch t(s, K_FLCE_TO_PROBS);
-      hipLaunchKernelGGL(slice_to_probs_kernel, dim3(unsigned((groups + 15) / 16), unsigned(rows)),
-                         dim3(256), 0, s, ws.slice, ws.ldz, v, lab, a.ignore_index, ws.lse_c);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
+      if (!a.grad_hidden && !a.grad_weight && !a.grad_bias) continue;
+      // 3'. pass 2: the logits are recomputed tile by tile and leave as bf16 probabilities in
+      //     the slice (and, for grad_bias, as fp32 column sums)
+      EpiProbs e2{reinterpret_cast<uint16_t*>(ws.slice), 2 * ws.ldz, a.bias, ws.lse_c, lab, v,
+                  a.ignore_index, a.grad_bias ? ws.colsum : nullptr};
+      {
+        TimedLaunch t(s, K_FLCE_GEMM_PROBS);
+        if ((e = gemm::v2::launch<Wide, true, true>(Ah, Bw, rows, ws.ldz, h, 1, true, e2, s)) !=
+            hipSuccess)
+          return e;
+      }
+      if (a.grad_bias) {
+        TimedLaunch t(s, K_FLCE_BIAS_GRAD);
+        hipLaunchKernelGGL(bias_from_colsums_kernel, dim3(unsigned((v + 255) / 256)), dim3(256), 0,
+                           s, ws.colsum, row_tiles(rows), rows, v, lab, a.ignore_index,
+                           a.grad_bias, int(first && !accumulate), ws.count, th, a.grad_output);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
+      if (!a.grad_hidden && !a.grad_weight) continue;
     }
     const uint16_t* P = reinterpret_cast<const uint16_t*>(ws.slice);
     const int64_t p_ld = 2 * ws.ldz, p_gs = 2 * kGroup;

@@ -578,6 +578,9 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
     rm[i] = -INFINITY;
     rs[i] = 0.f;
   }
+  f32x4_t cs[TN];  // kColSums: this lane's column sums (4 columns per fragment column)
+#pragma unroll
+  for (int j = 0; j < TN; ++j) cs[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i0 = 0; i0 < TM; i0 += 2) {
     typename Epi::Aux aux[2][TN];
@@ -599,6 +602,7 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
         const int64_t gn = n0 + wn * (C::BN / C::WN) + 16 * j + 4 * (lane >> 4);
         if (gn + 4 <= N) {
           epi.store4(gm, gn, acc[i0 + di][j], aux[di][j]);
+          if constexpr (Epi::kColSums) cs[j] += epi.colvalue4(acc[i0 + di][j], aux[di][j]);
           if constexpr (Epi::kRowStats) {
             const f32x4_t z = epi.value4(acc[i0 + di][j], aux[di][j]);
             const float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
@@ -625,6 +629,33 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
             }
         }
       }
+    }
+  }
+  if constexpr (Epi::kColSums) {
+    // (launched with N % 4 == 0: every column went through colvalue4.) Lanes 16 g .. 16 g + 15
+    // hold the same columns: reduce over them, then over the WM wavefronts sharing the
+    // columns through LDS, in wavefront order.
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int off = 1; off <= 8; off <<= 1) cs[j][q] += __shfl_xor(cs[j][q], off, 64);
+    __syncthreads();  // every wavefront is past the main loop: the LDS ring is free
+    float* cred = reinterpret_cast<float*>(lds + 16384);  // [WM][BN]
+    if ((lane & 15) == 0) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          cred[wm * C::BN + wn * (C::BN / C::WN) + 16 * j + 4 * (lane >> 4) + q] = cs[j][q];
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < C::BN; c += C::THREADS) {
+      float sum = cred[c];
+#pragma unroll
+      for (int w = 1; w < C::WM; ++w) sum += cred[w * C::BN + c];
+      if (n0 + c < N) epi.col_sums(tc.mt, n0 + c, sum);
     }
   }
   if constexpr (Epi::kRowStats) {
