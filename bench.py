@@ -68,7 +68,7 @@ KERNEL_NAMES = [
     ("slice_row_lse_kernel", "flce_row_lse"), ("slice_bias_grad_kernel", "flce_bias_grad"),
     ("slice_to_probs_kernel", "flce_to_probs"), ("onehot_weight_fix_kernel", "flce_onehot_fix"),
     ("grad_hidden_reduce_kernel", "flce_grad_hidden_reduce"), ("fill_zero", "fill_zero"),
-    ("label_prep_kernel", "label_prep"), ("loss_reduce_kernel", "loss_reduce"),
+    ("label_sort_kernel", "flce_label_sort"), ("label_prep_kernel", "label_prep"), ("loss_reduce_kernel", "loss_reduce"),
     ("ce_fwd_rows_kernel", "ce_fwd_rows"), ("ce_bwd_rows_kernel", "ce_bwd_rows"),
 ]
 CALIB_BYTES = 1 << 30  # bytes read and bytes written by one launch of the calibration copy

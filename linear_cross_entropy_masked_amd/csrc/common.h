@@ -98,6 +98,7 @@ enum KernelId {
   K_FILL,
   K_FLCE_GRAD_HIDDEN_REDUCE,
   K_FLCE_GEMM_PROBS,
+  K_FLCE_LABEL_SORT,
   K_COUNT
 };
 

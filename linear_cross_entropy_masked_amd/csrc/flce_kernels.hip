@@ -80,6 +80,12 @@ struct EpiLogits {
   }
 };
 
+// Once the slice holds probabilities (first half of every 64-column group), the second half
+// of every group is free scratch: flat element e sits at float offset (e / 32) * 64 + 32 +
+// e % 32. It takes grad_hidden's split-K partial sums and the recomputing schedule's
+// probability column sums.
+__device__ __forceinline__ int64_t gap_index(int64_t e) { return (e >> 5) * 64 + 32 + (e & 31); }
+
 // Pass 1 of the recomputing schedule: the logits tile is only reduced, never stored. Leaves
 // the per-tile (max, Σ exp) pairs like EpiLogits, and zy[m] = z[m, y_m] for the tile holding
 // the label column.
@@ -117,7 +123,8 @@ struct EpiLseOnly {
 // P = exp(z − lse) in the slice's probability layout (first half of every 64-column group),
 // 0 for rows without a label and for the padding columns v .. ldz − 1 (the GEMM runs over
 // N = ldz; weight rows past v read as zero). With grad_bias it also leaves, per 256-row tile
-// mt and column n, colsum[mt · v + n] = Σ_m p (the fp32 values, before rounding).
+// mt and column n, Σ_m p (the fp32 values, before rounding) as flat element mt · v + n of the
+// slice's free halves.
 struct EpiProbs {
   uint16_t* p;
   int64_t p_ld;  // elements between rows (2 · ldz)
@@ -126,7 +133,7 @@ struct EpiProbs {
   const int32_t* labels;
   int64_t v;
   int32_t ignore_index;
-  float* colsum;  // NULL: no column sums
+  float* colsum;  // the slice as floats, or NULL: no column sums
   static constexpr bool kRowStats = false;
   static constexpr bool kColSums = true;
   __device__ void begin(int64_t) {}
@@ -165,7 +172,7 @@ struct EpiProbs {
   }
   __device__ __forceinline__ void operator()(int64_t, int64_t, float) {}  // N % 4 == 0: unused
   __device__ __forceinline__ void col_sums(int64_t mt, int64_t n, float sum) {
-    if (colsum && n < v) colsum[mt * v + n] = sum;
+    if (colsum && n < v) colsum[gap_index(mt * v + n)] = sum;
   }
 };
 
@@ -236,10 +243,80 @@ struct EpiGradWeight {
   }
 };
 
-// Split-K partial sums of grad_hidden live in the unused second half of every 64-column
-// group of the slice once it holds probabilities: flat element e sits at float offset
-// (e / 32) * 64 + 32 + e % 32.
-__device__ __forceinline__ int64_t gap_index(int64_t e) { return (e >> 5) * 64 + 32 + (e & 31); }
+// Each chunk's rows sorted by label, stably (rows in increasing order within a label):
+// slab[c0 + p] is the chunk's p-th smallest label (rows without a label count as 0x7fffffff
+// and come last) and srow[c0 + p] its row within the chunk. Workgroup b sorts the chunk that
+// starts at row c0 = b · chunk; each row's position is the number of the chunk's rows before
+// it in that order, counted over the labels held in LDS.
+constexpr int kSortMax = 8192;
+__global__ void __launch_bounds__(1024) label_sort_kernel(const int32_t* __restrict__ labels_all,
+                                                          int64_t n_all, int64_t chunk, int64_t v,
+                                                          int32_t ignore_index,
+                                                          int32_t* __restrict__ slab_all,
+                                                          int32_t* __restrict__ srow_all) {
+  __shared__ __attribute__((aligned(16))) int32_t k[kSortMax];
+  const int64_t c0 = int64_t(blockIdx.x) * chunk;
+  const int n = int(n_all - c0 < chunk ? n_all - c0 : chunk);
+  const int32_t* labels = labels_all + c0;
+  int32_t* slab = slab_all + c0;
+  int32_t* srow = srow_all + c0;
+  for (int i = threadIdx.x; i < n; i += 1024) {
+    const int32_t y = labels[i];
+    k[i] = has_label(y, v, ignore_index) ? y : 0x7fffffff;
+  }
+  for (int i = n + threadIdx.x; i < ((n + 3) & ~3); i += 1024) k[i] = 0x7fffffff;  // pad to 4
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += 1024) {
+    const int32_t x = k[i];
+    int rank = 0;
+    const int n4 = (n + 3) >> 2;
+    for (int j4 = 0; j4 < n4; ++j4) {
+      const int4 q = reinterpret_cast<const int4*>(k)[j4];
+      const int j = 4 * j4;
+      rank += (q.x < x) | ((q.x == x) & (j < i));
+      rank += (q.y < x) | ((q.y == x) & (j + 1 < i));
+      rank += (q.z < x) | ((q.z == x) & (j + 2 < i));
+      rank += (q.w < x) | ((q.w == x) & (j + 3 < i));
+    }
+    slab[rank] = x;
+    srow[rank] = i;
+  }
+}
+
+// dW[y] −= coef · Σ_{i in chunk, y_i = y} h_i. Workgroup p handles sorted position p if it
+// starts a run of equal labels: it adds the run's hidden rows in increasing row order and
+// updates dW row y once.
+__global__ void __launch_bounds__(256) onehot_segments_kernel(
+    const uint16_t* __restrict__ hidden, int64_t h, int64_t rows,
+    const int32_t* __restrict__ slab, const int32_t* __restrict__ srow, int64_t v,
+    float* grad_weight, const long long* count_dev, long long count_host, const float* gout) {
+  const int64_t p = blockIdx.x;
+  const int32_t y = slab[p];
+  if (y >= v || (p > 0 && slab[p - 1] == y)) return;
+  int64_t end = p + 1;
+  while (end < rows && slab[end] == y) ++end;
+  const float coef = flce_coef(count_dev, count_host, gout);
+  for (int64_t col = 4 * int64_t(threadIdx.x); col < h; col += 4 * 256) {
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int64_t e = p; e < end; ++e) {
+      const uint16_t* hr = hidden + int64_t(srow[e]) * h + col;
+      if (col + 4 <= h) {
+        const uint2 x = *reinterpret_cast<const uint2*>(hr);
+        a0 += bf16_lo(x.x); a1 += bf16_hi(x.x); a2 += bf16_lo(x.y); a3 += bf16_hi(x.y);
+      } else {
+        a0 += bf16_to_f32(hr[0]);
+        if (col + 1 < h) a1 += bf16_to_f32(hr[1]);
+        if (col + 2 < h) a2 += bf16_to_f32(hr[2]);
+      }
+    }
+    float* d = grad_weight + int64_t(y) * h + col;
+    d[0] -= coef * a0;
+    if (col + 1 < h) d[1] -= coef * a1;
+    if (col + 2 < h) d[2] -= coef * a2;
+    if (col + 3 < h) d[3] -= coef * a3;
+  }
+}
+
 
 struct EpiPartial {
   static constexpr bool kColSums = false;
@@ -407,7 +484,7 @@ __global__ void __launch_bounds__(256) slice_bias_grad_kernel(
 }
 
 // grad_bias[v] (=|+=) coef · (Σ_mt colsum[mt, v] − #{labelled i: y_i = v}), the column sums
-// added in row-tile order.
+// (in the slice's free halves) added in row-tile order.
 __global__ void __launch_bounds__(256) bias_from_colsums_kernel(
     const float* __restrict__ colsum, int64_t mtiles, int64_t rows, int64_t v,
     const int32_t* __restrict__ labels, int32_t ignore_index, float* __restrict__ grad_bias,
@@ -415,7 +492,7 @@ __global__ void __launch_bounds__(256) bias_from_colsums_kernel(
   const int64_t col = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (col >= v) return;
   float sp = 0.f;
-  for (int64_t t = 0; t < mtiles; ++t) sp += colsum[t * v + col];
+  for (int64_t t = 0; t < mtiles; ++t) sp += colsum[gap_index(t * v + col)];
   int cnt = 0;
   for (int64_t i = 0; i < rows; ++i) {
     const int32_t y = labels[i];
@@ -510,7 +587,8 @@ struct FlceWs {
   float2* part;     // [C, tiles] per-tile (max, Σ exp) of the logits rows
   int64_t tiles;
   float* zy;        // [C] label logits (recomputing schedule)
-  float* colsum;    // [C / 256, V] probability column sums (recomputing schedule, bias)
+  int32_t* slab;    // [n] every chunk's labels sorted (one-hot term of dW)
+  int32_t* srow;    // [n] their rows within the chunk
   float* slice;     // [C, ldz] fp32
   int64_t ldz;
 };
@@ -534,8 +612,10 @@ FlceWs flce_carve(void* base, int64_t n, int64_t v, int64_t chunk) {
   off += align256(size_t(chunk) * size_t(w.tiles) * 8);
   w.zy = reinterpret_cast<float*>(b + off);
   off += align256(size_t(chunk) * 4);
-  w.colsum = reinterpret_cast<float*>(b + off);
-  off += align256(size_t(row_tiles(chunk)) * size_t(v) * 4);
+  w.slab = reinterpret_cast<int32_t*>(b + off);
+  off += align256(size_t(n) * 4);
+  w.srow = reinterpret_cast<int32_t*>(b + off);
+  off += align256(size_t(n) * 4);
   w.slice = reinterpret_cast<float*>(b + off);
   w.ldz = round_up(v, kGroup);
   return w;
@@ -559,7 +639,7 @@ size_t flce_workspace_bytes(int64_t n, int64_t h, int64_t v, int64_t chunk_size,
   const int64_t ldz = round_up(v, kGroup);
   return 256 + align256(size_t(n) * 4) + align256(size_t(c) * 4) +
          align256(size_t(c) * size_t(lse_tiles(v)) * 8) + align256(size_t(c) * 4) +
-         align256(size_t(row_tiles(c)) * size_t(v) * 4) + align256(size_t(c) * size_t(ldz) * 4);
+         2 * align256(size_t(n) * 4) + align256(size_t(c) * size_t(ldz) * 4);
 }
 
 hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
@@ -588,6 +668,15 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     }
   }
 
+  // every chunk's labels sorted into runs up front (one-hot term of dW), when chunks fit LDS
+  const bool sorted_labels = a.grad_weight && n > 0 && chunk <= kSortMax;
+  if (sorted_labels) {
+    TimedLaunch t(s, K_FLCE_LABEL_SORT);
+    hipLaunchKernelGGL(label_sort_kernel, dim3(unsigned((n + chunk - 1) / chunk)), dim3(1024), 0,
+                       s, a.labels, n, chunk, v, a.ignore_index, ws.slab, ws.srow);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+
   for (int64_t c0 = 0; c0 < n; c0 += chunk) {
     const int64_t rows = (n - c0) < chunk ? (n - c0) : chunk;
     const bool first = c0 == 0;
@@ -598,7 +687,12 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     View Bw{a.weight, h, kGroup, v, h};
     const bool fused_lse = h % Wide::BK == 0;
     float* lo = a.lse_out ? a.lse_out + c0 : nullptr;
-    if (!recompute) {
+    // grad_bias column sums of the recomputing schedule sit in the slice's free halves: the
+    // highest float offset they reach must stay inside the slice (fails only for chunks of a
+    // row or two; those take the stored-slice schedule, same results)
+    const bool recompute_chunk =
+        recompute && (!a.grad_bias || 2 * row_tiles(rows) * v + 64 <= chunk * ws.ldz);
+    if (!recompute_chunk) {
       // 1. logits slice (the pipelined GEMM also leaves per-tile logsumexp pairs; the
       //    register-staged one, used when h is not a multiple of 64, does not)
       EpiLogits el{ws.slice, ws.ldz, a.bias, ws.part, ws.tiles};
@@ -664,7 +758,7 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
       // 3'. pass 2: the logits are recomputed tile by tile and leave as bf16 probabilities in
       //     the slice (and, for grad_bias, as fp32 column sums)
       EpiProbs e2{reinterpret_cast<uint16_t*>(ws.slice), 2 * ws.ldz, a.bias, ws.lse_c, lab, v,
-                  a.ignore_index, a.grad_bias ? ws.colsum : nullptr};
+                  a.ignore_index, a.grad_bias ? ws.slice : nullptr};
       {
         TimedLaunch t(s, K_FLCE_GEMM_PROBS);
         if ((e = gemm::v2::launch<Wide, true, true>(Ah, Bw, rows, ws.ldz, h, 1, true, e2, s)) !=
@@ -674,7 +768,7 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
       if (a.grad_bias) {
         TimedLaunch t(s, K_FLCE_BIAS_GRAD);
         hipLaunchKernelGGL(bias_from_colsums_kernel, dim3(unsigned((v + 255) / 256)), dim3(256), 0,
-                           s, ws.colsum, row_tiles(rows), rows, v, lab, a.ignore_index,
+                           s, ws.slice, row_tiles(rows), rows, v, lab, a.ignore_index,
                            a.grad_bias, int(first && !accumulate), ws.count, th, a.grad_output);
         if ((e = hipGetLastError()) != hipSuccess) return e;
       }
@@ -718,9 +812,19 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (a.grad_weight) {
-      TimedLaunch t(s, K_FLCE_ONEHOT_FIX);
-      hipLaunchKernelGGL(onehot_weight_fix_kernel, dim3(unsigned(rows)), dim3(256), 0, s, hid, h,
-                         rows, lab, a.ignore_index, v, a.grad_weight, ws.count, th, a.grad_output);
+      // one-hot term of dW: one pass over the chunk's labels sorted into runs (chunks up to
+      // kSortMax rows), else the per-row pass that finds each label's first row by scanning
+      if (sorted_labels) {
+        TimedLaunch t(s, K_FLCE_ONEHOT_FIX);
+        hipLaunchKernelGGL(onehot_segments_kernel, dim3(unsigned(rows)), dim3(256), 0, s, hid, h,
+                           rows, ws.slab + c0, ws.srow + c0, v, a.grad_weight, ws.count, th,
+                           a.grad_output);
+      } else {
+        TimedLaunch t(s, K_FLCE_ONEHOT_FIX);
+        hipLaunchKernelGGL(onehot_weight_fix_kernel, dim3(unsigned(rows)), dim3(256), 0, s, hid,
+                           h, rows, lab, a.ignore_index, v, a.grad_weight, ws.count, th,
+                           a.grad_output);
+      }
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }

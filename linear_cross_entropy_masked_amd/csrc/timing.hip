@@ -39,7 +39,7 @@ const char* kNames[K_COUNT] = {
     "ce_bwd_rows",        "flce_gemm_logits",      "flce_row_lse",
     "flce_bias_grad",     "flce_to_probs",         "flce_gemm_grad_hidden",
     "flce_gemm_grad_weight", "flce_onehot_fix",    "fill_zero",
-    "flce_grad_hidden_reduce", "flce_gemm_probs",
+    "flce_grad_hidden_reduce", "flce_gemm_probs", "flce_label_sort",
 };
 
 }  // namespace
