@@ -9,7 +9,10 @@ synthetic input already resident in HBM:
     [128256, 4096] bf16, no bias, 5% ignored labels, chunk 1024 (loss, grad_hidden, fp32
     grad_weight) — this is `value` (tokens/s), with the bf16 MFMA roofline;
   * chunked masked CE on [16384, 128256] bf16 logits (spiked labels, 5% ignored, chunk 1024,
-    in-place backward) — reported under "ce_only" with its HBM roofline.
+    in-place backward) — reported under "ce_only" with its HBM roofline;
+  * fused linear CE on the long-context packed workload (hidden [32768, 8192], weight
+    [128256, 8192], 8 documents, chunk 2048) with the recomputing schedule — reported under
+    "long_context" (at most 3 timed steps; --no-long-context skips it).
 
 Prints one JSON line. Timing uses hipEvents recorded on the stream the library launches on;
 the in-place CE backward destroys its input, so the logits are restored from a pristine copy
@@ -33,6 +36,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "FLCE fwd+bwd tokens/s (H4096,V128256) % MFMA peak; CE-only HBM GB/s % peak"
 
 FLCE_WORKLOAD = "flce_8192x4096x128256"
+LONG_WORKLOAD = "flce_32768x8192x128256_packed"
 CE_WORKLOAD = "ce_16384x128256"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "linear_cross_entropy_masked_amd", "csrc")
@@ -174,8 +178,10 @@ def timed_kernels(torch, lce, stream, step, steps):
     return steps, ev[0].elapsed_time(ev[1]) / steps, kernels
 
 
-def run_flce(args, torch, lce, workloads):
-    w = workloads.WORKLOADS[FLCE_WORKLOAD]
+def run_flce(args, torch, lce, workloads, name=None, recompute=False, steps=None, warmup=None):
+    w = workloads.WORKLOADS[name or FLCE_WORKLOAD]
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
     t0 = time.time()
     inp = workloads.make_flce_inputs(w, seed=0)
     gen_s = time.time() - t0
@@ -186,16 +192,17 @@ def run_flce(args, torch, lce, workloads):
     lab = torch.from_numpy(inp.labels).to(dev)
     gh = torch.empty((w.n, w.h), dtype=torch.bfloat16, device=dev)
     gw = torch.empty((w.v, w.h), dtype=torch.float32, device=dev)
-    ws = torch.empty(lce.flce_workspace_size(w.n, w.h, w.v, w.chunk_size, 0), dtype=torch.uint8,
-                     device=dev)
+    flags = lce.FLCE_RECOMPUTE if recompute else 0
+    ws = torch.empty(lce.flce_workspace_size(w.n, w.h, w.v, w.chunk_size, flags),
+                     dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     nvalid = int((inp.labels != -100).sum())
 
     def step():
         return lce.flce_fwd_bwd(hid, wt, lab, None, chunk_size=w.chunk_size, grad_hidden=gh,
-                                grad_weight=gw, workspace=ws)
+                                grad_weight=gw, workspace=ws, recompute=recompute)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     mem_before = torch.cuda.memory_allocated(dev)
@@ -204,17 +211,17 @@ def run_flce(args, torch, lce, workloads):
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     ev[0].record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         loss = step()[0]
     ev[1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    ms = ev[0].elapsed_time(ev[1]) / steps
     peak_extra = torch.cuda.max_memory_allocated(dev) - mem_before + ws.numel()
 
     # per-kernel breakdown: the same K steps again with a hipEvent pair around every launch,
     # recorded by the library on the stream it launches on
-    kreps, inst_ms, kernels = timed_kernels(torch, lce, stream, step, args.steps)
+    kreps, inst_ms, kernels = timed_kernels(torch, lce, stream, step, steps)
 
     flops = 6.0 * w.n * w.h * w.v
     chunks = -(-w.n // w.chunk_size)
@@ -232,10 +239,12 @@ def run_flce(args, torch, lce, workloads):
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                 "avg_launch_ms": round(avg_ms, 4),
-                "traffic": stored_traffic(dom[0], FLCE_WORKLOAD)}
+                "traffic": stored_traffic(dom[0], w.name)}
+    executed = (8.0 if recompute else 6.0) * w.n * w.h * w.v
     return {
         "workload": w, "ms": ms, "wall_s": wall, "tokens_per_s": w.n / (ms * 1e-3),
         "tflops": flops / (ms * 1e-3) / 1e12, "loss": float(loss.item()), "roofline": roof,
+        "executed_tflops": executed / (ms * 1e-3) / 1e12,
         "instrumented_ms": inst_ms,
         "kernels": {k[0]: {"ms_per_step": round(k[1] / kreps, 4), "launches_per_step": k[2] // kreps}
                     for k in kernels},
@@ -362,6 +371,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["flce", "ce"], default=None,
                     help="run one layer only (profiling)")
+    ap.add_argument("--no-long-context", action="store_true",
+                    help="skip the [32768, 8192] x [128256, 8192] recompute workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a 1 GiB copy whose HBM counters calibrate the others")
     ap.add_argument("--record-traffic", nargs=3, metavar=("LAYER", "FETCH_DIR", "WRITE_DIR"),
@@ -413,6 +424,24 @@ def main(argv=None) -> int:
             "slice_budget_bytes": fl["slice_budget_bytes"],
             "loss": fl["loss"],
         })
+    if args.only in (None, "flce") and not args.no_long_context:
+        lc = run_flce(args, torch, lce, workloads, name=LONG_WORKLOAD, recompute=True,
+                      steps=min(args.steps, 3), warmup=1)
+        w = lc["workload"]
+        print(f"# flce {w.name} (recompute): {lc['ms']:.3f} ms/step, "
+              f"{lc['tokens_per_s']:.0f} tokens/s", file=sys.stderr, flush=True)
+        out["long_context"] = {
+            "workload": w.name, "schedule": "recompute (logits GEMM twice: 8*N*H*V flop)",
+            "tokens": w.n, "hidden": w.h, "vocab": w.v, "chunk_size": w.chunk_size,
+            "steps": min(args.steps, 3), "ms_per_step": round(lc["ms"], 3),
+            "tokens_per_s": round(lc["tokens_per_s"], 1),
+            "model_tflops": round(lc["tflops"], 2), "executed_tflops": round(lc["executed_tflops"], 2),
+            "mfma_frac_executed": round(lc["executed_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+            "roofline": lc["roofline"], "kernels": lc["kernels"],
+            "peak_extra_bytes": lc["peak_extra_bytes"], "slice_budget_bytes": lc["slice_budget_bytes"],
+            "loss": lc["loss"]}
+        del lc
+        torch.cuda.empty_cache()
     if args.only in (None, "ce"):
         ce = run_ce(args, torch, lce, workloads)
         w = ce["workload"]

@@ -217,3 +217,31 @@ def test_llama3_head_workload_sampled(dev):
     gw = device_to_f64(res["gw"][torch.from_numpy(wrows).to(dev)])
     assert normwise_rel(gw, ref.grad_weight) <= 1e-4
     assert math.isfinite(res["loss"])
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(1500)
+def test_long_context_packed_workload_sampled(dev):
+    """[32768, 8192] x [128256, 8192], 8 packed documents, chunk 2048, with the recomputing
+    schedule: the full loss and every row's lse against the oracle, grad_hidden rows and
+    grad_weight rows (label hits and others) on samples."""
+    w = WORKLOADS["flce_32768x8192x128256_packed"]
+    inp = make_flce_inputs(w, seed=0)
+    assert int((inp.labels == -100).sum()) == 8
+    res = run_flce(dev, inp, w.chunk_size, recompute=True)
+    rng = np.random.default_rng(2)
+    hrows = np.unique(np.concatenate([[0, w.n - 1], rng.choice(w.n, 30, replace=False)]))
+    lab = inp.labels
+    hit = np.unique(lab[lab >= 0])
+    wrows = np.unique(np.concatenate([[0, w.v - 1], rng.choice(hit, 16, replace=False),
+                                      rng.choice(w.v, 16, replace=False)]))
+    ref = oracle.flce(inp.hidden, inp.weight, lab, hidden_rows=hrows, weight_rows=wrows)
+    assert_close_rel(res["loss"], ref.loss, 1e-5)
+    ok = lab != -100
+    assert np.all(np.abs(res["lse"][ok] - ref.lse[ok]) <= 1e-5 * np.abs(ref.lse[ok]))
+    gh = device_to_f64(res["gh"][torch.from_numpy(hrows).to(dev)])
+    assert np.max(np.abs(gh - ref.grad_hidden)) <= 2e-3
+    assert normwise_rel(gh, ref.grad_hidden) <= 1e-2
+    assert not res["gh"][torch.from_numpy(np.nonzero(~ok)[0]).to(dev)].any().item()
+    gw = device_to_f64(res["gw"][torch.from_numpy(wrows).to(dev)])
+    assert normwise_rel(gw, ref.grad_weight) <= 1e-4
