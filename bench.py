@@ -369,8 +369,9 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["flce", "ce"], default=None,
-                    help="run one layer only (profiling)")
+    ap.add_argument("--only", choices=["flce", "long", "ce"], default=None,
+                    help="run one workload only (profiling): the Llama3-8B-shaped FLCE head, "
+                         "the long-context recompute FLCE, or the CE-only logits")
     ap.add_argument("--no-long-context", action="store_true",
                     help="skip the [32768, 8192] x [128256, 8192] recompute workload")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -381,7 +382,8 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
     if args.record_traffic:
         layer, fdir, wdir = args.record_traffic
-        record_traffic({"flce": FLCE_WORKLOAD, "ce": CE_WORKLOAD}[layer], fdir, wdir)
+        record_traffic({"flce": FLCE_WORKLOAD, "long": LONG_WORKLOAD, "ce": CE_WORKLOAD}[layer],
+                       fdir, wdir)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -424,7 +426,7 @@ def main(argv=None) -> int:
             "slice_budget_bytes": fl["slice_budget_bytes"],
             "loss": fl["loss"],
         })
-    if args.only in (None, "flce") and not args.no_long_context:
+    if args.only == "long" or (args.only is None and not args.no_long_context):
         lc = run_flce(args, torch, lce, workloads, name=LONG_WORKLOAD, recompute=True,
                       steps=min(args.steps, 3), warmup=1)
         w = lc["workload"]
@@ -440,6 +442,12 @@ def main(argv=None) -> int:
             "roofline": lc["roofline"], "kernels": lc["kernels"],
             "peak_extra_bytes": lc["peak_extra_bytes"], "slice_budget_bytes": lc["slice_budget_bytes"],
             "loss": lc["loss"]}
+        if args.only == "long":
+            out.update({"value": round(lc["tokens_per_s"], 1), "ms_per_step": round(lc["ms"], 4),
+                        "config": {"workload": w.name, "tokens": w.n, "hidden": w.h,
+                                   "vocab": w.v, "chunk_size": w.chunk_size,
+                                   "schedule": "recompute"},
+                        "roofline": lc["roofline"]})
         del lc
         torch.cuda.empty_cache()
     if args.only in (None, "ce"):
