@@ -151,6 +151,34 @@ int flce_fwd_bwd(const uint16_t* hidden, const uint16_t* weight, const float* bi
                  uint16_t* grad_hidden, float* grad_weight, float* grad_bias,
                  int32_t* status_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Split form of flce_fwd_bwd for callers that run the loss in a forward pass and the
+ * gradients in a later backward pass (Liger-Kernel issue #533, feature pitch and comments:
+ * keeping a [V, H] grad_weight alive from forward to backward is what a fully recomputed
+ * variant avoids). Between the two calls only lse [n] (fp32, 4·n bytes) has to be kept.
+ *
+ * flce_fwd: loss_out and lse_out (both required; lse_out [n] receives the logsumexp of each
+ * labelled row, 0 for the others). With h a multiple of 64 the logits are reduced inside the
+ * logits GEMM and never stored; otherwise they pass through the workspace slice. No
+ * gradients; the workspace is sized by flce_workspace_size(n, h, v, chunk_size, 0). */
+int flce_fwd(const uint16_t* hidden, const uint16_t* weight, const float* bias,
+             const int32_t* labels, int64_t n, int64_t h, int64_t v, int32_t ignore_index,
+             int64_t chunk_size, int64_t num_label_tokens, float* loss_out, float* lse_out,
+             int32_t* status_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* flce_bwd: the gradients of flce_fwd_bwd from flce_fwd's lse (same hidden, weight, bias,
+ * labels, ignore_index and num_label_tokens): per chunk the logits are recomputed and turned
+ * into bf16 probabilities with the given lse, then grad_hidden / grad_weight / grad_bias as
+ * in flce_fwd_bwd (any may be NULL; grad_bias needs bias). flags: FLCE_ACCUMULATE only
+ * (FLCE_RECOMPUTE is implied and rejected with LCE_ERR_BAD_FLAGS). No loss. grad_hidden and
+ * grad_weight equal flce_fwd_bwd's bit for bit; grad_bias is summed in another order when
+ * h is a multiple of 64. */
+int flce_bwd(const uint16_t* hidden, const uint16_t* weight, const float* bias,
+             const int32_t* labels, const float* lse, int64_t n, int64_t h, int64_t v,
+             int32_t ignore_index, int64_t chunk_size, int64_t num_label_tokens, uint32_t flags,
+             const float* grad_output, uint16_t* grad_hidden, float* grad_weight,
+             float* grad_bias, int32_t* status_out, void* workspace, size_t workspace_bytes,
+             void* stream);
+
 /* ------------------------------------------------------------------ measurement aid */
 
 /* Opt-in launch timing. While enabled, every kernel the library enqueues is bracketed by a

@@ -7,7 +7,7 @@ runs in the library's HIP kernels; there is no CPU or PyTorch fallback, and impo
 function whose library is missing raises.
 
 Entry points (same names as the C ABI):
-    ce_chunked_fwd, ce_chunked_bwd, ce_chunked_bwd_inplace, flce_fwd_bwd,
+    ce_chunked_fwd, ce_chunked_bwd, ce_chunked_bwd_inplace, flce_fwd_bwd, flce_fwd, flce_bwd,
     ce_chunked_workspace_size, flce_workspace_size, lce_status_str
 """
 from __future__ import annotations
@@ -18,7 +18,7 @@ import os
 __all__ = [
     "LceError", "library_path", "load_library",
     "ce_chunked_workspace_size", "ce_chunked_fwd", "ce_chunked_bwd", "ce_chunked_bwd_inplace",
-    "flce_workspace_size", "flce_fwd_bwd", "lce_status_str",
+    "flce_workspace_size", "flce_fwd_bwd", "flce_fwd", "flce_bwd", "lce_status_str",
     "FLCE_RECOMPUTE", "FLCE_ACCUMULATE", "LCE_STATUS_BAD_LABEL",
     "lce_timing_enable", "lce_timing_read",
 ]
@@ -63,6 +63,10 @@ def load_library() -> ctypes.CDLL:
         "flce_workspace_size": (ctypes.c_int, [i64, i64, i64, i64, u32, psz]),
         "flce_fwd_bwd": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, i64, i32, i64, i64, u32, vp, vp, vp,
                                         vp, vp, vp, vp, vp, sz, vp]),
+        "flce_fwd": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, i64, i32, i64, i64, vp, vp, vp, vp,
+                                    sz, vp]),
+        "flce_bwd": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, i64, i64, i32, i64, i64, u32, vp, vp,
+                                    vp, vp, vp, vp, sz, vp]),
         "lce_timing_enable": (ctypes.c_int, [ctypes.c_int]),
         "lce_timing_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
                                            ctypes.POINTER(ctypes.c_double),
@@ -285,6 +289,82 @@ def flce_fwd_bwd(hidden, weight, labels, bias=None, *, ignore_index: int = -100,
         _ptr(gw), _ptr(gb), _ptr(status), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(dev)))
     return loss, gh, gw, gb, lse
+
+
+def _flce_inputs(hidden, weight, labels, bias):
+    import torch
+    _require(hidden, "hidden", torch.bfloat16, 2)
+    dev = hidden.device
+    _require(weight, "weight", torch.bfloat16, 2, dev)
+    n, h = hidden.shape
+    v, h2 = weight.shape
+    if h2 != h:
+        raise ValueError(f"hidden has {h} columns but weight has {h2}")
+    labels = _labels_i32(labels, n, dev)
+    if bias is not None:
+        _require(bias, "bias", torch.float32, 1, dev)
+        if bias.shape[0] != v:
+            raise ValueError("bias must have v entries")
+        bias = bias.contiguous()
+    return hidden.contiguous(), weight.contiguous(), labels, bias, dev, n, h, v
+
+
+def flce_fwd(hidden, weight, labels, bias=None, *, ignore_index: int = -100,
+             chunk_size: int = 1024, num_label_tokens: int | None = None, status=None,
+             workspace=None):
+    """Fused linear CE forward only. Returns (loss, lse); keep lse for :func:`flce_bwd`."""
+    import torch
+    lib = load_library()
+    hidden, weight, labels, bias, dev, n, h, v = _flce_inputs(hidden, weight, labels, bias)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    lse = torch.empty(n, dtype=torch.float32, device=dev)
+    ws = _workspace(flce_workspace_size(n, h, v, chunk_size, 0), dev, workspace)
+    _check("flce_fwd", lib.flce_fwd(
+        _ptr(hidden), _ptr(weight), _ptr(bias), _ptr(labels), n, h, v, ignore_index, chunk_size,
+        _count_arg(num_label_tokens), _ptr(loss), _ptr(lse), _ptr(status), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(dev)))
+    return loss, lse
+
+
+def flce_bwd(hidden, weight, labels, lse, bias=None, *, ignore_index: int = -100,
+             chunk_size: int = 1024, num_label_tokens: int | None = None,
+             accumulate: bool = False, grad_output=None, grad_hidden=True, grad_weight=True,
+             grad_bias=None, status=None, workspace=None):
+    """Fused linear CE backward from :func:`flce_fwd`'s lse (the logits are recomputed).
+    Output arguments as in :func:`flce_fwd_bwd`. Returns (grad_hidden, grad_weight, grad_bias)."""
+    import torch
+    lib = load_library()
+    hidden, weight, labels, bias, dev, n, h, v = _flce_inputs(hidden, weight, labels, bias)
+    _require(lse, "lse", torch.float32, 1, dev)
+    if lse.shape[0] != n or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous [n] float32 tensor")
+    if grad_bias is None:
+        grad_bias = bias is not None
+    flags = FLCE_ACCUMULATE if accumulate else 0
+
+    def out(spec, shape, dtype, name):
+        if spec is True:
+            if accumulate and name != "grad_hidden":
+                raise ValueError(f"accumulate=True needs an existing {name} tensor")
+            return torch.empty(shape, dtype=dtype, device=dev)
+        if spec is False or spec is None:
+            return None
+        _require(spec, name, dtype, len(shape), dev)
+        if tuple(spec.shape) != tuple(shape) or not spec.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {tuple(shape)} {dtype} tensor")
+        return spec
+
+    gh = out(grad_hidden, (n, h), torch.bfloat16, "grad_hidden")
+    gw = out(grad_weight, (v, h), torch.float32, "grad_weight")
+    gb = out(grad_bias, (v,), torch.float32, "grad_bias")
+    if grad_output is not None:
+        _require(grad_output, "grad_output", torch.float32, 0, dev)
+    ws = _workspace(flce_workspace_size(n, h, v, chunk_size, flags), dev, workspace)
+    _check("flce_bwd", lib.flce_bwd(
+        _ptr(hidden), _ptr(weight), _ptr(bias), _ptr(labels), _ptr(lse), n, h, v, ignore_index,
+        chunk_size, _count_arg(num_label_tokens), flags, _ptr(grad_output), _ptr(gh), _ptr(gw),
+        _ptr(gb), _ptr(status), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)))
+    return gh, gw, gb
 
 
 def lce_timing_enable(on: bool = True) -> None:

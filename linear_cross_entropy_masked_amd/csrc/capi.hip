@@ -160,7 +160,52 @@ int flce_fwd_bwd(const uint16_t* hidden, const uint16_t* weight, const float* bi
   if ((rc = check_device()) != LCE_OK) return rc;
   lce::FlceArgs a{hidden, weight, bias, labels, n, h, v, ignore_index, chunk_size,
                   num_label_tokens, flags, grad_output, loss_out, lse_out, grad_hidden,
-                  grad_weight, grad_bias, status_out, workspace};
+                  grad_weight, grad_bias, status_out, workspace, lce::kFwdBwd, nullptr};
+  return lce::flce_run(a, static_cast<hipStream_t>(stream)) == hipSuccess ? LCE_OK : LCE_ERR_HIP;
+}
+
+int flce_fwd(const uint16_t* hidden, const uint16_t* weight, const float* bias,
+             const int32_t* labels, int64_t n, int64_t h, int64_t v, int32_t ignore_index,
+             int64_t chunk_size, int64_t num_label_tokens, float* loss_out, float* lse_out,
+             int32_t* status_out, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = lce::flce_check_shape(n, h, v, chunk_size, 0);
+  if (rc != LCE_OK) return rc;
+  if (!loss_out || !weight || (n > 0 && (!hidden || !labels || !lse_out))) return LCE_ERR_NULL_ARG;
+  if (!workspace || workspace_bytes < lce::flce_workspace_bytes(n, h, v, chunk_size, 0))
+    return LCE_ERR_WORKSPACE;
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(bias, 4) || !aligned(labels, 4) ||
+      !aligned(loss_out, 4) || !aligned(lse_out, 4) || !aligned(status_out, 4) ||
+      !aligned(workspace, 256))
+    return LCE_ERR_ALIGNMENT;
+  if ((rc = check_device()) != LCE_OK) return rc;
+  lce::FlceArgs a{hidden, weight, bias, labels, n, h, v, ignore_index, chunk_size,
+                  num_label_tokens, 0, nullptr, loss_out, lse_out, nullptr, nullptr, nullptr,
+                  status_out, workspace, lce::kFwdOnly, nullptr};
+  return lce::flce_run(a, static_cast<hipStream_t>(stream)) == hipSuccess ? LCE_OK : LCE_ERR_HIP;
+}
+
+int flce_bwd(const uint16_t* hidden, const uint16_t* weight, const float* bias,
+             const int32_t* labels, const float* lse, int64_t n, int64_t h, int64_t v,
+             int32_t ignore_index, int64_t chunk_size, int64_t num_label_tokens, uint32_t flags,
+             const float* grad_output, uint16_t* grad_hidden, float* grad_weight,
+             float* grad_bias, int32_t* status_out, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  if (flags & FLCE_RECOMPUTE) return LCE_ERR_BAD_FLAGS;  // the backward always recomputes
+  int rc = lce::flce_check_shape(n, h, v, chunk_size, flags);
+  if (rc != LCE_OK) return rc;
+  if (!weight || (n > 0 && (!hidden || !labels || !lse)) || (grad_bias && !bias))
+    return LCE_ERR_NULL_ARG;
+  if (!workspace || workspace_bytes < lce::flce_workspace_bytes(n, h, v, chunk_size, flags))
+    return LCE_ERR_WORKSPACE;
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(bias, 4) || !aligned(labels, 4) ||
+      !aligned(lse, 4) || !aligned(grad_output, 4) || !aligned(grad_hidden, 16) ||
+      !aligned(grad_weight, 16) || !aligned(grad_bias, 4) || !aligned(status_out, 4) ||
+      !aligned(workspace, 256))
+    return LCE_ERR_ALIGNMENT;
+  if ((rc = check_device()) != LCE_OK) return rc;
+  lce::FlceArgs a{hidden, weight, bias, labels, n, h, v, ignore_index, chunk_size,
+                  num_label_tokens, flags, grad_output, nullptr, nullptr, grad_hidden,
+                  grad_weight, grad_bias, status_out, workspace, lce::kBwdOnly, lse};
   return lce::flce_run(a, static_cast<hipStream_t>(stream)) == hipSuccess ? LCE_OK : LCE_ERR_HIP;
 }
 

@@ -24,7 +24,10 @@ struct FlceArgs {
   float* grad_bias;
   int32_t* status_out;
   void* workspace;
+  int pass;             // kFwdBwd, kFwdOnly (loss and lse, no gradients) or kBwdOnly
+  const float* lse_in;  // kBwdOnly: the lse kFwdOnly returned
 };
+constexpr int kFwdBwd = 0, kFwdOnly = 1, kBwdOnly = 2;
 
 int flce_check_shape(int64_t n, int64_t h, int64_t v, int64_t chunk_size, uint32_t flags);
 size_t flce_workspace_bytes(int64_t n, int64_t h, int64_t v, int64_t chunk_size, uint32_t flags);

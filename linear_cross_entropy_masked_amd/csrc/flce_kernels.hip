@@ -650,7 +650,11 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
   const bool accumulate = (a.flags & FLCE_ACCUMULATE) != 0;
   // the recomputing schedule needs the pipelined GEMM's epilogue hooks (h % 64 == 0); for other
   // h the flag runs the stored-slice schedule, whose results are the same
-  const bool recompute = (a.flags & FLCE_RECOMPUTE) != 0 && h % Wide::BK == 0;
+  const bool fwd_only = a.pass == kFwdOnly, bwd_only = a.pass == kBwdOnly;
+  // the split exports always take the recomputing passes (the forward keeps no logits; the
+  // backward rebuilds them from the saved lse)
+  const bool recompute =
+      ((a.flags & FLCE_RECOMPUTE) != 0 || fwd_only || bwd_only) && h % Wide::BK == 0;
   hipError_t e;
 
   if ((e = launch_label_prep(a.labels, n, v, a.ignore_index, ws.count, a.status_out, s)) != hipSuccess)
@@ -687,6 +691,8 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     View Bw{a.weight, h, kGroup, v, h};
     const bool fused_lse = h % Wide::BK == 0;
     float* lo = a.lse_out ? a.lse_out + c0 : nullptr;
+    // the chunk's lse: computed here, or given to the backward-only pass
+    float* lse_c = bwd_only ? const_cast<float*>(a.lse_in + c0) : ws.lse_c;
     // grad_bias column sums of the recomputing schedule sit in the slice's free halves: the
     // highest float offset they reach must stay inside the slice (fails only for chunks of a
     // row or two; those take the stored-slice schedule, same results)
@@ -703,16 +709,16 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
       }
 
-      // 2. row logsumexp and loss terms
-      {
+      // 2. row logsumexp and loss terms (the backward-only pass has them already)
+      if (!bwd_only) {
         TimedLaunch t(s, K_FLCE_ROW_LSE);
         if (fused_lse)
           hipLaunchKernelGGL(lse_merge_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0,
                              s, ws.part, ws.tiles, ws.slice, ws.ldz, nullptr, rows, v, lab,
-                             a.ignore_index, ws.lse_c, ws.row_loss + c0, lo);
+                             a.ignore_index, lse_c, ws.row_loss + c0, lo);
         else
           hipLaunchKernelGGL(slice_row_lse_kernel, dim3(unsigned(rows)), dim3(kRowThreads), 0, s,
-                             ws.slice, ws.ldz, v, lab, a.ignore_index, ws.lse_c,
+                             ws.slice, ws.ldz, v, lab, a.ignore_index, lse_c,
                              ws.row_loss + c0, lo);
         if ((e = hipGetLastError()) != hipSuccess) return e;
       }
@@ -721,7 +727,7 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
       if (a.grad_bias) {
         TimedLaunch t(s, K_FLCE_BIAS_GRAD);
         hipLaunchKernelGGL(slice_bias_grad_kernel, dim3(unsigned((v + 255) / 256)), dim3(256), 0,
-                           s, ws.slice, ws.ldz, rows, v, lab, a.ignore_index, ws.lse_c,
+                           s, ws.slice, ws.ldz, rows, v, lab, a.ignore_index, lse_c,
                            a.grad_bias, int(first && !accumulate), ws.count, th, a.grad_output);
         if ((e = hipGetLastError()) != hipSuccess) return e;
       }
@@ -733,31 +739,33 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
         TimedLaunch t(s, K_FLCE_TO_PROBS);
         hipLaunchKernelGGL(slice_to_probs_kernel,
                            dim3(unsigned((groups + 15) / 16), unsigned(rows)), dim3(256), 0, s,
-                           ws.slice, ws.ldz, v, lab, a.ignore_index, ws.lse_c);
+                           ws.slice, ws.ldz, v, lab, a.ignore_index, lse_c);
         if ((e = hipGetLastError()) != hipSuccess) return e;
       }
     } else {
-      // 1'. pass 1: the logits are reduced to per-tile logsumexp pairs and the label logit,
-      //     never stored
-      EpiLseOnly e1{a.bias, ws.part, ws.tiles, lab, ws.zy};
-      {
-        TimedLaunch t(s, K_FLCE_GEMM_LOGITS);
-        if ((e = gemm::v2::launch<Wide, true, true>(Ah, Bw, rows, v, h, 1, true, e1, s)) !=
-            hipSuccess)
-          return e;
-      }
-      // 2'. row logsumexp and loss terms
-      {
-        TimedLaunch t(s, K_FLCE_ROW_LSE);
-        hipLaunchKernelGGL(lse_merge_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s,
-                           ws.part, ws.tiles, nullptr, 0, ws.zy, rows, v, lab, a.ignore_index,
-                           ws.lse_c, ws.row_loss + c0, lo);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+      if (!bwd_only) {
+        // 1'. pass 1: the logits are reduced to per-tile logsumexp pairs and the label logit,
+        //     never stored
+        EpiLseOnly e1{a.bias, ws.part, ws.tiles, lab, ws.zy};
+        {
+          TimedLaunch t(s, K_FLCE_GEMM_LOGITS);
+          if ((e = gemm::v2::launch<Wide, true, true>(Ah, Bw, rows, v, h, 1, true, e1, s)) !=
+              hipSuccess)
+            return e;
+        }
+        // 2'. row logsumexp and loss terms
+        {
+          TimedLaunch t(s, K_FLCE_ROW_LSE);
+          hipLaunchKernelGGL(lse_merge_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0,
+                             s, ws.part, ws.tiles, nullptr, 0, ws.zy, rows, v, lab,
+                             a.ignore_index, lse_c, ws.row_loss + c0, lo);
+          if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
       }
       if (!a.grad_hidden && !a.grad_weight && !a.grad_bias) continue;
       // 3'. pass 2: the logits are recomputed tile by tile and leave as bf16 probabilities in
       //     the slice (and, for grad_bias, as fp32 column sums)
-      EpiProbs e2{reinterpret_cast<uint16_t*>(ws.slice), 2 * ws.ldz, a.bias, ws.lse_c, lab, v,
+      EpiProbs e2{reinterpret_cast<uint16_t*>(ws.slice), 2 * ws.ldz, a.bias, lse_c, lab, v,
                   a.ignore_index, a.grad_bias ? ws.slice : nullptr};
       {
         TimedLaunch t(s, K_FLCE_GEMM_PROBS);
@@ -828,6 +836,7 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
+  if (bwd_only) return hipSuccess;
   return launch_loss_reduce(ws.row_loss, n, ws.count, th, a.loss_out, s);
 }
 

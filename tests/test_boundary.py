@@ -150,3 +150,35 @@ def test_flce_argument_errors(lib):
     assert call(wsb=64) == WORKSPACE
     assert call(hidden=FAKE + 8) == ALIGN
     assert call(gw=FAKE + 4) == ALIGN
+
+
+def test_flce_split_argument_errors(lib):
+    fwd = lib.flce_fwd
+    fa = dict(hidden=FAKE, weight=FAKE, bias=None, labels=FAKE, n=4, h=16, v=10, ign=-100,
+              chunk=2, t=-1, loss=FAKE, lse=FAKE, status=None, ws=FAKE, wsb=1 << 22, stream=None)
+
+    def cf(**kw):
+        return fwd(*dict(fa, **kw).values())
+
+    assert cf(lse=None) == NULL_ARG                  # the backward needs it
+    assert cf(loss=None) == NULL_ARG
+    assert cf(n=0, hidden=None, labels=None, lse=None) != NULL_ARG
+    assert cf(h=12) == BAD_SHAPE
+    assert cf(chunk=0) == BAD_CHUNK
+    assert cf(wsb=64) == WORKSPACE
+    assert cf(lse=FAKE + 2) == ALIGN
+    bwd = lib.flce_bwd
+    ba = dict(hidden=FAKE, weight=FAKE, bias=None, labels=FAKE, lse=FAKE, n=4, h=16, v=10,
+              ign=-100, chunk=2, t=-1, flags=0, gout=None, gh=None, gw=None, gb=None, status=None,
+              ws=FAKE, wsb=1 << 22, stream=None)
+
+    def cb(**kw):
+        return bwd(*dict(ba, **kw).values())
+
+    assert cb(lse=None) == NULL_ARG
+    assert cb(gb=FAKE) == NULL_ARG                   # grad_bias without a bias
+    assert cb(flags=lce.FLCE_RECOMPUTE) == BAD_FLAGS  # implied, not a choice here
+    assert cb(flags=8) == BAD_FLAGS
+    assert cb(h=12) == BAD_SHAPE
+    assert cb(ws=None) == WORKSPACE
+    assert cb(gw=FAKE + 4) == ALIGN

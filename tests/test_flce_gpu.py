@@ -245,3 +245,38 @@ def test_long_context_packed_workload_sampled(dev):
     assert not res["gh"][torch.from_numpy(np.nonzero(~ok)[0]).to(dev)].any().item()
     gw = device_to_f64(res["gw"][torch.from_numpy(wrows).to(dev)])
     assert normwise_rel(gw, ref.grad_weight) <= 1e-4
+
+
+@pytest.mark.parametrize("n,h,v,chunk,bias,accumulate", [
+    (300, 128, 2000, 128, True, False), (257, 64, 513, 100, False, True),
+    (130, 40, 1000, 64, True, False), (1, 64, 1, 1, True, False)])
+def test_split_forward_backward_matches_fused(dev, n, h, v, chunk, bias, accumulate):
+    """flce_fwd (loss, lse) then flce_bwd (from that lse) give the fused call's loss, lse,
+    grad_hidden and grad_weight bit for bit, and the oracle's grad_bias."""
+    inp = random_flce(n, h, v, weight_sigma=0.1, bias=bias, ignore_frac=0.15, seed=2 * n + v)
+    rng = np.random.default_rng(11)
+    init = None
+    if accumulate:
+        init = (rng.normal(0, 0.01, (v, h)), rng.normal(0, 0.01, v))
+    fused = run_flce(dev, inp, chunk, count=n + 5, g=1.5, accumulate_init=init)
+    hid = bits_to_device(inp.hidden, dev)
+    w = bits_to_device(inp.weight, dev)
+    lab = torch.from_numpy(inp.labels.astype(np.int32)).to(dev)
+    b = None if inp.bias is None else torch.from_numpy(inp.bias).to(dev)
+    gout = torch.tensor(1.5, dtype=torch.float32, device=dev)
+    loss, lse = lce.flce_fwd(hid, w, lab, b, chunk_size=chunk, num_label_tokens=n + 5)
+    gw = True
+    gb = None
+    if init is not None:
+        gw = torch.from_numpy(init[0].astype(np.float32)).to(dev)
+        gb = torch.from_numpy(init[1].astype(np.float32)).to(dev) if b is not None else None
+    gh, gw, gb = lce.flce_bwd(hid, w, lab, lse, b, chunk_size=chunk, num_label_tokens=n + 5,
+                              accumulate=init is not None, grad_output=gout, grad_weight=gw,
+                              grad_bias=gb if gb is not None else None)
+    torch.cuda.synchronize()
+    assert float(loss.item()) == fused["loss"]
+    assert np.array_equal(lse.cpu().numpy(), fused["lse"])
+    assert torch.equal(gh, fused["gh"])
+    assert torch.equal(gw, fused["gw"])
+    split = dict(loss=float(loss.item()), gh=gh, gw=gw, gb=gb, lse=lse.cpu().numpy(), status=0)
+    check(inp, split, count=n + 5, g=1.5, init=init)
