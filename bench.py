@@ -386,7 +386,7 @@ def main(argv=None) -> int:
                        fdir, wdir)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         return 2
     if args.steps < 1:
