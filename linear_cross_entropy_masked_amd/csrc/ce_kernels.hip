@@ -19,11 +19,14 @@ namespace lce {
 
 namespace {
 
-// Launch shapes (threads per row, 16-byte loads in flight per lane, non-temporal accesses),
-// chosen by measurement on the [16384, 128256] logits: with 1024 threads per row the forward
-// streams at about 6.0 TB/s and the in-place backward at about 5.7 TB/s (256 threads: 5.8 and
-// 5.1); the backward gains a further 4% from non-temporal loads and stores (each row is
-// touched once).
+// Launch shapes (threads per row, 16-byte loads in flight per lane, cache policy), chosen by
+// measurement on the [16384, 128256] logits. Every pass over a row keeps all of its loads in
+// flight (the last pass predicated) instead of finishing the row one vector per lane at a time.
+// The forward reads with non-temporal loads (about 14% faster than ordinary loads; a plain
+// non-temporal read kernel peaks near 6.8 TB/s on this buffer) and the in-place backward uses
+// non-temporal loads and stores (each row is touched once). The backward walks the rows last
+// to first, so it starts on the rows the forward read last; in that order it runs about 2%
+// faster after the forward. 1024 threads per row beat 256 and 512 in both passes.
 #ifndef LCE_CE_FWD_THREADS
 #define LCE_CE_FWD_THREADS 1024
 #endif
@@ -114,12 +117,16 @@ __device__ __forceinline__ void row_lse_partial(const uint16_t* row, int64_t v, 
     m = mn;
   };
 
-  int64_t j = tid;
-  // main loop: kUnroll full vectors per lane per iteration
-  for (; j + int64_t(kRowThreads) * (kUnroll - 1) < sp.nvec; j += int64_t(kRowThreads) * kUnroll) {
+  // kUnroll vectors per lane per pass; lanes past the row's end read -inf (bf16 0xff80),
+  // which adds nothing to the sum
+  for (int64_t j = tid; j < sp.nvec; j += int64_t(kRowThreads) * kUnroll) {
     uint4 q[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) q[u] = ld16<NT>(&vec[j + int64_t(u) * kRowThreads]);
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t jj = j + int64_t(u) * kRowThreads;
+      q[u] = jj < sp.nvec ? ld16<NT>(&vec[jj])
+                          : uint4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
+    }
     float x[8 * kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -129,12 +136,6 @@ __device__ __forceinline__ void row_lse_partial(const uint16_t* row, int64_t v, 
       x[8 * u + 6] = bf16_lo(q[u].w); x[8 * u + 7] = bf16_hi(q[u].w);
     }
     absorb(x, 8 * kUnroll);
-  }
-  for (; j < sp.nvec; j += kRowThreads) {
-    uint4 q = ld16<NT>(&vec[j]);
-    float x[8] = {bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y),
-                  bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w)};
-    absorb(x, 8);
   }
   if (tid < sp.head) {
     float x = bf16_to_f32(row[tid]);
@@ -198,7 +199,7 @@ __global__ void __launch_bounds__(kRowThreads) ce_fwd_rows_kernel(
   }
   const uint16_t* row = logits + i * ld;
   float m, s;
-  row_lse_partial<kRowThreads, kUnroll, false>(row, v, m, s);
+  row_lse_partial<kRowThreads, kUnroll, true>(row, v, m, s);
   block_lse_reduce<kRowThreads>(m, s);
   if (threadIdx.x == 0) {
     const float lse = m + fast_log2(s) * kLn2;
@@ -235,7 +236,8 @@ __global__ void __launch_bounds__(kRowThreads) ce_bwd_rows_kernel(
     const float* __restrict__ grad_output) {
   // No __restrict__ on logits/grad: in place they are the same memory, and every element is
   // read before the same lane overwrites it.
-  const int64_t i = blockIdx.x;
+  // rows last to first: the forward's last rows are the likeliest to still be cached
+  const int64_t i = int64_t(gridDim.x) - 1 - blockIdx.x;
   const int32_t y = labels[i];
   uint16_t* grow = grad + i * ldg;
   const long long t = count_host >= 0 ? count_host : *count_dev;
@@ -289,18 +291,19 @@ __global__ void __launch_bounds__(kRowThreads) ce_bwd_rows_kernel(
       o.w = pack_bf16x2(coef * p[6], coef * p[7]);
       return o;
     };
-    int64_t j = tid;
-    for (; j + int64_t(kRowThreads) * (kUnroll - 1) < sp.nvec; j += int64_t(kRowThreads) * kUnroll) {
+    for (int64_t j = tid; j < sp.nvec; j += int64_t(kRowThreads) * kUnroll) {
       uint4 q[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) q[u] = ld16<true>(&xv[j + int64_t(u) * kRowThreads]);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int64_t jj = j + int64_t(u) * kRowThreads;
-        st16<true>(&gv[jj], one(q[u], jj));
+        if (jj < sp.nvec) q[u] = ld16<true>(&xv[jj]);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t jj = j + int64_t(u) * kRowThreads;
+        if (jj < sp.nvec) st16<true>(&gv[jj], one(q[u], jj));
       }
     }
-    for (; j < sp.nvec; j += kRowThreads) st16<true>(&gv[j], one(ld16<true>(&xv[j]), j));
     auto scalar = [&](int64_t col) {
       float p = fast_exp2(fmaf(bf16_to_f32(row[col]), kLog2e, -c));
       if (col == y) p -= 1.f;
