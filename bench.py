@@ -9,7 +9,9 @@ synthetic input already resident in HBM:
     [128256, 4096] bf16, no bias, 5% ignored labels, chunk 1024 (loss, grad_hidden, fp32
     grad_weight) — this is `value` (tokens/s), with the bf16 MFMA roofline;
   * chunked masked CE on [16384, 128256] bf16 logits (spiked labels, 5% ignored, chunk 1024,
-    in-place backward) — reported under "ce_only" with its HBM roofline;
+    in-place backward) — reported under "ce_only" with its HBM roofline, as the two calls
+    (forward, then in-place backward) and, under "ce_only.single_pass", as the one call that
+    does both when the upstream gradient is known (each labelled row read once);
   * fused linear CE on the long-context packed workload (hidden [32768, 8192], weight
     [128256, 8192], 8 documents, chunk 2048) with the recomputing schedule — reported under
     "long_context" (at most 3 timed steps; --no-long-context skips it).
@@ -74,6 +76,7 @@ KERNEL_NAMES = [
     ("grad_hidden_reduce_kernel", "flce_grad_hidden_reduce"), ("fill_zero", "fill_zero"),
     ("label_sort_kernel", "flce_label_sort"), ("label_prep_kernel", "label_prep"), ("loss_reduce_kernel", "loss_reduce"),
     ("ce_fwd_rows_kernel", "ce_fwd_rows"), ("ce_bwd_rows_kernel", "ce_bwd_rows"),
+    ("ce_fused_rows_kernel", "ce_fused_rows"),
 ]
 CALIB_BYTES = 1 << 30  # bytes read and bytes written by one launch of the calibration copy
 
@@ -310,6 +313,8 @@ def run_ce(args, torch, lce, workloads):
                 "traffic": stored_traffic("ce_bwd_rows", CE_WORKLOAD)}
     fwd_gbs = fwd_bytes / (fwd_ms * 1e-3) / 1e9
     tot_gbs = (fwd_bytes + bwd_bytes) / (ms * 1e-3) / 1e9
+    single = run_ce_single_pass(args, torch, lce, w, pristine, logits, lab, ws, stream,
+                                bwd_bytes)
     return {
         "workload": w, "ms": ms, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "wall_s": wall,
         "tokens_per_s": w.n / (ms * 1e-3), "gbs": tot_gbs, "fwd_gbs": fwd_gbs,
@@ -318,8 +323,47 @@ def run_ce(args, torch, lce, workloads):
         "instrumented_ms": inst_ms,
         "kernels": {k[0]: {"ms_per_step": round(k[1] / kreps, 4), "launches_per_step": k[2] // kreps}
                     for k in kernels},
-        "inputs": inp, "nvalid": nvalid,
+        "inputs": inp, "nvalid": nvalid, "single": single,
     }
+
+
+def run_ce_single_pass(args, torch, lce, w, pristine, logits, lab, ws, stream, nbytes):
+    """The same CE step as one call (ce_chunked_fwd_bwd_inplace): each labelled row read once
+    and every row written once, so its algorithmic bytes are those of the backward alone."""
+    def step(timed):
+        logits.copy_(pristine)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)] if timed else None
+        if timed:
+            e[0].record(stream)
+        loss, _ = lce.ce_chunked_fwd_bwd_inplace(logits, lab, chunk_size=w.chunk_size,
+                                                 workspace=ws)
+        if timed:
+            e[1].record(stream)
+        return loss, e
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    evs = [step(True)[1] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    kreps, _, kernels = timed_kernels(torch, lce, stream, lambda: step(False), args.steps)
+    kd = {k[0]: k for k in kernels}
+    roof = None
+    if "ce_fused_rows" in kd:
+        k = kd["ce_fused_rows"]
+        avg_ms = k[1] / k[2]
+        achieved = nbytes / (avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "ce_fused_rows", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "avg_launch_ms": round(avg_ms, 4),
+                "traffic": stored_traffic("ce_fused_rows", CE_WORKLOAD)}
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.n / (ms * 1e-3), 1),
+            "GB_per_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": nbytes, "roofline": roof,
+            "kernels": {k[0]: {"ms_per_step": round(k[1] / kreps, 4),
+                               "launches_per_step": k[2] // kreps} for k in kernels}}
 
 
 def blas_threads():
@@ -453,8 +497,8 @@ def main(argv=None) -> int:
     if args.only in (None, "ce"):
         ce = run_ce(args, torch, lce, workloads)
         w = ce["workload"]
-        print(f"# ce {w.name}: {ce['ms']:.3f} ms/step, {ce['gbs']:.0f} GB/s", file=sys.stderr,
-              flush=True)
+        print(f"# ce {w.name}: {ce['ms']:.3f} ms/step, {ce['gbs']:.0f} GB/s; single pass "
+              f"{ce['single']['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
         ce_obj = {
             "workload": w.name, "ms_per_step": round(ce["ms"], 4),
             "fwd_ms": round(ce["fwd_ms"], 4), "bwd_ms": round(ce["bwd_ms"], 4),
@@ -462,7 +506,7 @@ def main(argv=None) -> int:
             "hbm_frac": round(ce["gbs"] / HBM_PEAK_GBS, 4),
             "fwd_GB_per_s": round(ce["fwd_gbs"], 1), "bwd_GB_per_s": round(ce["bwd_gbs"], 1),
             "algorithmic_bytes": ce["algorithmic_bytes"], "roofline": ce["roofline"],
-            "kernels": ce["kernels"], "loss": ce["loss"],
+            "kernels": ce["kernels"], "loss": ce["loss"], "single_pass": ce["single"],
         }
         if fl is None:
             out.update({"value": round(ce["tokens_per_s"], 1), "ms_per_step": round(ce["ms"], 4),

@@ -123,6 +123,27 @@ int ce_chunked_bwd_inplace(uint16_t* logits_inout, int64_t n, int64_t v, int64_t
                            int32_t* status_out, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* Forward and in-place backward in one call, when the upstream gradient g is known at
+ * forward time (NULL grad_output: g = 1). Liger-Kernel issue #533, feature pitch: Liger's
+ * fused linear CE already forms the logits gradient inside its chunked forward and only
+ * applies it in the backward; this is that schedule for the materialised logits of NeMo
+ * Automodel PR #2996 (first and fourth commit messages: the loss and the gradient of
+ * ce_chunked_fwd and ce_chunked_bwd_inplace, written into the logits storage).
+ *   logits_inout  bf16 [n, ld], first v columns; on return the gradient
+ *                 g · s · (softmax − onehot) for labelled rows and exactly 0 for the others.
+ *   loss_out      as ce_chunked_fwd.
+ *   lse_out       fp32 [n] or NULL, as ce_chunked_fwd.
+ * Results are bitwise those of ce_chunked_fwd followed by ce_chunked_bwd_inplace with the
+ * same arguments. Rows with v / 8 <= 16384 (at most 16 aligned 8-element vectors per lane of
+ * a 1024-thread workgroup; v up to 131079) are read once, held in registers and written once;
+ * longer rows take the two passes internally. Workspace: ce_chunked_workspace_size. n == 0 is
+ * valid. */
+int ce_chunked_fwd_bwd_inplace(uint16_t* logits_inout, int64_t n, int64_t v, int64_t ld,
+                               const int32_t* labels, int32_t ignore_index, int64_t chunk_size,
+                               int64_t num_label_tokens, const float* grad_output,
+                               float* loss_out, float* lse_out, int32_t* status_out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------ fused linear CE */
 
 /* Workspace bytes for flce_fwd_bwd: one fp32 [chunk, V] logits slice (rows padded to a

@@ -18,6 +18,7 @@ import os
 __all__ = [
     "LceError", "library_path", "load_library",
     "ce_chunked_workspace_size", "ce_chunked_fwd", "ce_chunked_bwd", "ce_chunked_bwd_inplace",
+    "ce_chunked_fwd_bwd_inplace",
     "flce_workspace_size", "flce_fwd_bwd", "flce_fwd", "flce_bwd", "lce_status_str",
     "FLCE_RECOMPUTE", "FLCE_ACCUMULATE", "LCE_STATUS_BAD_LABEL",
     "lce_timing_enable", "lce_timing_read",
@@ -60,6 +61,8 @@ def load_library() -> ctypes.CDLL:
         "ce_chunked_fwd": (ctypes.c_int, [vp, i64, i64, i64, vp, i32, i64, i64, vp, vp, vp, vp, sz, vp]),
         "ce_chunked_bwd": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, vp, i32, i64, i64, vp, vp, vp, vp, sz, vp]),
         "ce_chunked_bwd_inplace": (ctypes.c_int, [vp, i64, i64, i64, vp, i32, i64, i64, vp, vp, vp, vp, sz, vp]),
+        "ce_chunked_fwd_bwd_inplace": (ctypes.c_int, [vp, i64, i64, i64, vp, i32, i64, i64, vp, vp, vp,
+                                                      vp, vp, sz, vp]),
         "flce_workspace_size": (ctypes.c_int, [i64, i64, i64, i64, u32, psz]),
         "flce_fwd_bwd": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, i64, i32, i64, i64, u32, vp, vp, vp,
                                         vp, vp, vp, vp, vp, sz, vp]),
@@ -229,6 +232,31 @@ def ce_chunked_bwd_inplace(logits, labels, *, ignore_index: int = -100, chunk_si
         _count_arg(num_label_tokens), _ptr(grad_output), _ptr(lse), _ptr(status), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(dev)))
     return logits
+
+
+def ce_chunked_fwd_bwd_inplace(logits, labels, *, ignore_index: int = -100,
+                               chunk_size: int = 1024, num_label_tokens: int | None = None,
+                               grad_output=None, return_lse: bool = False, status=None,
+                               workspace=None):
+    """Forward and in-place backward in one call (the upstream gradient is known now).
+
+    Overwrites ``logits`` with the gradient; returns (loss fp32 0-d tensor, lse fp32 [n] or
+    None). Bitwise equal to ``ce_chunked_fwd`` followed by ``ce_chunked_bwd_inplace``."""
+    import torch
+    lib = load_library()
+    n, v, ld = _logits_2d(logits)
+    dev = logits.device
+    labels = _labels_i32(labels, n, dev)
+    if grad_output is not None:
+        _require(grad_output, "grad_output", torch.float32, 0, dev)
+    ws = _workspace(ce_chunked_workspace_size(n, v, chunk_size), dev, workspace)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    lse = torch.empty(n, dtype=torch.float32, device=dev) if return_lse else None
+    _check("ce_chunked_fwd_bwd_inplace", lib.ce_chunked_fwd_bwd_inplace(
+        _ptr(logits), n, v, ld, _ptr(labels), ignore_index, chunk_size,
+        _count_arg(num_label_tokens), _ptr(grad_output), _ptr(loss), _ptr(lse), _ptr(status),
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)))
+    return loss, lse
 
 
 def flce_fwd_bwd(hidden, weight, labels, bias=None, *, ignore_index: int = -100,

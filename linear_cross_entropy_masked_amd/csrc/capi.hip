@@ -131,6 +131,39 @@ int ce_chunked_bwd_inplace(uint16_t* logits_inout, int64_t n, int64_t v, int64_t
                         workspace_bytes, stream);
 }
 
+int ce_chunked_fwd_bwd_inplace(uint16_t* logits_inout, int64_t n, int64_t v, int64_t ld,
+                               const int32_t* labels, int32_t ignore_index, int64_t chunk_size,
+                               int64_t num_label_tokens, const float* grad_output,
+                               float* loss_out, float* lse_out, int32_t* status_out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = ce_check_shape(n, v, ld, chunk_size);
+  if (rc != LCE_OK) return rc;
+  if (!loss_out || (n > 0 && (!logits_inout || !labels))) return LCE_ERR_NULL_ARG;
+  if (!workspace || workspace_bytes < lce::ce_workspace_bytes(n)) return LCE_ERR_WORKSPACE;
+  if (!aligned(logits_inout, 2) || !aligned(labels, 4) || !aligned(grad_output, 4) ||
+      !aligned(loss_out, 4) || !aligned(lse_out, 4) || !aligned(status_out, 4) ||
+      !aligned(workspace, 256))
+    return LCE_ERR_ALIGNMENT;
+  if ((rc = check_device()) != LCE_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  CeWorkspace ws = lce::ce_workspace_carve(workspace, n);
+  const long long th = num_label_tokens >= 0 ? num_label_tokens : -1;
+  LCE_TRY_HIP(lce::launch_label_prep(labels, n, v, ignore_index, ws.count, status_out, s));
+  if (lce::ce_fused_fits(v)) {
+    LCE_TRY_HIP(lce::launch_ce_fused_rows(logits_inout, n, v, ld, labels, ignore_index, ws.count,
+                                          th, grad_output, ws.row_loss, lse_out, s));
+  } else {
+    // rows too long to hold in registers: the forward pass, then the in-place backward (which
+    // reads each row again, and once more to rebuild its lse when lse_out is NULL)
+    LCE_TRY_HIP(lce::launch_ce_fwd_rows(logits_inout, n, v, ld, labels, ignore_index,
+                                        ws.row_loss, lse_out, s));
+    LCE_TRY_HIP(lce::launch_ce_bwd_rows(logits_inout, ld, logits_inout, ld, n, v, labels,
+                                        ignore_index, lse_out, ws.count, th, grad_output, s));
+  }
+  LCE_TRY_HIP(lce::launch_loss_reduce(ws.row_loss, n, ws.count, th, loss_out, s));
+  return LCE_OK;
+}
+
 int flce_workspace_size(int64_t n, int64_t h, int64_t v, int64_t chunk_size, uint32_t flags,
                         size_t* bytes) {
   if (!bytes) return LCE_ERR_NULL_ARG;

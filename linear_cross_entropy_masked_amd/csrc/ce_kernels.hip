@@ -13,6 +13,12 @@
 // HBM-bound (2 bytes per element read in the forward, 2 read + 2 written in the backward),
 // so the kernels are written around coalesced 16-byte accesses, several loads in flight per
 // lane, and about 7 VALU operations per element (unpack, max, one FMA, exp2, add).
+//
+// No implicit multiply-add contraction in this file (the helpers included below too): every
+// fused multiply-add is an explicit fmaf, so a value is computed by the same operations in
+// every kernel that inlines the same helper, and the one-pass kernel reproduces the two
+// passes bit for bit.
+#pragma clang fp contract(off)
 #include "common.h"
 
 namespace lce {
@@ -96,6 +102,74 @@ __device__ __forceinline__ void block_lse_reduce(float& m, float& s) {
   for (int w = 1; w < kRowThreads / 64; ++w) lse_merge(m, s, sm[w], ss[w]);
 }
 
+// Fold cnt values into a running (m, s) = (max, sum of exp(x - max)) pair; -inf values add
+// nothing.
+__device__ __forceinline__ void lse_absorb(float& m, float& s, const float* x, int cnt) {
+  float mx = x[0];
+  for (int k = 1; k < cnt; ++k) mx = fmaxf(mx, x[k]);
+  const float mn = fmaxf(m, mx);
+  if (mn == -INFINITY) return;
+  const float c = mn * kLog2e;
+  float acc = (m == mn) ? s : s * fast_exp2(fmaf(m, kLog2e, -c));
+  for (int k = 0; k < cnt; ++k) acc += fast_exp2(fmaf(x[k], kLog2e, -c));
+  s = acc;
+  m = mn;
+}
+
+// Element k (0..7) of eight packed bf16, widened to fp32.
+__device__ __forceinline__ float elem8(uint4 q, int k) {
+  const uint32_t w = k < 2 ? q.x : (k < 4 ? q.y : (k < 6 ? q.z : q.w));
+  return (k & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+// lse_absorb over the 8·N bf16 of q[0..N-1] in element order.
+template <int N>
+__device__ __forceinline__ void lse_absorb_vecs(float& m, float& s, const uint4* q) {
+  float mx = elem8(q[0], 0);
+#pragma unroll
+  for (int v = 0; v < N; ++v)
+#pragma unroll
+    for (int k = (v == 0 ? 1 : 0); k < 8; ++k) mx = fmaxf(mx, elem8(q[v], k));
+  const float mn = fmaxf(m, mx);
+  if (mn == -INFINITY) return;
+  const float c = mn * kLog2e;
+  float acc = (m == mn) ? s : s * fast_exp2(fmaf(m, kLog2e, -c));
+#pragma unroll
+  for (int v = 0; v < N; ++v)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc += fast_exp2(fmaf(elem8(q[v], k), kLog2e, -c));
+  s = acc;
+  m = mn;
+}
+
+// Eight bf16 of q unpacked to fp32 into x[0..7].
+__device__ __forceinline__ void unpack8(uint4 q, float* x) {
+  x[0] = bf16_lo(q.x); x[1] = bf16_hi(q.x); x[2] = bf16_lo(q.y); x[3] = bf16_hi(q.y);
+  x[4] = bf16_lo(q.z); x[5] = bf16_hi(q.z); x[6] = bf16_lo(q.w); x[7] = bf16_hi(q.w);
+}
+
+// Gradient of one 8-element vector: coef · (exp(x − lse) − onehot), each rounded to bf16
+// (nearest even). c = lse · log2(e); `off` is the label's position in the vector (none unless
+// 0 <= off < 8).
+__device__ __forceinline__ uint4 grad_vec8(uint4 q, float c, float coef, int64_t off) {
+  float x[8];
+  unpack8(q, x);
+  float p[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) p[k] = fast_exp2(fmaf(x[k], kLog2e, -c));
+  if (off >= 0 && off < 8) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k == off) p[k] -= 1.f;
+  }
+  uint4 o;
+  o.x = pack_bf16x2(coef * p[0], coef * p[1]);
+  o.y = pack_bf16x2(coef * p[2], coef * p[3]);
+  o.z = pack_bf16x2(coef * p[4], coef * p[5]);
+  o.w = pack_bf16x2(coef * p[6], coef * p[7]);
+  return o;
+}
+
 // Per-lane online logsumexp over one row. Returns the lane's (m, s) pair.
 template <int kRowThreads, int kUnroll, bool NT>
 __device__ __forceinline__ void row_lse_partial(const uint16_t* row, int64_t v, float& m_out,
@@ -105,17 +179,7 @@ __device__ __forceinline__ void row_lse_partial(const uint16_t* row, int64_t v, 
   float m = -INFINITY, s = 0.f;
   const int tid = threadIdx.x;
 
-  auto absorb = [&](const float* x, int cnt) {
-    float mx = x[0];
-    for (int k = 1; k < cnt; ++k) mx = fmaxf(mx, x[k]);
-    float mn = fmaxf(m, mx);
-    if (mn == -INFINITY) return;
-    const float c = mn * kLog2e;
-    float acc = (m == mn) ? s : s * fast_exp2(fmaf(m, kLog2e, -c));
-    for (int k = 0; k < cnt; ++k) acc += fast_exp2(fmaf(x[k], kLog2e, -c));
-    s = acc;
-    m = mn;
-  };
+  auto absorb = [&](const float* x, int cnt) { lse_absorb(m, s, x, cnt); };
 
   // kUnroll vectors per lane per pass; lanes past the row's end read -inf (bf16 0xff80),
   // which adds nothing to the sum
@@ -127,15 +191,7 @@ __device__ __forceinline__ void row_lse_partial(const uint16_t* row, int64_t v, 
       q[u] = jj < sp.nvec ? ld16<NT>(&vec[jj])
                           : uint4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
     }
-    float x[8 * kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      x[8 * u + 0] = bf16_lo(q[u].x); x[8 * u + 1] = bf16_hi(q[u].x);
-      x[8 * u + 2] = bf16_lo(q[u].y); x[8 * u + 3] = bf16_hi(q[u].y);
-      x[8 * u + 4] = bf16_lo(q[u].z); x[8 * u + 5] = bf16_hi(q[u].z);
-      x[8 * u + 6] = bf16_lo(q[u].w); x[8 * u + 7] = bf16_hi(q[u].w);
-    }
-    absorb(x, 8 * kUnroll);
+    lse_absorb_vecs<kUnroll>(m, s, q);
   }
   if (tid < sp.head) {
     float x = bf16_to_f32(row[tid]);
@@ -272,25 +328,7 @@ __global__ void __launch_bounds__(kRowThreads) ce_bwd_rows_kernel(
     const uint4* xv = reinterpret_cast<const uint4*>(row + sp.head);
     uint4* gv = reinterpret_cast<uint4*>(grow + sp.head);
     const int64_t ylocal = int64_t(y) - sp.head;  // label position relative to the vector base
-    auto one = [&](uint4 q, int64_t j) -> uint4 {
-      float x[8] = {bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y),
-                    bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w)};
-      float p[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) p[k] = fast_exp2(fmaf(x[k], kLog2e, -c));
-      const int64_t off = ylocal - j * 8;
-      if (off >= 0 && off < 8) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (k == off) p[k] -= 1.f;
-      }
-      uint4 o;
-      o.x = pack_bf16x2(coef * p[0], coef * p[1]);
-      o.y = pack_bf16x2(coef * p[2], coef * p[3]);
-      o.z = pack_bf16x2(coef * p[4], coef * p[5]);
-      o.w = pack_bf16x2(coef * p[6], coef * p[7]);
-      return o;
-    };
+    auto one = [&](uint4 q, int64_t j) -> uint4 { return grad_vec8(q, c, coef, ylocal - j * 8); };
     for (int64_t j = tid; j < sp.nvec; j += int64_t(kRowThreads) * kUnroll) {
       uint4 q[kUnroll];
 #pragma unroll
@@ -318,6 +356,102 @@ __global__ void __launch_bounds__(kRowThreads) ce_bwd_rows_kernel(
       grow[col] = f32_to_bf16(coef * p);
     }
   }
+}
+
+// Forward and in-place backward in one pass: the row stays in registers (kVec 16-byte
+// vectors per lane) from its logsumexp to its gradient, so a labelled row is read once and
+// written once instead of read twice. Each lane folds the same vectors in the same groups of
+// four as the forward kernel, so lse, the loss terms and the gradient are bitwise those of
+// the two passes. Rows of more than kRowThreads · kVec vectors are not handled here (the
+// launcher falls back to the two passes).
+template <int kRowThreads, int kVec>
+__global__ void __launch_bounds__(kRowThreads) ce_fused_rows_kernel(
+    uint16_t* logits, int64_t ld, int64_t v, const int32_t* __restrict__ labels,
+    int32_t ignore_index, const long long* __restrict__ count_dev, long long count_host,
+    const float* __restrict__ grad_output, float* __restrict__ row_loss,
+    float* __restrict__ lse_out) {
+  static_assert(kVec % 4 == 0, "vectors are folded four at a time");
+  const int64_t i = blockIdx.x;
+  const int32_t y = labels[i];
+  uint16_t* row = logits + i * ld;
+  const long long t = count_host >= 0 ? count_host : *count_dev;
+  const RowSplit sp = split_row(row, v);
+  const int tid = threadIdx.x;
+  uint4* vec = reinterpret_cast<uint4*>(row + sp.head);
+  auto zero_row = [&]() {
+    const uint4 z = {0u, 0u, 0u, 0u};
+    for (int64_t j = tid; j < sp.nvec; j += kRowThreads) st16<true>(&vec[j], z);
+    if (tid < sp.head) row[tid] = 0;
+    if (tid < sp.tail) row[sp.head + sp.nvec * 8 + tid] = 0;
+  };
+  if (!row_has_label(y, v, ignore_index)) {  // never read; loss term and lse 0
+    zero_row();
+    if (tid == 0) {
+      row_loss[i] = 0.f;
+      if (lse_out) lse_out[i] = 0.f;
+    }
+    return;
+  }
+  // every element this workgroup writes is read before the barrier in block_lse_reduce
+  uint4 q[kVec];
+#pragma unroll
+  for (int u = 0; u < kVec; ++u) {
+    const int64_t jj = tid + int64_t(u) * kRowThreads;
+    q[u] = jj < sp.nvec ? ld16<true>(&vec[jj])
+                        : uint4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
+  }
+  const float xh = tid < sp.head ? bf16_to_f32(row[tid]) : -INFINITY;
+  const float xt = tid < sp.tail ? bf16_to_f32(row[sp.head + sp.nvec * 8 + tid]) : -INFINITY;
+  const float zy = tid == 0 ? bf16_to_f32(row[y]) : 0.f;
+  float m = -INFINITY, s = 0.f;
+  // one group at a time: the whole row already takes half of the registers, so the scheduler
+  // is not allowed to interleave the groups (or, below, the vectors) and their temporaries
+#pragma unroll
+  for (int u0 = 0; u0 < kVec; u0 += 4) {
+    lse_absorb_vecs<4>(m, s, q + u0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (tid < sp.head) lse_absorb(m, s, &xh, 1);
+  if (tid < sp.tail) lse_absorb(m, s, &xt, 1);
+  block_lse_reduce<kRowThreads>(m, s);
+  const float lse = m + fast_log2(s) * kLn2;
+  if (tid == 0) {
+    row_loss[i] = lse - zy;
+    if (lse_out) lse_out[i] = lse;
+  }
+  if (t <= 0) {  // T == 0: all-zero gradient
+    zero_row();
+    return;
+  }
+  const float g = grad_output ? *grad_output : 1.f;
+  const float coef = float(double(g) / double(t));
+  const float c = lse * kLog2e;
+  const int64_t ylocal = int64_t(y) - sp.head;
+  // the packed row is made opaque here so that the gradient unpacks it again instead of the
+  // compiler keeping the logsumexp pass's fp32 copy of it (twice the registers) alive
+#pragma unroll
+  for (int u = 0; u < kVec; ++u) {
+    u32x4_t w = {q[u].x, q[u].y, q[u].z, q[u].w};
+    asm volatile("" : "+v"(w));
+    q[u] = uint4{w.x, w.y, w.z, w.w};
+  }
+  // the loads' 16 addresses are not kept for the stores (32 VGPRs): the store addresses are
+  // recomputed from a base the compiler cannot match to the earlier ones
+  uint4* vt = vec + tid;
+  asm volatile("" : "+v"(vt));
+#pragma unroll
+  for (int u = 0; u < kVec; ++u) {
+    const int64_t jj = tid + int64_t(u) * kRowThreads;
+    if (jj < sp.nvec) st16<true>(vt + int64_t(u) * kRowThreads, grad_vec8(q[u], c, coef, ylocal - jj * 8));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  auto scalar = [&](int64_t col, float x) {
+    float p = fast_exp2(fmaf(x, kLog2e, -c));
+    if (col == y) p -= 1.f;
+    row[col] = f32_to_bf16(coef * p);
+  };
+  if (tid < sp.head) scalar(tid, xh);
+  if (tid < sp.tail) scalar(sp.head + sp.nvec * 8 + tid, xt);
 }
 
 }  // namespace
@@ -370,6 +504,33 @@ hipError_t launch_ce_bwd_rows(const uint16_t* logits, int64_t ld, uint16_t* grad
                      dim3(kBwdThreads), 0, stream,
                      logits, ld, grad, ldg, v, labels, ignore_index, lse, count_dev, count_host,
                      grad_output);
+  return hipGetLastError();
+}
+
+
+bool ce_fused_fits(int64_t v) { return (v >> 3) <= int64_t(kFwdThreads) * 16; }
+
+hipError_t launch_ce_fused_rows(uint16_t* logits, int64_t n, int64_t v, int64_t ld,
+                                const int32_t* labels, int32_t ignore_index,
+                                const long long* count_dev, long long count_host,
+                                const float* grad_output, float* row_loss, float* lse_out,
+                                hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  if (!ce_fused_fits(v)) return hipErrorInvalidValue;
+  TimedLaunch t(stream, K_CE_FUSED_ROWS);
+  const int64_t nvec_max = v >> 3;  // a row's aligned vectors never exceed v / 8
+  if (nvec_max <= int64_t(kFwdThreads) * 4)
+    hipLaunchKernelGGL((ce_fused_rows_kernel<kFwdThreads, 4>), dim3(unsigned(n)),
+                       dim3(kFwdThreads), 0, stream, logits, ld, v, labels, ignore_index,
+                       count_dev, count_host, grad_output, row_loss, lse_out);
+  else if (nvec_max <= int64_t(kFwdThreads) * 8)
+    hipLaunchKernelGGL((ce_fused_rows_kernel<kFwdThreads, 8>), dim3(unsigned(n)),
+                       dim3(kFwdThreads), 0, stream, logits, ld, v, labels, ignore_index,
+                       count_dev, count_host, grad_output, row_loss, lse_out);
+  else
+    hipLaunchKernelGGL((ce_fused_rows_kernel<kFwdThreads, 16>), dim3(unsigned(n)),
+                       dim3(kFwdThreads), 0, stream, logits, ld, v, labels, ignore_index,
+                       count_dev, count_host, grad_output, row_loss, lse_out);
   return hipGetLastError();
 }
 

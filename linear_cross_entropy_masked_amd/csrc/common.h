@@ -73,6 +73,14 @@ hipError_t launch_ce_fwd_rows(const uint16_t* logits, int64_t n, int64_t v, int6
                               float* lse_out, hipStream_t stream);
 hipError_t launch_loss_reduce(const float* row_loss, int64_t n, const long long* count_dev,
                               long long count_host, float* loss_out, hipStream_t stream);
+// One pass per row (forward and in-place backward); rows up to 16 · 1024 aligned vectors
+// (ce_fused_fits). Returns hipErrorInvalidValue for longer rows without launching.
+bool ce_fused_fits(int64_t v);
+hipError_t launch_ce_fused_rows(uint16_t* logits, int64_t n, int64_t v, int64_t ld,
+                                const int32_t* labels, int32_t ignore_index,
+                                const long long* count_dev, long long count_host,
+                                const float* grad_output, float* row_loss, float* lse_out,
+                                hipStream_t stream);
 hipError_t launch_ce_bwd_rows(const uint16_t* logits, int64_t ld, uint16_t* grad, int64_t ldg,
                               int64_t n, int64_t v, const int32_t* labels, int32_t ignore_index,
                               const float* lse, const long long* count_dev, long long count_host,
@@ -99,6 +107,7 @@ enum KernelId {
   K_FLCE_GRAD_HIDDEN_REDUCE,
   K_FLCE_GEMM_PROBS,
   K_FLCE_LABEL_SORT,
+  K_CE_FUSED_ROWS,
   K_COUNT
 };
 

@@ -98,6 +98,29 @@ def test_ce_bwd_argument_errors(lib):
     assert g(FAKE, 4, 8, 8, FAKE, -100, 2, -1, None, None, None, FAKE, 8, None) == WORKSPACE
 
 
+def _fused(n=4, v=8, ld=8, logits=FAKE, labels=FAKE, chunk=2, gout=None, loss=FAKE, lse=None,
+           ws=FAKE, wsb=1 << 20):
+    return lce.load_library().ce_chunked_fwd_bwd_inplace(logits, n, v, ld, labels, -100, chunk,
+                                                         -1, gout, loss, lse, None, ws, wsb,
+                                                         None)
+
+
+def test_ce_fused_argument_errors(lib):
+    assert _fused(n=-1) == BAD_SHAPE
+    assert _fused(v=0) == BAD_SHAPE
+    assert _fused(ld=7) == BAD_SHAPE
+    assert _fused(chunk=0) == BAD_CHUNK
+    assert _fused(logits=None) == NULL_ARG
+    assert _fused(labels=None) == NULL_ARG
+    assert _fused(loss=None) == NULL_ARG
+    assert _fused(n=0, logits=None, labels=None) != NULL_ARG  # n == 0 needs no rows
+    assert _fused(ws=None) == WORKSPACE
+    assert _fused(wsb=16) == WORKSPACE
+    assert _fused(logits=FAKE + 1) == ALIGN
+    assert _fused(gout=FAKE + 2) == ALIGN
+    assert _fused(lse=FAKE + 2) == ALIGN
+
+
 def _fws(n, h, v, c, flags=0):
     out = ctypes.c_size_t()
     rc = lce.load_library().flce_workspace_size(n, h, v, c, flags, ctypes.byref(out))

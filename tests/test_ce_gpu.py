@@ -187,3 +187,95 @@ def test_large_vocab_workload_full_size(dev):
         assert_faithful_bf16(got[k:k + 1], one.grad, what=f"grad row {r}")
         if labels[r] == -100:
             assert not got[k].any()
+
+
+# ---- single pass (ce_chunked_fwd_bwd_inplace) --------------------------------------------
+
+def run_fused(dev, bits, labels, chunk=16, count=None, g=None, ld=None, return_lse=True):
+    n, v = bits.shape
+    if ld is None or ld == v:
+        logits = bits_to_device(bits, dev)
+    else:
+        buf = torch.zeros((n, ld), dtype=torch.bfloat16, device=dev)
+        buf[:, :v] = bits_to_device(bits, dev)
+        logits = buf[:, :v]
+    lab = torch.from_numpy(labels.astype(np.int32)).to(dev)
+    status = torch.full((), -1, dtype=torch.int32, device=dev)
+    gout = None if g is None else torch.tensor(g, dtype=torch.float32, device=dev)
+    loss, lse = lce.ce_chunked_fwd_bwd_inplace(logits, lab, chunk_size=chunk,
+                                               num_label_tokens=count, grad_output=gout,
+                                               return_lse=return_lse, status=status)
+    torch.cuda.synchronize()
+    return loss, lse, logits, int(status.item())
+
+
+def assert_fused_equals_two_pass(dev, bits, labels, chunk=16, count=None, g=None, ld=None):
+    loss_a, lse_a, grad_a, st_a, _ = run_ce(dev, bits, labels, chunk=chunk, count=count, g=g,
+                                            ld=ld)
+    loss_b, lse_b, grad_b, st_b = run_fused(dev, bits, labels, chunk=chunk, count=count, g=g,
+                                            ld=ld)
+    assert st_a == st_b
+    assert np.float32(loss_a).tobytes() == loss_b.cpu().numpy().tobytes()
+    assert np.array_equal(lse_a.view(np.uint32), lse_b.cpu().numpy().view(np.uint32))
+    assert torch.equal(grad_a.view(torch.int16), grad_b.view(torch.int16)), "gradient bits differ"
+    return loss_b, lse_b, grad_b, st_b
+
+
+# rows per lane-vector count: v/8 <= 4096 (4 vectors per lane), <= 8192 (8), <= 16384 (16),
+# and past it (the two passes inside the call); ld_extra shifts each row's alignment
+@pytest.mark.parametrize("n,v,ld_extra", [
+    (1, 1, 0), (3, 7, 0), (64, 1000, 0), (17, 1000, 3), (33, 32777, 0), (5, 32775, 1),
+    (9, 40000, 5), (5, 65543, 0), (7, 70001, 1), (6, 128256, 0), (4, 131079, 0),
+    (3, 131080, 2), (3, 140000, 0)])
+def test_fused_bitwise_equals_two_pass(dev, n, v, ld_extra):
+    inp = random_ce(n, v, sigma=2.5, ignore_frac=0.2, seed=n * 13 + v + ld_extra)
+    assert_fused_equals_two_pass(dev, inp.logits, inp.labels, ld=v + ld_extra)
+
+
+def test_fused_small_workload_vs_oracle(dev):
+    w = WORKLOADS["ce_64x1000"]
+    inp = make_ce_inputs(w, seed=0)
+    loss, lse, grad, status = run_fused(dev, inp.logits, inp.labels, chunk=w.chunk_size)
+    assert status == 0
+    ref = check_against_oracle(inp.logits, inp.labels, float(loss.item()), lse.cpu().numpy(),
+                               grad)
+    assert ref.count == 58
+
+
+def test_fused_zero_count_all_ignored_and_upstream_grad(dev):
+    inp = random_ce(12, 300, seed=21, ignore_frac=0.0)
+    loss, lse, grad, _ = run_fused(dev, inp.logits, inp.labels, count=0)
+    assert float(loss.item()) == 0.0 and not grad.float().abs().sum().item()
+    assert np.all(lse.cpu().numpy() != 0)  # lse still reported for labelled rows
+    labels = np.full_like(inp.labels, -100)
+    loss, lse, grad, _ = run_fused(dev, inp.logits, labels)
+    assert float(loss.item()) == 0.0 and not grad.float().abs().sum().item()
+    assert not lse.cpu().numpy().any()
+    inp = random_ce(70, 2048, seed=22)
+    assert_fused_equals_two_pass(dev, inp.logits, inp.labels, count=1000, g=2.5)
+    loss, lse, grad, _ = run_fused(dev, inp.logits, inp.labels, count=1000, g=2.5)
+    check_against_oracle(inp.logits, inp.labels, float(loss.item()), lse.cpu().numpy(), grad,
+                         count=1000, g=2.5)
+
+
+def test_fused_bad_labels_flagged_and_empty(dev):
+    inp = random_ce(10, 100, seed=23, ignore_frac=0.0)
+    labels = inp.labels.copy()
+    labels[2] = 100
+    labels[5] = -7
+    _, _, _, status = assert_fused_equals_two_pass(dev, inp.logits, labels)
+    assert status & lce.LCE_STATUS_BAD_LABEL
+    empty = torch.empty((0, 50), dtype=torch.bfloat16, device=dev)
+    loss, lse = lce.ce_chunked_fwd_bwd_inplace(
+        empty, torch.empty(0, dtype=torch.int32, device=dev), return_lse=True)
+    assert float(loss.item()) == 0.0 and lse.numel() == 0
+
+
+@pytest.mark.timeout(600)
+def test_fused_large_vocab_workload_full_size(dev):
+    """[16384, 128256], the launch configuration the benchmark times: bitwise the two passes
+    (whose values the full-size two-pass test pins to the oracle)."""
+    w = WORKLOADS["ce_16384x128256"]
+    inp = make_ce_inputs(w, seed=0)
+    _, _, _, status = assert_fused_equals_two_pass(dev, inp.logits, inp.labels, chunk=w.chunk_size)
+    assert status == 0
