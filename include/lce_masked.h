@@ -144,6 +144,23 @@ int ce_chunked_fwd_bwd_inplace(uint16_t* logits_inout, int64_t n, int64_t v, int
                                float* loss_out, float* lse_out, int32_t* status_out,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Unreduced loss (the per-row terms before the sum of NeMo Automodel PR #2996, first commit
+ * message; a framework's reduction="none"). No normaliser T is involved.
+ * ce_rows_fwd: row_loss_out fp32 [n] receives lse_i − z_{i,y_i} for labelled rows and 0 for
+ *   the others; lse_out (fp32 [n] or NULL) as ce_chunked_fwd.
+ * ce_rows_bwd: grad[i, :] = grad_rows[i] · (softmax(z_i) − onehot(y_i)) for labelled rows,
+ *   exactly 0 for the others (grad_rows: fp32 [n], the upstream gradient of each row's term);
+ *   grad == logits with ldg == ld is the in-place case; lse as ce_chunked_bwd.
+ * chunk_size is validated as in ce_chunked_fwd and has no other effect. Workspace:
+ * ce_chunked_workspace_size. n == 0 is valid. */
+int ce_rows_fwd(const uint16_t* logits, int64_t n, int64_t v, int64_t ld, const int32_t* labels,
+                int32_t ignore_index, int64_t chunk_size, float* row_loss_out, float* lse_out,
+                int32_t* status_out, void* workspace, size_t workspace_bytes, void* stream);
+int ce_rows_bwd(const uint16_t* logits, int64_t n, int64_t v, int64_t ld, uint16_t* grad,
+                int64_t ldg, const int32_t* labels, int32_t ignore_index, int64_t chunk_size,
+                const float* grad_rows, const float* lse, int32_t* status_out, void* workspace,
+                size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------ fused linear CE */
 
 /* Workspace bytes for flce_fwd_bwd: one fp32 [chunk, V] logits slice (rows padded to a

@@ -18,7 +18,7 @@ import os
 __all__ = [
     "LceError", "library_path", "load_library",
     "ce_chunked_workspace_size", "ce_chunked_fwd", "ce_chunked_bwd", "ce_chunked_bwd_inplace",
-    "ce_chunked_fwd_bwd_inplace",
+    "ce_chunked_fwd_bwd_inplace", "ce_rows_fwd", "ce_rows_bwd",
     "flce_workspace_size", "flce_fwd_bwd", "flce_fwd", "flce_bwd", "lce_status_str",
     "FLCE_RECOMPUTE", "FLCE_ACCUMULATE", "LCE_STATUS_BAD_LABEL",
     "lce_timing_enable", "lce_timing_read",
@@ -63,6 +63,9 @@ def load_library() -> ctypes.CDLL:
         "ce_chunked_bwd_inplace": (ctypes.c_int, [vp, i64, i64, i64, vp, i32, i64, i64, vp, vp, vp, vp, sz, vp]),
         "ce_chunked_fwd_bwd_inplace": (ctypes.c_int, [vp, i64, i64, i64, vp, i32, i64, i64, vp, vp, vp,
                                                       vp, vp, sz, vp]),
+        "ce_rows_fwd": (ctypes.c_int, [vp, i64, i64, i64, vp, i32, i64, vp, vp, vp, vp, sz, vp]),
+        "ce_rows_bwd": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, vp, i32, i64, vp, vp, vp, vp, sz,
+                                       vp]),
         "flce_workspace_size": (ctypes.c_int, [i64, i64, i64, i64, u32, psz]),
         "flce_fwd_bwd": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, i64, i32, i64, i64, u32, vp, vp, vp,
                                         vp, vp, vp, vp, vp, sz, vp]),
@@ -257,6 +260,57 @@ def ce_chunked_fwd_bwd_inplace(logits, labels, *, ignore_index: int = -100,
         _count_arg(num_label_tokens), _ptr(grad_output), _ptr(loss), _ptr(lse), _ptr(status),
         _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)))
     return loss, lse
+
+
+def ce_rows_fwd(logits, labels, *, ignore_index: int = -100, chunk_size: int = 1024,
+                return_lse: bool = True, status=None, workspace=None):
+    """Unreduced forward. Returns (row_loss fp32 [n], lse fp32 [n] or None); rows without a
+    label get 0."""
+    import torch
+    lib = load_library()
+    n, v, ld = _logits_2d(logits)
+    dev = logits.device
+    labels = _labels_i32(labels, n, dev)
+    ws = _workspace(ce_chunked_workspace_size(n, v, chunk_size), dev, workspace)
+    rows = torch.empty(n, dtype=torch.float32, device=dev)
+    lse = torch.empty(n, dtype=torch.float32, device=dev) if return_lse else None
+    _check("ce_rows_fwd", lib.ce_rows_fwd(
+        _ptr(logits), n, v, ld, _ptr(labels), ignore_index, chunk_size, _ptr(rows), _ptr(lse),
+        _ptr(status), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)))
+    return rows, lse
+
+
+def ce_rows_bwd(logits, labels, grad_rows, *, out=None, inplace: bool = False,
+                ignore_index: int = -100, chunk_size: int = 1024, lse=None, status=None,
+                workspace=None):
+    """Unreduced backward: row i of the result is grad_rows[i] · (softmax − onehot). With
+    ``inplace`` the gradient overwrites ``logits``; otherwise it goes to ``out`` (or a new
+    tensor)."""
+    import torch
+    lib = load_library()
+    n, v, ld = _logits_2d(logits)
+    dev = logits.device
+    labels = _labels_i32(labels, n, dev)
+    _require(grad_rows, "grad_rows", torch.float32, 1, dev)
+    if grad_rows.numel() != n or (n > 1 and grad_rows.stride(0) != 1):
+        raise ValueError("grad_rows must be a contiguous fp32 [n] tensor")
+    if lse is not None:
+        _require(lse, "lse", torch.float32, 1, dev)
+    if inplace:
+        out, ldg = logits, ld
+    else:
+        if out is None:
+            out = torch.empty((n, v), dtype=torch.bfloat16, device=dev)
+        _require(out, "out", torch.bfloat16, 2, dev)
+        if tuple(out.shape) != (n, v) or (n > 0 and v > 1 and out.stride(1) != 1):
+            raise ValueError("out must be [n, v] bf16 with contiguous rows")
+        ldg = out.stride(0) if n > 1 else v
+    ws = _workspace(ce_chunked_workspace_size(n, v, chunk_size), dev, workspace)
+    _check("ce_rows_bwd", lib.ce_rows_bwd(
+        _ptr(logits), n, v, ld, _ptr(out), ldg, _ptr(labels), ignore_index, chunk_size,
+        _ptr(grad_rows), _ptr(lse), _ptr(status), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(dev)))
+    return out
 
 
 def flce_fwd_bwd(hidden, weight, labels, bias=None, *, ignore_index: int = -100,

@@ -117,7 +117,7 @@ int ce_chunked_bwd(const uint16_t* logits, int64_t n, int64_t v, int64_t ld, uin
   LCE_TRY_HIP(lce::launch_label_prep(labels, n, v, ignore_index, ws.count, status_out, s));
   LCE_TRY_HIP(lce::launch_ce_bwd_rows(logits, ld, grad, ldg, n, v, labels, ignore_index, lse,
                                       ws.count, num_label_tokens >= 0 ? num_label_tokens : -1,
-                                      grad_output, s));
+                                      grad_output, nullptr, s));
   return LCE_OK;
 }
 
@@ -158,9 +158,50 @@ int ce_chunked_fwd_bwd_inplace(uint16_t* logits_inout, int64_t n, int64_t v, int
     LCE_TRY_HIP(lce::launch_ce_fwd_rows(logits_inout, n, v, ld, labels, ignore_index,
                                         ws.row_loss, lse_out, s));
     LCE_TRY_HIP(lce::launch_ce_bwd_rows(logits_inout, ld, logits_inout, ld, n, v, labels,
-                                        ignore_index, lse_out, ws.count, th, grad_output, s));
+                                        ignore_index, lse_out, ws.count, th, grad_output,
+                                        nullptr, s));
   }
   LCE_TRY_HIP(lce::launch_loss_reduce(ws.row_loss, n, ws.count, th, loss_out, s));
+  return LCE_OK;
+}
+
+int ce_rows_fwd(const uint16_t* logits, int64_t n, int64_t v, int64_t ld, const int32_t* labels,
+                int32_t ignore_index, int64_t chunk_size, float* row_loss_out, float* lse_out,
+                int32_t* status_out, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = ce_check_shape(n, v, ld, chunk_size);
+  if (rc != LCE_OK) return rc;
+  if (n > 0 && (!logits || !labels || !row_loss_out)) return LCE_ERR_NULL_ARG;
+  if (!workspace || workspace_bytes < lce::ce_workspace_bytes(n)) return LCE_ERR_WORKSPACE;
+  if (!aligned(logits, 2) || !aligned(labels, 4) || !aligned(row_loss_out, 4) ||
+      !aligned(lse_out, 4) || !aligned(status_out, 4) || !aligned(workspace, 256))
+    return LCE_ERR_ALIGNMENT;
+  if ((rc = check_device()) != LCE_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  CeWorkspace ws = lce::ce_workspace_carve(workspace, n);
+  LCE_TRY_HIP(lce::launch_label_prep(labels, n, v, ignore_index, ws.count, status_out, s));
+  LCE_TRY_HIP(lce::launch_ce_fwd_rows(logits, n, v, ld, labels, ignore_index, row_loss_out,
+                                      lse_out, s));
+  return LCE_OK;
+}
+
+int ce_rows_bwd(const uint16_t* logits, int64_t n, int64_t v, int64_t ld, uint16_t* grad,
+                int64_t ldg, const int32_t* labels, int32_t ignore_index, int64_t chunk_size,
+                const float* grad_rows, const float* lse, int32_t* status_out, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  int rc = ce_check_shape(n, v, ld, chunk_size);
+  if (rc != LCE_OK) return rc;
+  if (ldg < v || mul_overflows(n, ldg) || mul_overflows(n * ldg, 2)) return LCE_ERR_BAD_SHAPE;
+  if (n > 0 && (!logits || !grad || !labels || !grad_rows)) return LCE_ERR_NULL_ARG;
+  if (!workspace || workspace_bytes < lce::ce_workspace_bytes(n)) return LCE_ERR_WORKSPACE;
+  if (!aligned(logits, 2) || !aligned(grad, 2) || !aligned(labels, 4) || !aligned(grad_rows, 4) ||
+      !aligned(lse, 4) || !aligned(status_out, 4) || !aligned(workspace, 256))
+    return LCE_ERR_ALIGNMENT;
+  if ((rc = check_device()) != LCE_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  CeWorkspace ws = lce::ce_workspace_carve(workspace, n);
+  LCE_TRY_HIP(lce::launch_label_prep(labels, n, v, ignore_index, ws.count, status_out, s));
+  LCE_TRY_HIP(lce::launch_ce_bwd_rows(logits, ld, grad, ldg, n, v, labels, ignore_index, lse,
+                                      ws.count, -1, nullptr, grad_rows, s));
   return LCE_OK;
 }
 

@@ -289,9 +289,10 @@ __global__ void __launch_bounds__(kRowThreads) ce_bwd_rows_kernel(
     const uint16_t* logits, int64_t ld, uint16_t* grad, int64_t ldg, int64_t v,
     const int32_t* __restrict__ labels, int32_t ignore_index, const float* __restrict__ lse_in,
     const long long* __restrict__ count_dev, long long count_host,
-    const float* __restrict__ grad_output) {
+    const float* __restrict__ grad_output, const float* __restrict__ grad_rows) {
   // No __restrict__ on logits/grad: in place they are the same memory, and every element is
-  // read before the same lane overwrites it.
+  // read before the same lane overwrites it. grad_rows (unreduced loss): row i's upstream
+  // gradient, used as its coefficient in place of g / T.
   // rows last to first: the forward's last rows are the likeliest to still be cached
   const int64_t i = int64_t(gridDim.x) - 1 - blockIdx.x;
   const int32_t y = labels[i];
@@ -301,7 +302,8 @@ __global__ void __launch_bounds__(kRowThreads) ce_bwd_rows_kernel(
   const RowSplit gs = split_row(grow, v);
   const int tid = threadIdx.x;
 
-  if (!row_has_label(y, v, ignore_index) || t <= 0) {  // zero row (also the T == 0 guard)
+  // zero row (also the T == 0 guard of the reduced loss)
+  if (!row_has_label(y, v, ignore_index) || (!grad_rows && t <= 0)) {
     uint4* gv = reinterpret_cast<uint4*>(grow + gs.head);
     const uint4 z = {0u, 0u, 0u, 0u};
     for (int64_t j = tid; j < gs.nvec; j += kRowThreads) st16<true>(&gv[j], z);
@@ -319,7 +321,7 @@ __global__ void __launch_bounds__(kRowThreads) ce_bwd_rows_kernel(
     block_lse_reduce<kRowThreads>(m, s);
     lse = m + fast_log2(s) * kLn2;
   }
-  const float coef = float(double(g) / double(t));
+  const float coef = grad_rows ? grad_rows[i] : float(double(g) / double(t));
   const float c = lse * kLog2e;
   // The input and output rows share their alignment when ld == ldg (always in place); the
   // vector path needs it, otherwise fall back to scalars.
@@ -497,13 +499,14 @@ hipError_t launch_loss_reduce(const float* row_loss, int64_t n, const long long*
 hipError_t launch_ce_bwd_rows(const uint16_t* logits, int64_t ld, uint16_t* grad, int64_t ldg,
                               int64_t n, int64_t v, const int32_t* labels, int32_t ignore_index,
                               const float* lse, const long long* count_dev, long long count_host,
-                              const float* grad_output, hipStream_t stream) {
+                              const float* grad_output, const float* grad_rows,
+                              hipStream_t stream) {
   if (n == 0) return hipSuccess;
   TimedLaunch t(stream, K_CE_BWD_ROWS);
   hipLaunchKernelGGL((ce_bwd_rows_kernel<kBwdThreads, kBwdUnroll>), dim3(unsigned(n)),
                      dim3(kBwdThreads), 0, stream,
                      logits, ld, grad, ldg, v, labels, ignore_index, lse, count_dev, count_host,
-                     grad_output);
+                     grad_output, grad_rows);
   return hipGetLastError();
 }
 

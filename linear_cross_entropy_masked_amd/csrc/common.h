@@ -84,7 +84,8 @@ hipError_t launch_ce_fused_rows(uint16_t* logits, int64_t n, int64_t v, int64_t 
 hipError_t launch_ce_bwd_rows(const uint16_t* logits, int64_t ld, uint16_t* grad, int64_t ldg,
                               int64_t n, int64_t v, const int32_t* labels, int32_t ignore_index,
                               const float* lse, const long long* count_dev, long long count_host,
-                              const float* grad_output, hipStream_t stream);
+                              const float* grad_output, const float* grad_rows,
+                              hipStream_t stream);
 
 }  // namespace lce
 

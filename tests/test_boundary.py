@@ -121,6 +121,23 @@ def test_ce_fused_argument_errors(lib):
     assert _fused(lse=FAKE + 2) == ALIGN
 
 
+def test_ce_rows_argument_errors(lib):
+    f, b = lib.ce_rows_fwd, lib.ce_rows_bwd
+    assert f(FAKE, 4, 8, 8, FAKE, -100, 2, FAKE, None, None, FAKE, 1 << 20, None) != NULL_ARG
+    assert f(FAKE, 4, 8, 8, FAKE, -100, 2, None, None, None, FAKE, 1 << 20, None) == NULL_ARG
+    assert f(FAKE, 4, 0, 8, FAKE, -100, 2, FAKE, None, None, FAKE, 1 << 20, None) == BAD_SHAPE
+    assert f(FAKE, 4, 8, 8, FAKE, -100, 0, FAKE, None, None, FAKE, 1 << 20, None) == BAD_CHUNK
+    assert f(FAKE, 4, 8, 8, FAKE, -100, 2, FAKE + 2, None, None, FAKE, 1 << 20, None) == ALIGN
+    assert f(FAKE, 4, 8, 8, FAKE, -100, 2, FAKE, None, None, FAKE, 8, None) == WORKSPACE
+    assert b(FAKE, 4, 8, 8, FAKE, 8, FAKE, -100, 2, None, None, None, FAKE, 1 << 20,
+             None) == NULL_ARG  # grad_rows is required
+    assert b(FAKE, 4, 8, 8, FAKE, 7, FAKE, -100, 2, FAKE, None, None, FAKE, 1 << 20,
+             None) == BAD_SHAPE
+    assert b(FAKE, 4, 8, 8, FAKE, 8, FAKE, -100, 2, FAKE + 2, None, None, FAKE, 1 << 20,
+             None) == ALIGN
+    assert b(FAKE, 4, 8, 8, FAKE, 8, FAKE, -100, 2, FAKE, None, None, FAKE, 8, None) == WORKSPACE
+
+
 def _fws(n, h, v, c, flags=0):
     out = ctypes.c_size_t()
     rc = lce.load_library().flce_workspace_size(n, h, v, c, flags, ctypes.byref(out))
