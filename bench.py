@@ -181,6 +181,42 @@ def timed_kernels(torch, lce, stream, step, steps):
     return steps, ev[0].elapsed_time(ev[1]) / steps, kernels
 
 
+def gemm_bytes(kernel, w, chunks, stored_slice=True):
+    """Algorithmic HBM bytes of one launch of an FLCE product (one full chunk of C rows): each
+    operand read once, each result written once. grad_weight adds its fp32 accumulator: written
+    by the first chunk, read and written by the others (averaged over the launches)."""
+    c, h, v = w.chunk_size, w.h, w.v
+    if kernel == "flce_gemm_logits":  # W and the hidden chunk in; fp32 logits out (stored slice)
+        return 2 * v * h + 2 * c * h + (4 * c * v if stored_slice else 0)
+    if kernel == "flce_gemm_probs":  # W and the hidden chunk in; bf16 probabilities out
+        return 2 * v * h + 2 * c * h + 2 * c * v
+    if kernel == "flce_gemm_grad_hidden":  # probabilities and W in; grad_hidden rows out
+        return 2 * c * v + 2 * v * h + 2 * c * h
+    if kernel == "flce_gemm_grad_weight":  # probabilities and hidden in; fp32 accumulator
+        acc = (4 + 8 * (chunks - 1)) * v * h / chunks
+        return 2 * c * v + 2 * c * h + acc
+    raise KeyError(kernel)
+
+
+def gemm_roofline(kernel, flops, nbytes, avg_ms):
+    """Roofline of one product launch: it is bound by whichever floor is higher, flops at the
+    bf16 MFMA peak or algorithmic bytes at the HBM peak; the other figure is kept beside it."""
+    t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    tflops = flops / (avg_ms * 1e-3) / 1e12
+    gbs = nbytes / (avg_ms * 1e-3) / 1e9
+    mfma = {"achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    hbm = {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": int(nbytes)}
+    if t_hbm > t_mfma:
+        roof = {"bound": "hbm", "kernel": kernel, **hbm, "mfma": mfma}
+    else:
+        roof = {"bound": "mfma", "kernel": kernel, **mfma, "hbm": hbm}
+    roof["avg_launch_ms"] = round(avg_ms, 4)
+    return roof
+
+
 def run_flce(args, torch, lce, workloads, name=None, recompute=False, steps=None, warmup=None):
     w = workloads.WORKLOADS[name or FLCE_WORKLOAD]
     steps = args.steps if steps is None else steps
@@ -237,12 +273,9 @@ def run_flce(args, torch, lce, workloads, name=None, recompute=False, steps=None
     roof = None
     if dom:
         avg_ms = dom[1] / dom[2]
-        achieved = per_launch[dom[0]] / (avg_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": dom[0], "achieved": round(achieved, 2),
-                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                "avg_launch_ms": round(avg_ms, 4),
-                "traffic": stored_traffic(dom[0], w.name)}
+        roof = gemm_roofline(dom[0], per_launch[dom[0]],
+                             gemm_bytes(dom[0], w, chunks, stored_slice=not recompute), avg_ms)
+        roof["traffic"] = stored_traffic(dom[0], w.name)
     executed = (8.0 if recompute else 6.0) * w.n * w.h * w.v
     return {
         "workload": w, "ms": ms, "wall_s": wall, "tokens_per_s": w.n / (ms * 1e-3),
