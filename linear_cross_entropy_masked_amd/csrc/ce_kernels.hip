@@ -103,15 +103,17 @@ __device__ __forceinline__ void block_lse_reduce(float& m, float& s) {
 }
 
 // Fold cnt values into a running (m, s) = (max, sum of exp(x - max)) pair; -inf values add
-// nothing.
+// nothing. The shift is taken as (x - max) · log2(e): the difference of two bf16 values is
+// exact in fp32, so the maximum contributes exactly 1 (a one-column row has lse = z exactly
+// and loss 0), where exp2(fma(x, log2 e, -max · log2 e)) would leave the rounding residue of
+// max · log2 e.
 __device__ __forceinline__ void lse_absorb(float& m, float& s, const float* x, int cnt) {
   float mx = x[0];
   for (int k = 1; k < cnt; ++k) mx = fmaxf(mx, x[k]);
   const float mn = fmaxf(m, mx);
   if (mn == -INFINITY) return;
-  const float c = mn * kLog2e;
-  float acc = (m == mn) ? s : s * fast_exp2(fmaf(m, kLog2e, -c));
-  for (int k = 0; k < cnt; ++k) acc += fast_exp2(fmaf(x[k], kLog2e, -c));
+  float acc = (m == mn) ? s : s * fast_exp2((m - mn) * kLog2e);
+  for (int k = 0; k < cnt; ++k) acc += fast_exp2((x[k] - mn) * kLog2e);
   s = acc;
   m = mn;
 }
@@ -132,12 +134,11 @@ __device__ __forceinline__ void lse_absorb_vecs(float& m, float& s, const uint4*
     for (int k = (v == 0 ? 1 : 0); k < 8; ++k) mx = fmaxf(mx, elem8(q[v], k));
   const float mn = fmaxf(m, mx);
   if (mn == -INFINITY) return;
-  const float c = mn * kLog2e;
-  float acc = (m == mn) ? s : s * fast_exp2(fmaf(m, kLog2e, -c));
+  float acc = (m == mn) ? s : s * fast_exp2((m - mn) * kLog2e);
 #pragma unroll
   for (int v = 0; v < N; ++v)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc += fast_exp2(fmaf(elem8(q[v], k), kLog2e, -c));
+    for (int k = 0; k < 8; ++k) acc += fast_exp2((elem8(q[v], k) - mn) * kLog2e);
   s = acc;
   m = mn;
 }
@@ -149,14 +150,19 @@ __device__ __forceinline__ void unpack8(uint4 q, float* x) {
 }
 
 // Gradient of one 8-element vector: coef · (exp(x − lse) − onehot), each rounded to bf16
-// (nearest even). c = lse · log2(e); `off` is the label's position in the vector (none unless
-// 0 <= off < 8).
-__device__ __forceinline__ uint4 grad_vec8(uint4 q, float c, float coef, int64_t off) {
+// (nearest even); `off` is the label's position in the vector (none unless 0 <= off < 8).
+// `others` accumulates the probabilities of the non-label elements, in element order: the
+// label element is rewritten at the end of the row as −coef · (their row sum), exact where
+// p_y − 1 computed in fp32 would cancel (p_y near 1).
+__device__ __forceinline__ uint4 grad_vec8(uint4 q, float lse, float coef, int64_t off,
+                                           float& others) {
   float x[8];
   unpack8(q, x);
   float p[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) p[k] = fast_exp2(fmaf(x[k], kLog2e, -c));
+  for (int k = 0; k < 8; ++k) p[k] = fast_exp2((x[k] - lse) * kLog2e);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) others += (k == off) ? 0.f : p[k];
   if (off >= 0 && off < 8) {
 #pragma unroll
     for (int k = 0; k < 8; ++k)
@@ -168,6 +174,31 @@ __device__ __forceinline__ uint4 grad_vec8(uint4 q, float c, float coef, int64_t
   o.z = pack_bf16x2(coef * p[4], coef * p[5]);
   o.w = pack_bf16x2(coef * p[6], coef * p[7]);
   return o;
+}
+
+// Sum over the workgroup in a fixed order (wavefront butterflies, then the wavefronts in
+// order); every lane gets the same value.
+template <int kRowThreads>
+__device__ __forceinline__ float block_sum(float x) {
+  __shared__ float part[kRowThreads / 64];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float t = part[0];
+#pragma unroll
+  for (int w = 1; w < kRowThreads / 64; ++w) t += part[w];
+  return t;
+}
+
+// The lane that wrote element y of a row split as `sp` and walked by kRowThreads lanes
+// (vector j by lane j mod kRowThreads, head and tail scalars by lane = their index there).
+template <int kRowThreads>
+__device__ __forceinline__ int label_owner(const RowSplit& sp, int64_t y) {
+  if (y < sp.head) return int(y);
+  const int64_t r = y - sp.head;
+  if (r >= sp.nvec * 8) return int(r - sp.nvec * 8);
+  return int((r >> 3) % kRowThreads);
 }
 
 // Per-lane online logsumexp over one row. Returns the lane's (m, s) pair.
@@ -322,15 +353,23 @@ __global__ void __launch_bounds__(kRowThreads) ce_bwd_rows_kernel(
     lse = m + fast_log2(s) * kLn2;
   }
   const float coef = grad_rows ? grad_rows[i] : float(double(g) / double(t));
-  const float c = lse * kLog2e;
+  float others = 0.f;  // this lane's probabilities of the non-label elements
+  int owner;           // the lane that writes the label element
   // The input and output rows share their alignment when ld == ldg (always in place); the
   // vector path needs it, otherwise fall back to scalars.
   const RowSplit sp = split_row(row, v);
+  auto scalar_p = [&](int64_t col, float x) {
+    const float p = fast_exp2((x - lse) * kLog2e);
+    if (col != y) others += p;
+    return col == y ? p - 1.f : p;
+  };
   if (sp.head == gs.head) {
     const uint4* xv = reinterpret_cast<const uint4*>(row + sp.head);
     uint4* gv = reinterpret_cast<uint4*>(grow + sp.head);
     const int64_t ylocal = int64_t(y) - sp.head;  // label position relative to the vector base
-    auto one = [&](uint4 q, int64_t j) -> uint4 { return grad_vec8(q, c, coef, ylocal - j * 8); };
+    auto one = [&](uint4 q, int64_t j) -> uint4 {
+      return grad_vec8(q, lse, coef, ylocal - j * 8, others);
+    };
     for (int64_t j = tid; j < sp.nvec; j += int64_t(kRowThreads) * kUnroll) {
       uint4 q[kUnroll];
 #pragma unroll
@@ -345,19 +384,20 @@ __global__ void __launch_bounds__(kRowThreads) ce_bwd_rows_kernel(
       }
     }
     auto scalar = [&](int64_t col) {
-      float p = fast_exp2(fmaf(bf16_to_f32(row[col]), kLog2e, -c));
-      if (col == y) p -= 1.f;
-      grow[col] = f32_to_bf16(coef * p);
+      grow[col] = f32_to_bf16(coef * scalar_p(col, bf16_to_f32(row[col])));
     };
     if (tid < sp.head) scalar(tid);
     if (tid < sp.tail) scalar(sp.head + sp.nvec * 8 + tid);
+    owner = label_owner<kRowThreads>(sp, y);
   } else {
-    for (int64_t col = tid; col < v; col += kRowThreads) {
-      float p = fast_exp2(fmaf(bf16_to_f32(row[col]), kLog2e, -c));
-      if (col == y) p -= 1.f;
-      grow[col] = f32_to_bf16(coef * p);
-    }
+    for (int64_t col = tid; col < v; col += kRowThreads)
+      grow[col] = f32_to_bf16(coef * scalar_p(col, bf16_to_f32(row[col])));
+    owner = int(int64_t(y) % kRowThreads);
   }
+  // the label element again, from the other elements: p_y − 1 = −Σ_{v≠y} p_v. The lane that
+  // stored it above stores it again, so this value is the one that stays.
+  const float rest = block_sum<kRowThreads>(others);
+  if (tid == owner) grow[y] = f32_to_bf16(coef * -rest);
 }
 
 // Forward and in-place backward in one pass: the row stays in registers (kVec 16-byte
@@ -427,7 +467,7 @@ __global__ void __launch_bounds__(kRowThreads) ce_fused_rows_kernel(
   }
   const float g = grad_output ? *grad_output : 1.f;
   const float coef = float(double(g) / double(t));
-  const float c = lse * kLog2e;
+  float others = 0.f;  // this lane's probabilities of the non-label elements
   const int64_t ylocal = int64_t(y) - sp.head;
   // the packed row is made opaque here so that the gradient unpacks it again instead of the
   // compiler keeping the logsumexp pass's fp32 copy of it (twice the registers) alive
@@ -444,16 +484,21 @@ __global__ void __launch_bounds__(kRowThreads) ce_fused_rows_kernel(
 #pragma unroll
   for (int u = 0; u < kVec; ++u) {
     const int64_t jj = tid + int64_t(u) * kRowThreads;
-    if (jj < sp.nvec) st16<true>(vt + int64_t(u) * kRowThreads, grad_vec8(q[u], c, coef, ylocal - jj * 8));
+    if (jj < sp.nvec)
+      st16<true>(vt + int64_t(u) * kRowThreads,
+                 grad_vec8(q[u], lse, coef, ylocal - jj * 8, others));
     __builtin_amdgcn_sched_barrier(0);
   }
   auto scalar = [&](int64_t col, float x) {
-    float p = fast_exp2(fmaf(x, kLog2e, -c));
-    if (col == y) p -= 1.f;
-    row[col] = f32_to_bf16(coef * p);
+    const float p = fast_exp2((x - lse) * kLog2e);
+    if (col != y) others += p;
+    row[col] = f32_to_bf16(coef * (col == y ? p - 1.f : p));
   };
   if (tid < sp.head) scalar(tid, xh);
   if (tid < sp.tail) scalar(sp.head + sp.nvec * 8 + tid, xt);
+  // the label element again, from the other elements (as in the two-pass backward)
+  const float rest = block_sum<kRowThreads>(others);
+  if (tid == label_owner<kRowThreads>(sp, y)) row[y] = f32_to_bf16(coef * -rest);
 }
 
 }  // namespace

@@ -142,7 +142,7 @@ struct EpiProbs {
   }
   struct Aux {
     gemm::f32x4_t b;
-    float c;  // lse · log2 e, or NaN for a row without a label
+    float c;  // the row's lse, or NaN for a row without a label
   };
   __device__ __forceinline__ Aux load4(int64_t m, int64_t n) const {
     Aux x;
@@ -152,14 +152,14 @@ struct EpiProbs {
       for (int q = 0; q < 4; ++q)
         if (n + q < v) x.b[q] = bias[n + q];
     }
-    x.c = has_label(labels[m], v, ignore_index) ? lse[m] * kLog2e : __builtin_nanf("");
+    x.c = has_label(labels[m], v, ignore_index) ? lse[m] : __builtin_nanf("");
     return x;
   }
   __device__ __forceinline__ gemm::f32x4_t colvalue4(gemm::f32x4_t a, Aux x) const {
     gemm::f32x4_t r{0.f, 0.f, 0.f, 0.f};
     if (x.c == x.c) {  // labelled row
 #pragma unroll
-      for (int q = 0; q < 4; ++q) r[q] = fast_exp2(fmaf(a[q] + x.b[q], kLog2e, -x.c));
+      for (int q = 0; q < 4; ++q) r[q] = fast_exp2(((a[q] + x.b[q]) - x.c) * kLog2e);
     }
     return r;
   }
@@ -384,9 +384,8 @@ __global__ void __launch_bounds__(kRowThreads) slice_row_lse_kernel(
     float mx = x[0];
     for (int k = 1; k < cnt; ++k) mx = fmaxf(mx, x[k]);
     const float mn = fmaxf(m, mx);
-    const float c = mn * kLog2e;
-    float acc = (m == mn) ? s : s * fast_exp2(fmaf(m, kLog2e, -c));
-    for (int k = 0; k < cnt; ++k) acc += fast_exp2(fmaf(x[k], kLog2e, -c));
+    float acc = (m == mn) ? s : s * fast_exp2((m - mn) * kLog2e);
+    for (int k = 0; k < cnt; ++k) acc += fast_exp2((x[k] - mn) * kLog2e);
     s = acc;
     m = mn;
   };
@@ -520,13 +519,13 @@ __global__ void __launch_bounds__(256) slice_to_probs_kernel(float* z, int64_t l
   float* row = z + i * ldz;
   const int64_t col = g * kGroup + 4 * L;
   const float4 x = *reinterpret_cast<const float4*>(row + col);
-  const float c = ok ? lse_c[i] * kLog2e : 0.f;
+  const float c = ok ? lse_c[i] : 0.f;
   float p[4] = {0.f, 0.f, 0.f, 0.f};
-  if (ok) {
+  if (ok) {  // exp((z − lse)): as the recomputing schedule's probabilities, bit for bit
     const float xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      if (col + k < v) p[k] = fast_exp2(fmaf(xs[k], kLog2e, -c));
+      if (col + k < v) p[k] = fast_exp2((xs[k] - c) * kLog2e);
   }
   uint2 o;
   o.x = pack_bf16x2(p[0], p[1]);

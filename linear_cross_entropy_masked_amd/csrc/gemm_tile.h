@@ -606,11 +606,12 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
           if constexpr (Epi::kRowStats) {
             const f32x4_t z = epi.value4(acc[i0 + di][j], aux[di][j]);
             const float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-            const float mn = fmaxf(rm[i0 + di], mx), c = mn * kLog2e;
+            // shift as (z − max) · log2 e: the maximum contributes exactly 1
+            const float mn = fmaxf(rm[i0 + di], mx);
             float t = rm[i0 + di] == mn ? rs[i0 + di]
-                                        : rs[i0 + di] * fast_exp2(fmaf(rm[i0 + di], kLog2e, -c));
+                                        : rs[i0 + di] * fast_exp2((rm[i0 + di] - mn) * kLog2e);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) t += fast_exp2(fmaf(z[q], kLog2e, -c));
+            for (int q = 0; q < 4; ++q) t += fast_exp2((z[q] - mn) * kLog2e);
             rm[i0 + di] = mn;
             rs[i0 + di] = t;
           }
