@@ -115,6 +115,16 @@ def test_ragged_shapes(dev, n, h, v, chunk, bias):
     check(inp, res)
 
 
+@pytest.mark.parametrize("recompute,h", [(False, 16), (True, 64)])
+def test_chunk_longer_than_label_sort(dev, recompute, h):
+    """A chunk of more rows than the label sort holds in LDS (8192): the one-hot term of
+    grad_weight takes the per-row pass instead of the sorted label runs."""
+    inp = random_flce(9000, h, 50, weight_sigma=0.1, bias=True, ignore_frac=0.1, seed=7)
+    res = run_flce(dev, inp, 9000, recompute=recompute)
+    assert res["status"] == 0
+    check(inp, res)
+
+
 @pytest.mark.parametrize("recompute,h", [(False, 40), (True, 40), (True, 64)])
 def test_accumulate_into_existing_grads(dev, recompute, h):
     inp = random_flce(90, h, 333, bias=True, seed=3)
