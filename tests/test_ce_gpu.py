@@ -108,6 +108,17 @@ def test_out_of_place_leaves_logits_and_matches_in_place(dev):
         logits.view(torch.int16).cpu().numpy().view(np.uint16), inp.logits)
 
 
+@pytest.mark.parametrize("ld_extra", [1, 3])
+def test_out_of_place_with_different_row_alignment(dev, ld_extra):
+    """Logits rows ld = v + odd apart, gradient rows v apart: on the rows whose 16-byte phase
+    differs the backward takes its scalar path (label element included)."""
+    inp = random_ce(33, 1003, sigma=3.0, ignore_frac=0.2, seed=40 + ld_extra)
+    loss, lse, grad, status, _ = run_ce(dev, inp.logits, inp.labels, inplace=False,
+                                        ld=1003 + ld_extra, g=0.75, count=17)
+    assert status == 0
+    check_against_oracle(inp.logits, inp.labels, loss, lse, grad, count=17, g=0.75)
+
+
 def test_recomputed_lse_matches_saved(dev):
     inp = random_ce(50, 4099, sigma=3.0, seed=12)
     _, _, g_saved, _, _ = run_ce(dev, inp.logits, inp.labels, save_lse=True)
