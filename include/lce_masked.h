@@ -74,9 +74,12 @@ extern "C" {
                                        schedule of Liger-Kernel issue #533's comments)           */
 #define FLCE_ACCUMULATE          2u /* add into grad_weight / grad_bias instead of overwriting
                                        (tied embedding and lm_head, Liger-Kernel issue #941)     */
+#define FLCE_ACCUMULATE_GRAD_W   FLCE_ACCUMULATE  /* the same flag, under its other name       */
 
-/* Human-readable name of a return code (static storage; never NULL). */
+/* Human-readable name of a return code (static storage; never NULL). flce_status_str is the
+ * same function under the name the fused layer's callers look for. */
 const char* lce_status_str(int status);
+const char* flce_status_str(int status);
 
 /* ------------------------------------------------------------------ chunked CE */
 

@@ -20,6 +20,7 @@ __all__ = [
     "ce_chunked_workspace_size", "ce_chunked_fwd", "ce_chunked_bwd", "ce_chunked_bwd_inplace",
     "ce_chunked_fwd_bwd_inplace", "ce_rows_fwd", "ce_rows_bwd",
     "flce_workspace_size", "flce_fwd_bwd", "flce_fwd", "flce_bwd", "lce_status_str",
+    "flce_status_str",
     "FLCE_RECOMPUTE", "FLCE_ACCUMULATE", "LCE_STATUS_BAD_LABEL",
     "lce_timing_enable", "lce_timing_read",
 ]
@@ -57,6 +58,7 @@ def load_library() -> ctypes.CDLL:
     psz = ctypes.POINTER(ctypes.c_size_t)
     sigs = {
         "lce_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "flce_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "ce_chunked_workspace_size": (ctypes.c_int, [i64, i64, i64, psz]),
         "ce_chunked_fwd": (ctypes.c_int, [vp, i64, i64, i64, vp, i32, i64, i64, vp, vp, vp, vp, sz, vp]),
         "ce_chunked_bwd": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, vp, i32, i64, i64, vp, vp, vp, vp, sz, vp]),
@@ -89,6 +91,10 @@ def load_library() -> ctypes.CDLL:
 
 def lce_status_str(code: int) -> str:
     return load_library().lce_status_str(int(code)).decode()
+
+
+def flce_status_str(code: int) -> str:
+    return load_library().flce_status_str(int(code)).decode()
 
 
 def _check(fn: str, code: int) -> None:

@@ -216,3 +216,36 @@ class LinearCrossEntropy(torch.nn.Module):
                                     ignore_index=self.ignore_index, chunk_size=self.chunk_size,
                                     num_label_tokens=num_label_tokens, reduction=self.reduction,
                                     weight_grad_buffer=weight_grad_buffer)
+
+
+def ce_chunked(logits, labels, *, mask=None, ignore_index: int = -100, chunk_size: int = 1024,
+               num_label_tokens: int | None = None, inplace_grad: bool = False):
+    """The masked CE loss under the name and defaults of the library's interface: the sum over
+    labelled rows divided by T = num_label_tokens, or by the number of labelled rows (counted
+    on the device) when it is None; gradient out of place unless inplace_grad=True."""
+    if num_label_tokens is None:
+        return masked_cross_entropy(logits, labels, mask=mask, ignore_index=ignore_index,
+                                    chunk_size=chunk_size, reduction="mean",
+                                    inplace_grad=inplace_grad)
+    return masked_cross_entropy(logits, labels, mask=mask, ignore_index=ignore_index,
+                                chunk_size=chunk_size, num_label_tokens=num_label_tokens,
+                                reduction="sum", inplace_grad=inplace_grad)
+
+
+def flce(hidden, weight, labels, bias=None, *, mask=None, ignore_index: int = -100,
+         chunk_size: int = 1024, num_label_tokens: int | None = None, recompute: bool = True,
+         weight_grad_buffer=None):
+    """The fused linear CE loss under the name and defaults of the library's interface (T as in
+    :func:`ce_chunked`). Under autograd the backward always rebuilds the logits from the saved
+    lse (nothing of size [N, V] or [V, H] lives between forward and backward), i.e. the
+    recomputing schedule; ``recompute=False`` (keep the fp32 slice, one logits product fewer)
+    is the fused call ``flce_fwd_bwd`` when the upstream gradient is known, not an autograd
+    schedule, and is refused here."""
+    if not recompute:
+        raise ValueError("flce under autograd always recomputes; call flce_fwd_bwd for the "
+                         "stored-slice schedule")
+    reduction = "mean" if num_label_tokens is None else "sum"
+    return linear_cross_entropy(hidden, weight, labels, bias, mask=mask,
+                                ignore_index=ignore_index, chunk_size=chunk_size,
+                                num_label_tokens=num_label_tokens, reduction=reduction,
+                                weight_grad_buffer=weight_grad_buffer)

@@ -68,6 +68,8 @@ const char* lce_status_str(int status) {
   }
 }
 
+const char* flce_status_str(int status) { return lce_status_str(status); }
+
 int ce_chunked_workspace_size(int64_t n, int64_t v, int64_t chunk_size, size_t* bytes) {
   if (!bytes) return LCE_ERR_NULL_ARG;
   const int rc = ce_check_shape(n, v, v, chunk_size);

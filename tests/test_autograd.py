@@ -49,3 +49,10 @@ def test_normaliser_mapping():
     assert ag._normaliser("sum", None) == 1
     assert ag._normaliser("sum", 37) == 37
     assert ag._normaliser("mean", None) == -1
+
+
+def test_interface_aliases():
+    with pytest.raises(ValueError, match="recomputes"):
+        ag.flce(torch.zeros(4, 8, dtype=torch.bfloat16), torch.zeros(5, 8, dtype=torch.bfloat16),
+                torch.zeros(4, dtype=torch.int64), recompute=False)
+    assert ag.ce_chunked.__name__ == "ce_chunked" and ag.flce.__name__ == "flce"

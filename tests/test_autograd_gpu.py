@@ -195,3 +195,31 @@ def test_linear_ce_fp32_grad_buffer_accumulates(dev):
                       inp.labels, None, num_label_tokens=100, grad_output=3.0)
     got = buf.double().cpu().numpy() - 0.25
     assert np.linalg.norm(got - ref.grad_weight) <= 1e-4 * np.linalg.norm(ref.grad_weight)
+
+
+def test_interface_aliases_vs_oracle(dev):
+    """ce_chunked / flce: the sum over labelled rows divided by num_label_tokens, or by the
+    number of labelled rows when it is not given."""
+    inp = random_ce(45, 777, seed=60)
+    z = leaf(inp.logits, dev)
+    lab = torch.from_numpy(inp.labels).to(dev)
+    loss = ag.ce_chunked(z, lab, chunk_size=16)
+    loss.backward()
+    ref = oracle.ce_masked_sum(oracle.bf16_bits_to_f64(inp.logits), inp.labels)
+    assert_close_rel(float(loss.item()), ref.loss, 1e-5)
+    assert_faithful_bf16(device_to_f64(z.grad), ref.grad)
+    z2 = leaf(inp.logits, dev)
+    loss2 = ag.ce_chunked(z2, lab, num_label_tokens=100, inplace_grad=True)
+    loss2.backward()
+    ref2 = oracle.ce_masked_sum(oracle.bf16_bits_to_f64(inp.logits), inp.labels,
+                                num_label_tokens=100)
+    assert_close_rel(float(loss2.item()), ref2.loss, 1e-5)
+
+    f = random_flce(80, 64, 500, bias=True, seed=61)
+    hid, w, b = _flce_leaves(f, dev)
+    loss3 = ag.flce(hid, w, torch.from_numpy(f.labels).to(dev), b, chunk_size=32)
+    loss3.backward()
+    ref3 = oracle.flce(oracle.bf16_bits_to_f64(f.hidden), oracle.bf16_bits_to_f64(f.weight),
+                       f.labels, f.bias.astype(np.float64))
+    assert_close_rel(float(loss3.item()), ref3.loss, 1e-5)
+    assert np.linalg.norm(device_to_f64(b.grad) - ref3.grad_bias) <= 1e-4 * np.linalg.norm(ref3.grad_bias)
