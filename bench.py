@@ -74,7 +74,9 @@ KERNEL_NAMES = [
     ("slice_row_lse_kernel", "flce_row_lse"), ("slice_bias_grad_kernel", "flce_bias_grad"),
     ("slice_to_probs_kernel", "flce_to_probs"), ("onehot_weight_fix_kernel", "flce_onehot_fix"),
     ("grad_hidden_reduce_kernel", "flce_grad_hidden_reduce"), ("fill_zero", "fill_zero"),
-    ("label_sort_kernel", "flce_label_sort"), ("label_prep_kernel", "label_prep"), ("loss_reduce_kernel", "loss_reduce"),
+    ("label_rank_kernel", "flce_label_sort"), ("label_prep_kernel", "label_prep"),
+    ("loss_finish_kernel", "loss_reduce"), ("loss_accumulate_kernel", "flce_loss_acc"),
+    ("state_move_kernel", "flce_loss_acc"), ("loss_reduce_kernel", "loss_reduce"),
     ("ce_fwd_rows_kernel", "ce_fwd_rows"), ("ce_bwd_rows_kernel", "ce_bwd_rows"),
     ("ce_fused_rows_kernel", "ce_fused_rows"),
 ]
@@ -243,9 +245,15 @@ def run_flce(args, torch, lce, workloads, name=None, recompute=False, steps=None
 
     for _ in range(warmup):
         step()
+    # peak extra memory of one call: its peak allocation above what it leaves behind (the
+    # inputs, the caller's buffers and the outputs it returns), plus the workspace
     torch.cuda.synchronize()
-    mem_before = torch.cuda.memory_allocated(dev)
     torch.cuda.reset_peak_memory_stats(dev)
+    kept = step()
+    torch.cuda.synchronize()
+    peak_extra = (torch.cuda.max_memory_allocated(dev) - torch.cuda.memory_allocated(dev)
+                  + ws.numel())
+    del kept
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -256,7 +264,6 @@ def run_flce(args, torch, lce, workloads, name=None, recompute=False, steps=None
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = ev[0].elapsed_time(ev[1]) / steps
-    peak_extra = torch.cuda.max_memory_allocated(dev) - mem_before + ws.numel()
 
     # per-kernel breakdown: the same K steps again with a hipEvent pair around every launch,
     # recorded by the library on the stream it launches on

@@ -166,10 +166,15 @@ int ce_rows_bwd(const uint16_t* logits, int64_t n, int64_t v, int64_t ld, uint16
 
 /* ------------------------------------------------------------------ fused linear CE */
 
-/* Workspace bytes for flce_fwd_bwd: one fp32 [chunk, V] logits slice (rows padded to a
- * multiple of 64) plus bookkeeping below 1% of it: n per-row loss terms, chunk lse values and
- * one (max, sum) pair per chunk row and 256-column tile of the logits. Host-only; safe
- * without a GPU. */
+/* Workspace bytes for flce_fwd_bwd, flce_fwd and flce_bwd: one fp32 [C, V] logits slice,
+ * C = min(chunk_size, n), rows padded to a multiple of 64 columns. The fp32 working set of
+ * one chunk is that slice (NeMo Automodel PR #2996, Motivation), and with h a multiple of 64
+ * and C >= 64 it is the whole workspace: the call's other state (lse, loss terms, per-tile
+ * (max, sum) pairs, label count, sorted labels) then lives in the halves of the slice that
+ * the bf16 probabilities leave free, or in rows of grad_hidden before the call writes them.
+ * Otherwise a few words per chunk row sit beside the slice (lse, label logit, loss term and
+ * one (max, sum) pair per 256-column tile); nothing grows with n. Host-only; safe without a
+ * GPU. */
 int flce_workspace_size(int64_t n, int64_t h, int64_t v, int64_t chunk_size, uint32_t flags,
                         size_t* bytes);
 
@@ -184,7 +189,10 @@ int flce_workspace_size(int64_t n, int64_t h, int64_t v, int64_t chunk_size, uin
  * where P is the row softmax of z = hidden·weightᵀ + bias and Y the one-hot labels.
  * h must be a multiple of 8 (16-byte rows). Matrix products run on bf16 MFMA with fp32
  * accumulation; the probabilities enter the gradient products as bf16, the one-hot term and
- * the scale g·s are applied in fp32. */
+ * the scale g·s are applied in fp32. The loss adds the rows' terms in row order in fp64, so
+ * it does not depend on chunk_size.
+ * grad_hidden also serves as scratch before its rows are written (see flce_workspace_size):
+ * it must not overlap any input, and its contents are defined only once the call has run. */
 int flce_fwd_bwd(const uint16_t* hidden, const uint16_t* weight, const float* bias,
                  const int32_t* labels, int64_t n, int64_t h, int64_t v, int32_t ignore_index,
                  int64_t chunk_size, int64_t num_label_tokens, uint32_t flags,

@@ -109,6 +109,7 @@ enum KernelId {
   K_FLCE_GEMM_PROBS,
   K_FLCE_LABEL_SORT,
   K_CE_FUSED_ROWS,
+  K_FLCE_LOSS_ACC,
   K_COUNT
 };
 

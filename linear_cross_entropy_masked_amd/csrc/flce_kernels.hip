@@ -84,7 +84,15 @@ struct EpiLogits {
 // of every group is free scratch: flat element e sits at float offset (e / 32) * 64 + 32 +
 // e % 32. It takes grad_hidden's split-K partial sums and the recomputing schedule's
 // probability column sums.
-__device__ __forceinline__ int64_t gap_index(int64_t e) { return (e >> 5) * 64 + 32 + (e & 31); }
+__host__ __device__ __forceinline__ int64_t gap_index(int64_t e) {
+  return (e >> 5) * 64 + 32 + (e & 31);
+}
+
+// Where row i's lse sits: lse[i], or (gap >= 0) flat free-half element gap + i of the slice
+// that lse points at, for a schedule with no other room beside the probabilities.
+__device__ __forceinline__ int64_t lse_off(int64_t gap, int64_t i) {
+  return gap < 0 ? i : gap_index(gap + i);
+}
 
 // Pass 1 of the recomputing schedule: the logits tile is only reduced, never stored. Leaves
 // the per-tile (max, Σ exp) pairs like EpiLogits, and zy[m] = z[m, y_m] for the tile holding
@@ -130,6 +138,7 @@ struct EpiProbs {
   int64_t p_ld;  // elements between rows (2 · ldz)
   const float* bias;
   const float* lse;
+  int64_t lse_gap;  // lse layout (lse_off)
   const int32_t* labels;
   int64_t v;
   int32_t ignore_index;
@@ -152,7 +161,7 @@ struct EpiProbs {
       for (int q = 0; q < 4; ++q)
         if (n + q < v) x.b[q] = bias[n + q];
     }
-    x.c = has_label(labels[m], v, ignore_index) ? lse[m] : __builtin_nanf("");
+    x.c = has_label(labels[m], v, ignore_index) ? lse[lse_off(lse_gap, m)] : __builtin_nanf("");
     return x;
   }
   __device__ __forceinline__ gemm::f32x4_t colvalue4(gemm::f32x4_t a, Aux x) const {
@@ -243,43 +252,51 @@ struct EpiGradWeight {
   }
 };
 
-// Each chunk's rows sorted by label, stably (rows in increasing order within a label):
-// slab[c0 + p] is the chunk's p-th smallest label (rows without a label count as 0x7fffffff
-// and come last) and srow[c0 + p] its row within the chunk. Workgroup b sorts the chunk that
-// starts at row c0 = b · chunk; each row's position is the number of the chunk's rows before
-// it in that order, counted over the labels held in LDS.
+// One chunk's rows sorted by label, stably (rows in increasing order within a label):
+// slab[p] is the chunk's p-th smallest label (rows without a label count as 0x7fffffff and
+// come last) and srow[p] its row. A row's position is the number of the chunk's rows before
+// it in that order. Workgroup b places rows 64 b .. 64 b + 63: its four wavefronts count over
+// one quarter each of the chunk's labels, held in LDS, and the four counts are added.
 constexpr int kSortMax = 8192;
-__global__ void __launch_bounds__(1024) label_sort_kernel(const int32_t* __restrict__ labels_all,
-                                                          int64_t n_all, int64_t chunk, int64_t v,
-                                                          int32_t ignore_index,
-                                                          int32_t* __restrict__ slab_all,
-                                                          int32_t* __restrict__ srow_all) {
+__global__ void __launch_bounds__(256) label_rank_kernel(const int32_t* __restrict__ labels,
+                                                         int64_t rows, int64_t v,
+                                                         int32_t ignore_index,
+                                                         int32_t* __restrict__ slab,
+                                                         int32_t* __restrict__ srow) {
   __shared__ __attribute__((aligned(16))) int32_t k[kSortMax];
-  const int64_t c0 = int64_t(blockIdx.x) * chunk;
-  const int n = int(n_all - c0 < chunk ? n_all - c0 : chunk);
-  const int32_t* labels = labels_all + c0;
-  int32_t* slab = slab_all + c0;
-  int32_t* srow = srow_all + c0;
-  for (int i = threadIdx.x; i < n; i += 1024) {
-    const int32_t y = labels[i];
-    k[i] = has_label(y, v, ignore_index) ? y : 0x7fffffff;
-  }
-  for (int i = n + threadIdx.x; i < ((n + 3) & ~3); i += 1024) k[i] = 0x7fffffff;  // pad to 4
-  __syncthreads();
-  for (int i = threadIdx.x; i < n; i += 1024) {
-    const int32_t x = k[i];
-    int rank = 0;
-    const int n4 = (n + 3) >> 2;
-    for (int j4 = 0; j4 < n4; ++j4) {
-      const int4 q = reinterpret_cast<const int4*>(k)[j4];
-      const int j = 4 * j4;
-      rank += (q.x < x) | ((q.x == x) & (j < i));
-      rank += (q.y < x) | ((q.y == x) & (j + 1 < i));
-      rank += (q.z < x) | ((q.z == x) & (j + 2 < i));
-      rank += (q.w < x) | ((q.w == x) & (j + 3 < i));
+  __shared__ int cnt[4][64];
+  const int n = int(rows);
+  const int n4 = (n + 3) & ~3;  // padded with 0x7fffffff: never before any row
+  for (int i = threadIdx.x; i < n4; i += 256) {
+    int32_t key = 0x7fffffff;
+    if (i < n) {
+      const int32_t y = labels[i];
+      if (has_label(y, v, ignore_index)) key = y;
     }
-    slab[rank] = x;
-    srow[rank] = i;
+    k[i] = key;
+  }
+  __syncthreads();
+  const int r = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int i = int(blockIdx.x) * 64 + r;
+  int rank = 0;
+  if (i < n) {
+    const int32_t x = k[i];
+    const int per = ((n4 >> 2) + 3) & ~3;  // a multiple of 4 with 4 · per >= n4
+    const int lo = q * per, hi = lo + per < n4 ? lo + per : n4;
+    for (int j = lo; j < hi; j += 4) {
+      const int4 c = *reinterpret_cast<const int4*>(k + j);
+      rank += (c.x < x) | ((c.x == x) & (j < i));
+      rank += (c.y < x) | ((c.y == x) & (j + 1 < i));
+      rank += (c.z < x) | ((c.z == x) & (j + 2 < i));
+      rank += (c.w < x) | ((c.w == x) & (j + 3 < i));
+    }
+  }
+  cnt[q][r] = rank;
+  __syncthreads();
+  if (q == 0 && i < n) {
+    const int p = cnt[0][r] + cnt[1][r] + cnt[2][r] + cnt[3][r];
+    slab[p] = k[i];
+    srow[p] = i;
   }
 }
 
@@ -429,19 +446,20 @@ __global__ void __launch_bounds__(kRowThreads) slice_row_lse_kernel(
 
 // lse of each labelled row from the logits GEMM's per-tile (max, Σ exp) pairs, merged in a
 // fixed order; loss term lse − z[y] and lse_out. z[y] comes from zy when given, else from the
-// fp32 slice. One wavefront per row.
+// fp32 slice; the lse goes to lse_c in the layout lse_gap names (lse_off). One wavefront per
+// row.
 __global__ void __launch_bounds__(256) lse_merge_rows_kernel(
     const float2* __restrict__ part, int64_t tiles, const float* __restrict__ z, int64_t ldz,
     const float* __restrict__ zy, int64_t rows, int64_t v, const int32_t* __restrict__ labels,
-    int32_t ignore_index, float* __restrict__ lse_c, float* __restrict__ row_loss,
-    float* __restrict__ lse_out) {
+    int32_t ignore_index, float* __restrict__ lse_c, int64_t lse_gap,
+    float* __restrict__ row_loss, float* __restrict__ lse_out) {
   const int64_t i = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (i >= rows) return;
   const int32_t y = labels[i];
   if (!has_label(y, v, ignore_index)) {
     if (lane == 0) {
-      lse_c[i] = 0.f;
+      lse_c[lse_off(lse_gap, i)] = 0.f;
       row_loss[i] = 0.f;
       if (lse_out) lse_out[i] = 0.f;
     }
@@ -455,7 +473,7 @@ __global__ void __launch_bounds__(256) lse_merge_rows_kernel(
   wave_lse_reduce(m, sum);
   if (lane == 0) {
     const float lse = m + fast_log2(sum) * kLn2;
-    lse_c[i] = lse;
+    lse_c[lse_off(lse_gap, i)] = lse;
     row_loss[i] = lse - (zy ? zy[i] : z[i * ldz + y]);
     if (lse_out) lse_out[i] = lse;
   }
@@ -573,50 +591,137 @@ __global__ void __launch_bounds__(256) onehot_weight_fix_kernel(
   }
 }
 
+// The call's label count (when counted on the device) and its running loss sum.
+struct FlceState {
+  long long count;
+  double sum;
+};
+
+// Adds one chunk's loss terms to the running fp64 sum one at a time, in row order, so the
+// loss is the same sum whatever the chunk size; first = 1 starts the sum. The terms are
+// staged in LDS 4096 at a time; one lane then adds them, its LDS reads issued a few vectors
+// ahead of the dependent additions.
+constexpr int kAccStage = 4096;
+__global__ void __launch_bounds__(256) loss_accumulate_kernel(const float* __restrict__ term,
+                                                              int64_t rows, FlceState* st,
+                                                              int first) {
+  __shared__ __attribute__((aligned(16))) float t[kAccStage];
+  double acc = (first || threadIdx.x != 0) ? 0.0 : st->sum;
+  for (int64_t b = 0; b < rows; b += kAccStage) {
+    const int cnt = rows - b < kAccStage ? int(rows - b) : kAccStage;
+    __syncthreads();
+    for (int i = threadIdx.x; i < cnt; i += 256) t[i] = term[b + i];
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const float4* t4 = reinterpret_cast<const float4*>(t);
+      const int n16 = cnt >> 4;
+      float4 q[4] = {};
+      if (n16 > 0) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) q[u] = t4[u];
+      }
+      for (int k = 0; k < n16; ++k) {
+        float4 nx[4] = {q[0], q[1], q[2], q[3]};
+        if (k + 1 < n16) {  // the next 16 terms load while these are added
+#pragma unroll
+          for (int u = 0; u < 4; ++u) nx[u] = t4[4 * (k + 1) + u];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          acc += double(q[u].x);
+          acc += double(q[u].y);
+          acc += double(q[u].z);
+          acc += double(q[u].w);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) q[u] = nx[u];
+      }
+      for (int i = n16 * 16; i < cnt; ++i) acc += double(t[i]);
+    }
+  }
+  if (threadIdx.x == 0) st->sum = acc;
+}
+
+// loss = Σ terms / T, 0 when T = 0 or there are no rows.
+__global__ void loss_finish_kernel(const FlceState* __restrict__ st, long long count_host,
+                                   int64_t n, float* __restrict__ loss_out) {
+  if (threadIdx.x != 0) return;
+  const long long t = count_host >= 0 ? count_host : st->count;
+  *loss_out = (n > 0 && t > 0) ? float(st->sum / double(t)) : 0.f;
+}
+
+__global__ void state_move_kernel(const FlceState* __restrict__ src, FlceState* __restrict__ dst) {
+  if (threadIdx.x == 0) *dst = *src;
+}
+
 __global__ void fill_zero_f32(float* p, int64_t count) {
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < count;
        i += int64_t(gridDim.x) * blockDim.x)
     p[i] = 0.f;
 }
 
-struct FlceWs {
-  long long* count;
-  float* row_loss;  // [n]
-  float* lse_c;     // [C]
-  float2* part;     // [C, tiles] per-tile (max, Σ exp) of the logits rows
-  int64_t tiles;
-  float* zy;        // [C] label logits (recomputing schedule)
-  int32_t* slab;    // [n] every chunk's labels sorted (one-hot term of dW)
-  int32_t* srow;    // [n] their rows within the chunk
-  float* slice;     // [C, ldz] fp32
-  int64_t ldz;
-};
-
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int64_t lse_tiles(int64_t v) { return (v + Wide::BN - 1) / Wide::BN; }
 int64_t row_tiles(int64_t c) { return (c + Wide::BM - 1) / Wide::BM; }
 
-FlceWs flce_carve(void* base, int64_t n, int64_t v, int64_t chunk) {
+// Free-half elements kept at the end of the slice in the compact layout: the chunk's lse
+// (recomputing schedule), then, in the last 32, the call's FlceState.
+int64_t reserved_gap(int64_t c) { return round_up(c, 32) + 32; }
+
+// Compact layout: the workspace is the fp32 slice [C, ldz] and nothing else. What the call
+// keeps beside the logits lives in memory it owns anyway:
+// - stored-slice schedule: each chunk's tile pairs, lse and loss terms in the chunk's own
+//   grad_hidden rows, which only the chunk's grad_hidden product writes, later; the
+//   FlceState in the last 16 bytes of grad_hidden, moved into the slice's reserved free
+//   halves before the last chunk's rows are written;
+// - recomputing schedule: its first pass never stores logits, so the tile pairs, label
+//   logits and loss terms sit at the start of the slice, the lse and the FlceState in the
+//   reserved free halves, clear of the probabilities and the column sums;
+// - per chunk, the labels sorted for the one-hot term at the start of the slice, once the
+//   probabilities are consumed.
+// It needs the pipelined GEMM's hooks (h a multiple of 64) and a chunk of 64 rows or more.
+// The free halves before the reserved ones take the column sums (row_tiles · v of them) and
+// the grad_hidden split partials; the first pass's scratch must end before them too.
+bool compact_layout(int64_t h, int64_t v, int64_t c) {
+  if (h % Wide::BK != 0 || c < 64) return false;
+  const int64_t usable = c * round_up(v, kGroup) / 2 - reserved_gap(c);
+  return row_tiles(c) * v <= usable && c * (lse_tiles(v) + 1) <= usable;
+}
+
+struct FlceWs {
+  float* slice;  // [C, ldz] fp32
+  int64_t ldz, tiles;
+  bool compact;
+  // extended layout only: bookkeeping beside the slice
+  FlceState* state;
+  float* lse_c;   // [C]
+  float2* part;   // [C, tiles] per-tile (max, Σ exp) of the logits rows
+  float* zy;      // [C] label logits (recomputing schedule)
+  float* term;    // [C] loss terms
+};
+
+FlceWs flce_carve(void* base, int64_t h, int64_t v, int64_t c) {
   char* b = static_cast<char*>(base);
-  FlceWs w;
-  w.count = reinterpret_cast<long long*>(b);
-  size_t off = 256;
-  w.row_loss = reinterpret_cast<float*>(b + off);
-  off += align256(size_t(n) * 4);
-  w.lse_c = reinterpret_cast<float*>(b + off);
-  off += align256(size_t(chunk) * 4);
-  w.tiles = lse_tiles(v);
-  w.part = reinterpret_cast<float2*>(b + off);
-  off += align256(size_t(chunk) * size_t(w.tiles) * 8);
-  w.zy = reinterpret_cast<float*>(b + off);
-  off += align256(size_t(chunk) * 4);
-  w.slab = reinterpret_cast<int32_t*>(b + off);
-  off += align256(size_t(n) * 4);
-  w.srow = reinterpret_cast<int32_t*>(b + off);
-  off += align256(size_t(n) * 4);
-  w.slice = reinterpret_cast<float*>(b + off);
+  FlceWs w{};
   w.ldz = round_up(v, kGroup);
+  w.tiles = lse_tiles(v);
+  w.compact = compact_layout(h, v, c);
+  if (w.compact) {
+    w.slice = reinterpret_cast<float*>(b);
+    return w;
+  }
+  w.state = reinterpret_cast<FlceState*>(b);
+  size_t off = 256;
+  w.lse_c = reinterpret_cast<float*>(b + off);
+  off += align256(size_t(c) * 4);
+  w.part = reinterpret_cast<float2*>(b + off);
+  off += align256(size_t(c) * size_t(w.tiles) * 8);
+  w.zy = reinterpret_cast<float*>(b + off);
+  off += align256(size_t(c) * 4);
+  w.term = reinterpret_cast<float*>(b + off);
+  off += align256(size_t(c) * 4);
+  w.slice = reinterpret_cast<float*>(b + off);
   return w;
 }
 
@@ -632,31 +737,42 @@ int flce_check_shape(int64_t n, int64_t h, int64_t v, int64_t chunk_size, uint32
 }
 
 size_t flce_workspace_bytes(int64_t n, int64_t h, int64_t v, int64_t chunk_size, uint32_t flags) {
-  (void)h;
   (void)flags;
   const int64_t c = chunk_size < n ? chunk_size : (n > 0 ? n : 1);
-  const int64_t ldz = round_up(v, kGroup);
-  return 256 + align256(size_t(n) * 4) + align256(size_t(c) * 4) +
-         align256(size_t(c) * size_t(lse_tiles(v)) * 8) + align256(size_t(c) * 4) +
-         2 * align256(size_t(n) * 4) + align256(size_t(c) * size_t(ldz) * 4);
+  const size_t slice = size_t(c) * size_t(round_up(v, kGroup)) * 4;
+  if (compact_layout(h, v, c)) return slice;
+  return 256 + 3 * align256(size_t(c) * 4) + align256(size_t(c) * size_t(lse_tiles(v)) * 8) +
+         slice;
 }
 
 hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
   const int64_t n = a.n, h = a.h, v = a.v;
   const int64_t chunk = a.chunk_size < n ? a.chunk_size : (n > 0 ? n : 1);
-  FlceWs ws = flce_carve(a.workspace, n, v, chunk);
+  FlceWs ws = flce_carve(a.workspace, h, v, chunk);
   const long long th = a.num_label_tokens >= 0 ? a.num_label_tokens : -1;
   const bool accumulate = (a.flags & FLCE_ACCUMULATE) != 0;
-  // the recomputing schedule needs the pipelined GEMM's epilogue hooks (h % 64 == 0); for other
-  // h the flag runs the stored-slice schedule, whose results are the same
   const bool fwd_only = a.pass == kFwdOnly, bwd_only = a.pass == kBwdOnly;
-  // the split exports always take the recomputing passes (the forward keeps no logits; the
-  // backward rebuilds them from the saved lse)
+  // The split exports always take the recomputing passes (the forward keeps no logits; the
+  // backward rebuilds them from the saved lse). That schedule needs the pipelined GEMM's
+  // epilogue hooks (h % 64 == 0); for other h the stored-slice schedule runs, with the same
+  // results. In the compact layout the stored-slice schedule keeps its bookkeeping in
+  // grad_hidden rows: without grad_hidden, or with fewer than 4 · ⌈v / 256⌉ + 12 hidden
+  // columns to hold it, the recomputing schedule runs instead.
+  const bool want_recompute = (a.flags & FLCE_RECOMPUTE) != 0 || fwd_only || bwd_only;
+  const bool gh_scratch = a.grad_hidden && 2 * h >= 8 * ws.tiles + 24;
   const bool recompute =
-      ((a.flags & FLCE_RECOMPUTE) != 0 || fwd_only || bwd_only) && h % Wide::BK == 0;
+      ws.compact ? (want_recompute || !gh_scratch) : (want_recompute && h % Wide::BK == 0);
+  const int64_t usable_gap = chunk * ws.ldz / 2 - reserved_gap(chunk);  // compact layout
+  FlceState* st_slice =
+      ws.compact ? reinterpret_cast<FlceState*>(ws.slice + gap_index(chunk * ws.ldz / 2 - 32))
+                 : ws.state;
+  FlceState* st = st_slice;  // where the state is now
+  if (ws.compact && !recompute)
+    st = reinterpret_cast<FlceState*>(reinterpret_cast<char*>(a.grad_hidden + n * h) - 16);
   hipError_t e;
 
-  if ((e = launch_label_prep(a.labels, n, v, a.ignore_index, ws.count, a.status_out, s)) != hipSuccess)
+  if ((e = launch_label_prep(a.labels, n, v, a.ignore_index, &st->count, a.status_out, s)) !=
+      hipSuccess)
     return e;
   if (n == 0 && !accumulate) {
     if (a.grad_weight) {
@@ -671,18 +787,9 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     }
   }
 
-  // every chunk's labels sorted into runs up front (one-hot term of dW), when chunks fit LDS
-  const bool sorted_labels = a.grad_weight && n > 0 && chunk <= kSortMax;
-  if (sorted_labels) {
-    TimedLaunch t(s, K_FLCE_LABEL_SORT);
-    hipLaunchKernelGGL(label_sort_kernel, dim3(unsigned((n + chunk - 1) / chunk)), dim3(1024), 0,
-                       s, a.labels, n, chunk, v, a.ignore_index, ws.slab, ws.srow);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-
   for (int64_t c0 = 0; c0 < n; c0 += chunk) {
     const int64_t rows = (n - c0) < chunk ? (n - c0) : chunk;
-    const bool first = c0 == 0;
+    const bool first = c0 == 0, last = c0 + rows >= n;
     const int32_t* lab = a.labels + c0;
     const uint16_t* hid = a.hidden + c0 * h;
 
@@ -690,17 +797,40 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     View Bw{a.weight, h, kGroup, v, h};
     const bool fused_lse = h % Wide::BK == 0;
     float* lo = a.lse_out ? a.lse_out + c0 : nullptr;
-    // the chunk's lse: computed here, or given to the backward-only pass
-    float* lse_c = bwd_only ? const_cast<float*>(a.lse_in + c0) : ws.lse_c;
-    // grad_bias column sums of the recomputing schedule sit in the slice's free halves: the
-    // highest float offset they reach must stay inside the slice (fails only for chunks of a
-    // row or two; those take the stored-slice schedule, same results)
+    // grad_bias column sums of the recomputing schedule sit in the slice's free halves: in the
+    // extended layout the highest float offset they reach must stay inside the slice (fails
+    // only for chunks of a row or two; those take the stored-slice schedule, same results)
     const bool recompute_chunk =
-        recompute && (!a.grad_bias || 2 * row_tiles(rows) * v + 64 <= chunk * ws.ldz);
+        recompute && (ws.compact || !a.grad_bias || 2 * row_tiles(rows) * v + 64 <= chunk * ws.ldz);
+
+    // the chunk's bookkeeping (see compact_layout)
+    float2* part = ws.part;
+    float* lse_c = ws.lse_c;
+    int64_t lse_gap = -1;
+    float* zy = ws.zy;
+    float* term = ws.term;
+    if (ws.compact && !recompute_chunk) {
+      float* scr = reinterpret_cast<float*>(a.grad_hidden + c0 * h);
+      part = reinterpret_cast<float2*>(scr);
+      lse_c = scr + 2 * rows * ws.tiles;
+      term = lse_c + rows;
+      zy = nullptr;
+    } else if (ws.compact) {
+      part = reinterpret_cast<float2*>(ws.slice);
+      zy = ws.slice + 2 * rows * ws.tiles;
+      term = zy + rows;
+      lse_c = ws.slice;
+      lse_gap = usable_gap;
+    }
+    if (bwd_only) {  // the chunk's lse is given
+      lse_c = const_cast<float*>(a.lse_in + c0);
+      lse_gap = -1;
+    }
+
     if (!recompute_chunk) {
       // 1. logits slice (the pipelined GEMM also leaves per-tile logsumexp pairs; the
       //    register-staged one, used when h is not a multiple of 64, does not)
-      EpiLogits el{ws.slice, ws.ldz, a.bias, ws.part, ws.tiles};
+      EpiLogits el{ws.slice, ws.ldz, a.bias, part, ws.tiles};
       {
         TimedLaunch t(s, K_FLCE_GEMM_LOGITS);
         e = fused_lse ? gemm::v2::launch<Wide, true, true>(Ah, Bw, rows, v, h, 1, true, el, s)
@@ -708,17 +838,22 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
       }
 
-      // 2. row logsumexp and loss terms (the backward-only pass has them already)
+      // 2. row logsumexp and loss terms (the backward-only pass has the lse already)
       if (!bwd_only) {
-        TimedLaunch t(s, K_FLCE_ROW_LSE);
-        if (fused_lse)
-          hipLaunchKernelGGL(lse_merge_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0,
-                             s, ws.part, ws.tiles, ws.slice, ws.ldz, nullptr, rows, v, lab,
-                             a.ignore_index, lse_c, ws.row_loss + c0, lo);
-        else
-          hipLaunchKernelGGL(slice_row_lse_kernel, dim3(unsigned(rows)), dim3(kRowThreads), 0, s,
-                             ws.slice, ws.ldz, v, lab, a.ignore_index, lse_c,
-                             ws.row_loss + c0, lo);
+        {
+          TimedLaunch t(s, K_FLCE_ROW_LSE);
+          if (fused_lse)
+            hipLaunchKernelGGL(lse_merge_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256),
+                               0, s, part, ws.tiles, ws.slice, ws.ldz, nullptr, rows, v, lab,
+                               a.ignore_index, lse_c, int64_t(-1), term, lo);
+          else
+            hipLaunchKernelGGL(slice_row_lse_kernel, dim3(unsigned(rows)), dim3(kRowThreads), 0,
+                               s, ws.slice, ws.ldz, v, lab, a.ignore_index, lse_c, term, lo);
+          if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        TimedLaunch t(s, K_FLCE_LOSS_ACC);
+        hipLaunchKernelGGL(loss_accumulate_kernel, dim3(1), dim3(256), 0, s, term, rows, st,
+                           int(first));
         if ((e = hipGetLastError()) != hipSuccess) return e;
       }
 
@@ -727,7 +862,7 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
         TimedLaunch t(s, K_FLCE_BIAS_GRAD);
         hipLaunchKernelGGL(slice_bias_grad_kernel, dim3(unsigned((v + 255) / 256)), dim3(256), 0,
                            s, ws.slice, ws.ldz, rows, v, lab, a.ignore_index, lse_c,
-                           a.grad_bias, int(first && !accumulate), ws.count, th, a.grad_output);
+                           a.grad_bias, int(first && !accumulate), &st->count, th, a.grad_output);
         if ((e = hipGetLastError()) != hipSuccess) return e;
       }
       if (!a.grad_hidden && !a.grad_weight) continue;
@@ -741,11 +876,19 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
                            ws.slice, ws.ldz, v, lab, a.ignore_index, lse_c);
         if ((e = hipGetLastError()) != hipSuccess) return e;
       }
+      // the last chunk's grad_hidden rows are about to be written: the state moves into the
+      // slice's reserved free halves, free now that the slice holds probabilities
+      if (ws.compact && last) {
+        TimedLaunch t(s, K_FLCE_LOSS_ACC);
+        hipLaunchKernelGGL(state_move_kernel, dim3(1), dim3(64), 0, s, st, st_slice);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        st = st_slice;
+      }
     } else {
       if (!bwd_only) {
         // 1'. pass 1: the logits are reduced to per-tile logsumexp pairs and the label logit,
         //     never stored
-        EpiLseOnly e1{a.bias, ws.part, ws.tiles, lab, ws.zy};
+        EpiLseOnly e1{a.bias, part, ws.tiles, lab, zy};
         {
           TimedLaunch t(s, K_FLCE_GEMM_LOGITS);
           if ((e = gemm::v2::launch<Wide, true, true>(Ah, Bw, rows, v, h, 1, true, e1, s)) !=
@@ -756,16 +899,20 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
         {
           TimedLaunch t(s, K_FLCE_ROW_LSE);
           hipLaunchKernelGGL(lse_merge_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0,
-                             s, ws.part, ws.tiles, nullptr, 0, ws.zy, rows, v, lab,
-                             a.ignore_index, lse_c, ws.row_loss + c0, lo);
+                             s, part, ws.tiles, nullptr, 0, zy, rows, v, lab, a.ignore_index,
+                             lse_c, lse_gap, term, lo);
           if ((e = hipGetLastError()) != hipSuccess) return e;
         }
+        TimedLaunch t(s, K_FLCE_LOSS_ACC);
+        hipLaunchKernelGGL(loss_accumulate_kernel, dim3(1), dim3(256), 0, s, term, rows, st,
+                           int(first));
+        if ((e = hipGetLastError()) != hipSuccess) return e;
       }
       if (!a.grad_hidden && !a.grad_weight && !a.grad_bias) continue;
       // 3'. pass 2: the logits are recomputed tile by tile and leave as bf16 probabilities in
       //     the slice (and, for grad_bias, as fp32 column sums)
-      EpiProbs e2{reinterpret_cast<uint16_t*>(ws.slice), 2 * ws.ldz, a.bias, lse_c, lab, v,
-                  a.ignore_index, a.grad_bias ? ws.slice : nullptr};
+      EpiProbs e2{reinterpret_cast<uint16_t*>(ws.slice), 2 * ws.ldz, a.bias, lse_c, lse_gap, lab,
+                  v, a.ignore_index, a.grad_bias ? ws.slice : nullptr};
       {
         TimedLaunch t(s, K_FLCE_GEMM_PROBS);
         if ((e = gemm::v2::launch<Wide, true, true>(Ah, Bw, rows, ws.ldz, h, 1, true, e2, s)) !=
@@ -776,7 +923,7 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
         TimedLaunch t(s, K_FLCE_BIAS_GRAD);
         hipLaunchKernelGGL(bias_from_colsums_kernel, dim3(unsigned((v + 255) / 256)), dim3(256), 0,
                            s, ws.slice, row_tiles(rows), rows, v, lab, a.ignore_index,
-                           a.grad_bias, int(first && !accumulate), ws.count, th, a.grad_output);
+                           a.grad_bias, int(first && !accumulate), &st->count, th, a.grad_output);
         if ((e = hipGetLastError()) != hipSuccess) return e;
       }
       if (!a.grad_hidden && !a.grad_weight) continue;
@@ -785,20 +932,23 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     const int64_t p_ld = 2 * ws.ldz, p_gs = 2 * kGroup;
 
     // 5.-7. gradients. grad_hidden splits K = V so that its few [rows, h] output tiles still
-    // fill the chip; its fp32 partials live in the free half of every slice group.
+    // fill the chip; its fp32 partials live in the free half of every slice group (in the
+    // compact layout, short of the reserved ones).
     View Ap{P, p_ld, p_gs, rows, v};         // P: rows = chunk rows, cols = vocab (K-major)
     View Bw2{a.weight, h, kGroup, v, h};      // W: rows = k (vocab), cols = n (hidden)
     View Bh{hid, h, kGroup, rows, h};         // hidden chunk: rows = k, cols = n
     const int64_t tiles = ((rows + Wide::BM - 1) / Wide::BM) * ((h + Wide::BN - 1) / Wide::BN);
-    const int64_t gap_cap = (rows * ws.ldz / 2) / (rows * h);  // partial sets that fit the gaps
+    const int64_t gap_free = ws.compact ? usable_gap : rows * ws.ldz / 2;
+    const int64_t gap_cap = gap_free / (rows * h);  // partial sets that fit the free halves
     int64_t splits = 256 / tiles;
     if (splits > gap_cap) splits = gap_cap;
     if (splits > (v + 2047) / 2048) splits = (v + 2047) / 2048;  // keep >= 2048 of K per split
     if (splits < 1) splits = 1;
+    const long long* cnt = &st->count;
     EpiGradHidden eh{a.grad_hidden + c0 * h, h, lab, a.weight, h, v, a.ignore_index,
-                     ws.count, th, a.grad_output, 0.f};
+                     cnt, th, a.grad_output, 0.f};
     EpiPartial ep{ws.slice, rows, h, 0};
-    EpiGradWeight ew{a.grad_weight, h, int(first && !accumulate), ws.count, th, a.grad_output, 0.f};
+    EpiGradWeight ew{a.grad_weight, h, int(first && !accumulate), cnt, th, a.grad_output, 0.f};
     if (a.grad_hidden) {
       TimedLaunch t(s, K_FLCE_GEMM_GRAD_HIDDEN);
       e = splits == 1 ? gemm::v2::launch<Wide, true, false>(Ap, Bw2, rows, h, v, 1, true, eh, s)
@@ -815,28 +965,38 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
       TimedLaunch t(s, K_FLCE_GRAD_HIDDEN_REDUCE);
       hipLaunchKernelGGL(grad_hidden_reduce_kernel, dim3(unsigned((rows * h + 255) / 256)),
                          dim3(256), 0, s, ws.slice, rows, h, splits, a.grad_hidden + c0 * h, lab,
-                         a.weight, v, a.ignore_index, ws.count, th, a.grad_output);
+                         a.weight, v, a.ignore_index, cnt, th, a.grad_output);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (a.grad_weight) {
-      // one-hot term of dW: one pass over the chunk's labels sorted into runs (chunks up to
-      // kSortMax rows), else the per-row pass that finds each label's first row by scanning
-      if (sorted_labels) {
+      // one-hot term of dW: the chunk's labels sorted into runs at the start of the slice
+      // (free once both products have read the probabilities), one pass over the runs; chunks
+      // longer than kSortMax take the per-row pass that finds each label's first row
+      if (rows <= kSortMax) {
+        int32_t* slab = reinterpret_cast<int32_t*>(ws.slice);
+        int32_t* srow = slab + rows;
+        {
+          TimedLaunch t(s, K_FLCE_LABEL_SORT);
+          hipLaunchKernelGGL(label_rank_kernel, dim3(unsigned((rows + 63) / 64)), dim3(256), 0, s,
+                             lab, rows, v, a.ignore_index, slab, srow);
+          if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
         TimedLaunch t(s, K_FLCE_ONEHOT_FIX);
         hipLaunchKernelGGL(onehot_segments_kernel, dim3(unsigned(rows)), dim3(256), 0, s, hid, h,
-                           rows, ws.slab + c0, ws.srow + c0, v, a.grad_weight, ws.count, th,
-                           a.grad_output);
+                           rows, slab, srow, v, a.grad_weight, cnt, th, a.grad_output);
       } else {
         TimedLaunch t(s, K_FLCE_ONEHOT_FIX);
         hipLaunchKernelGGL(onehot_weight_fix_kernel, dim3(unsigned(rows)), dim3(256), 0, s, hid,
-                           h, rows, lab, a.ignore_index, v, a.grad_weight, ws.count, th,
+                           h, rows, lab, a.ignore_index, v, a.grad_weight, cnt, th,
                            a.grad_output);
       }
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
   if (bwd_only) return hipSuccess;
-  return launch_loss_reduce(ws.row_loss, n, ws.count, th, a.loss_out, s);
+  TimedLaunch t(s, K_LOSS_REDUCE);
+  hipLaunchKernelGGL(loss_finish_kernel, dim3(1), dim3(64), 0, s, st, th, n, a.loss_out);
+  return hipGetLastError();
 }
 
 }  // namespace lce

@@ -160,24 +160,32 @@ def _fws(n, h, v, c, flags=0):
     return rc, out.value
 
 
-def test_flce_workspace_is_one_slice_plus_bookkeeping(lib):
+def test_flce_workspace_is_one_slice(lib):
     # The fp32 working set of one chunk is chunk * V * 4 bytes. Liger-Kernel issue #941's
     # reply works the same arithmetic for 2 x 1024 rows of V = 32768 fp32 logits: 256 MiB.
-    # Beside the slice the library keeps bookkeeping: 12 bytes per row (loss term, label and
-    # row sorted per chunk) and, per chunk row, below 1% of the slice (lse, label logit, one
-    # (max, sum) pair per 256-column tile).
+    # With h a multiple of 64 and a chunk of at least 64 rows that slice is the whole
+    # workspace, whatever n is and for either schedule.
     rc, b = _fws(2048, 768, 32768, 2048)
     assert rc == OK
     slice_bytes = 2 * 1024 * 32768 * 4
     assert slice_bytes == 256 * 1024 * 1024
-    assert slice_bytes <= b <= slice_bytes * 1.01 + 2048 * 12
-    # chunking bounds it independently of n (apart from the 12 bytes per row)
+    assert b == slice_bytes
     n = 1 << 20
-    rc, b2 = _fws(n, 4096, 128256, 1024)
-    slice2 = 1024 * 128256 * 4
-    assert rc == OK and slice2 <= b2 <= slice2 * 1.01 + n * 12
-    rc, b3 = _fws(8192, 4096, 128256, 1024, lce.FLCE_RECOMPUTE)
-    assert rc == OK
+    for flags in (0, lce.FLCE_RECOMPUTE):
+        rc, b2 = _fws(n, 4096, 128256, 1024, flags)
+        assert rc == OK and b2 == 1024 * 128256 * 4
+        rc, b3 = _fws(32768, 8192, 128256, 2048, flags)
+        assert rc == OK and b3 == 2048 * 128256 * 4
+    # V not a multiple of 64: rows are padded to 64 columns (256-byte groups)
+    rc, b4 = _fws(2048, 768, 32777, 512)
+    assert rc == OK and b4 == 512 * 32832 * 4
+    # Otherwise (h not a multiple of 64, or chunks under 64 rows) a few words per chunk row
+    # sit beside the slice: lse, label logit, loss term and one (max, Σexp) pair per
+    # 256-column tile; nothing grows with n.
+    for h, c in ((4104, 1024), (4096, 32)):
+        rc, b5 = _fws(n, h, 128256, c)
+        s5 = c * 128256 * 4
+        assert rc == OK and s5 < b5 <= s5 + c * (501 * 8 + 12) + 4 * 256
 
 
 def test_flce_argument_errors(lib):

@@ -152,6 +152,38 @@ def test_recompute_matches_stored_slice(dev, n, h, v, chunk, bias):
     assert torch.equal(rec["gw"], std["gw"])
 
 
+@pytest.mark.parametrize("recompute", [False, True])
+def test_one_slice_workspace_and_chunk_independent_loss(dev, recompute):
+    """With h a multiple of 64 and chunks of 64 rows or more the workspace is one fp32
+    [chunk, ldz] slice and nothing else: the bookkeeping sits in the slice's free halves and
+    in grad_hidden rows not yet written. Loss and lse are bitwise the same on either side of
+    that threshold (the loss is summed row by row in fp64), and grad_weight asked for without
+    grad_hidden (which then takes the recomputing passes) is bitwise the one computed with
+    it."""
+    n, h, v = 333, 128, 3001
+    ldz = (v + 63) // 64 * 64
+    flags = lce.FLCE_RECOMPUTE if recompute else 0
+    for c in (64, 100, n):
+        assert lce.flce_workspace_size(n, h, v, c, flags) == c * ldz * 4
+    assert lce.flce_workspace_size(n, h, v, 63, flags) > 63 * ldz * 4
+    inp = random_flce(n, h, v, weight_sigma=0.1, ignore_frac=0.1, seed=61)
+    res = {c: run_flce(dev, inp, c, recompute=recompute) for c in (63, 64, 100, n)}
+    for c, r in res.items():
+        assert r["status"] == 0, c
+        check(inp, r)
+        assert r["loss"] == res[63]["loss"], c
+        assert np.array_equal(r["lse"], res[63]["lse"]), c
+    hid = bits_to_device(inp.hidden, dev)
+    w = bits_to_device(inp.weight, dev)
+    lab = torch.from_numpy(inp.labels.astype(np.int32)).to(dev)
+    loss, gh, gw, _, _ = lce.flce_fwd_bwd(hid, w, lab, chunk_size=100, recompute=recompute,
+                                          grad_hidden=False)
+    torch.cuda.synchronize()
+    assert gh is None
+    assert float(loss.item()) == res[100]["loss"]
+    assert torch.equal(gw, res[100]["gw"])
+
+
 def test_caller_normaliser_and_upstream_grad(dev):
     inp = random_flce(150, 48, 700, bias=True, seed=5)
     res = run_flce(dev, inp, 64, count=999, g=2.5)
