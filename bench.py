@@ -183,21 +183,31 @@ def timed_kernels(torch, lce, stream, step, steps):
     return steps, ev[0].elapsed_time(ev[1]) / steps, kernels
 
 
-def gemm_bytes(kernel, w, chunks, stored_slice=True):
-    """Algorithmic HBM bytes of one launch of an FLCE product (one full chunk of C rows): each
-    operand read once, each result written once. grad_weight adds its fp32 accumulator: written
-    by the first chunk, read and written by the others (averaged over the launches)."""
+def gemm_bytes(kernel, w, stored_slice=True):
+    """Algorithmic HBM bytes of one launch of an FLCE product: each operand read once, each
+    result written once. The stored-logits schedule writes each chunk's logits as 16-bit
+    shifted values and runs grad_weight once per two chunks (K = 2C); the recomputing schedule
+    writes bf16 probabilities and runs grad_weight once per chunk. grad_weight adds its fp32
+    accumulator: written by the first launch, read and written by the others (averaged over
+    the launches)."""
     c, h, v = w.chunk_size, w.h, w.v
-    if kernel == "flce_gemm_logits":  # W and the hidden chunk in; fp32 logits out (stored slice)
-        return 2 * v * h + 2 * c * h + (4 * c * v if stored_slice else 0)
+    if kernel == "flce_gemm_logits":  # W and the hidden chunk in; 16-bit logits out (stored)
+        return 2 * v * h + 2 * c * h + (2 * c * v if stored_slice else 0)
     if kernel == "flce_gemm_probs":  # W and the hidden chunk in; bf16 probabilities out
         return 2 * v * h + 2 * c * h + 2 * c * v
     if kernel == "flce_gemm_grad_hidden":  # probabilities and W in; grad_hidden rows out
         return 2 * c * v + 2 * v * h + 2 * c * h
     if kernel == "flce_gemm_grad_weight":  # probabilities and hidden in; fp32 accumulator
-        acc = (4 + 8 * (chunks - 1)) * v * h / chunks
-        return 2 * c * v + 2 * c * h + acc
+        launches = grad_weight_launches(w, stored_slice)
+        k = w.n / launches
+        acc = (4 + 8 * (launches - 1)) * v * h / launches
+        return 2 * k * v + 2 * k * h + acc
     raise KeyError(kernel)
+
+
+def grad_weight_launches(w, stored_slice):
+    chunks = -(-w.n // w.chunk_size)
+    return -(-chunks // 2) if stored_slice else chunks
 
 
 def gemm_roofline(kernel, flops, nbytes, avg_ms):
@@ -272,16 +282,19 @@ def run_flce(args, torch, lce, workloads, name=None, recompute=False, steps=None
     flops = 6.0 * w.n * w.h * w.v
     chunks = -(-w.n // w.chunk_size)
     one = 2.0 * w.chunk_size * w.h * w.v  # one chunk's product (every chunk is full here)
-    # algorithmic flops per launch of each MFMA kernel (one chunk's product)
+    # algorithmic flops per launch of each MFMA kernel: one chunk's product, grad_weight's
+    # over the rows of its launch (two chunks in the stored-logits schedule)
     per_launch = {"flce_gemm_logits": one, "flce_gemm_probs": one,
-                  "flce_gemm_grad_hidden": one, "flce_gemm_grad_weight": one}
+                  "flce_gemm_grad_hidden": one,
+                  "flce_gemm_grad_weight": 2.0 * w.n * w.h * w.v
+                  / grad_weight_launches(w, not recompute)}
     gemms = [k for k in kernels if k[0] in per_launch]
     dom = max(gemms, key=lambda k: k[1]) if gemms else None
     roof = None
     if dom:
         avg_ms = dom[1] / dom[2]
         roof = gemm_roofline(dom[0], per_launch[dom[0]],
-                             gemm_bytes(dom[0], w, chunks, stored_slice=not recompute), avg_ms)
+                             gemm_bytes(dom[0], w, stored_slice=not recompute), avg_ms)
         roof["traffic"] = stored_traffic(dom[0], w.name)
     executed = (8.0 if recompute else 6.0) * w.n * w.h * w.v
     return {

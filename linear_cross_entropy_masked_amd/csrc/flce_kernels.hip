@@ -23,6 +23,12 @@
 // The probabilities enter the MFMA as unscaled bf16; the scale g·s and the one-hot are
 // applied in fp32, which keeps the fp32 grad_weight within 1e-4 normwise of the exact
 // result (scaling or subtracting inside the bf16 operand would not).
+//
+// Where h is a multiple of 64 and C >= 64 (the compact workspace: the slice and nothing
+// else), the stored-logits schedule keeps each chunk's logits as fp16(z − tile max), two
+// chunks per slice, and runs step 6 once per two chunks (flce_paired): the fp32 accumulator
+// is then read and written half as often. The lse and the loss come from the fp32 logits in
+// either form.
 #include "common.h"
 #include "flce.h"
 #include "gemm_tile.h"
@@ -56,6 +62,7 @@ __device__ __forceinline__ bool has_label(int32_t y, int64_t v, int32_t ignore_i
 // the logsumexp of each row is then a merge of ⌈V / 256⌉ pairs instead of a pass over Z.
 struct EpiLogits {
   static constexpr bool kColSums = false;
+  static constexpr bool kTileMax = false;
   float* z;
   int64_t ldz;
   const float* bias;
@@ -72,6 +79,57 @@ struct EpiLogits {
   }
   __device__ __forceinline__ void store4(int64_t m, int64_t n, gemm::f32x4_t a, Aux b) {
     *reinterpret_cast<gemm::f32x4_t*>(z + m * ldz + n) = a + b;
+  }
+  __device__ __forceinline__ gemm::f32x4_t value4(gemm::f32x4_t a, Aux b) const { return a + b; }
+  __device__ __forceinline__ float value1(int64_t n, float a) const { return bias ? a + bias[n] : a; }
+  __device__ __forceinline__ void row_stats(int64_t m, int64_t t, float mx, float sum) {
+    part[m * part_ld + t] = float2{mx, sum};
+  }
+};
+
+// fp16 encoding of a shifted logit (round to nearest even) and back (exact).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const _Float16 a = static_cast<_Float16>(lo), b = static_cast<_Float16>(hi);
+  return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+__device__ __forceinline__ float f16_to_f32(uint32_t bits) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits & 0xffffu)));
+}
+
+// The stored-logits schedule's logits tile in 16 bits: d = fp16(z − m_t) into a 16-bit
+// [rows, ldz] array, m_t = the row's maximum over this 256-column tile (known before the
+// stores, see kTileMax). The per-tile (max, Σ exp(z − max)) pairs come from the fp32 values
+// as in EpiLogits (so the lse is unchanged), and the label logit is kept in fp32 in zy[m]
+// (the loss term is then exact). exp(d + m_t − lse) is within 2^-11 · |z − m_t| relative of
+// the exact probability, and a chunk's logits take half the bytes of the fp32 slice.
+struct EpiLogits16 {
+  static constexpr bool kColSums = false;
+  static constexpr bool kTileMax = true;
+  static constexpr bool kRowStats = true;
+  uint16_t* z;
+  int64_t ldz;
+  const float* bias;
+  float2* part;
+  int64_t part_ld;
+  const int32_t* labels;
+  float* zy;
+  __device__ void begin(int64_t) {}
+  __device__ __forceinline__ void operator()(int64_t, int64_t, float) {}  // put1m instead
+  __device__ __forceinline__ void put1m(int64_t m, int64_t n, float a, float mx) {
+    const float x = bias ? a + bias[n] : a;
+    z[m * ldz + n] = uint16_t(pack_f16x2(x - mx, 0.f) & 0xffffu);
+    if (int64_t(labels[m]) == n) zy[m] = x;
+  }
+  using Aux = gemm::f32x4_t;
+  __device__ __forceinline__ Aux load4(int64_t, int64_t n) const {
+    return bias ? Aux{bias[n], bias[n + 1], bias[n + 2], bias[n + 3]} : Aux{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ __forceinline__ void store4m(int64_t m, int64_t n, gemm::f32x4_t a, Aux b, float mx) {
+    const gemm::f32x4_t x = a + b;
+    *reinterpret_cast<uint2*>(z + m * ldz + n) =
+        uint2{pack_f16x2(x[0] - mx, x[1] - mx), pack_f16x2(x[2] - mx, x[3] - mx)};
+    const int64_t d = int64_t(labels[m]) - n;
+    if (d >= 0 && d < 4) zy[m] = d == 0 ? x[0] : d == 1 ? x[1] : d == 2 ? x[2] : x[3];
   }
   __device__ __forceinline__ gemm::f32x4_t value4(gemm::f32x4_t a, Aux b) const { return a + b; }
   __device__ __forceinline__ float value1(int64_t n, float a) const { return bias ? a + bias[n] : a; }
@@ -105,6 +163,7 @@ struct EpiLseOnly {
   float* zy;
   static constexpr bool kRowStats = true;
   static constexpr bool kColSums = false;
+  static constexpr bool kTileMax = false;
   __device__ void begin(int64_t) {}
   __device__ __forceinline__ void operator()(int64_t m, int64_t n, float a) {
     if (int64_t(labels[m]) == n) zy[m] = bias ? a + bias[n] : a;
@@ -145,6 +204,7 @@ struct EpiProbs {
   float* colsum;  // the slice as floats, or NULL: no column sums
   static constexpr bool kRowStats = false;
   static constexpr bool kColSums = true;
+  static constexpr bool kTileMax = false;
   __device__ void begin(int64_t) {}
   __device__ __forceinline__ int64_t at(int64_t m, int64_t n) const {
     return m * p_ld + (n >> 6) * (2 * kGroup) + (n & 63);
@@ -188,6 +248,7 @@ struct EpiProbs {
 // dH[m, n] = coef · (acc − W[y_m, n]) for labelled rows, 0 otherwise; bf16 out.
 struct EpiGradHidden {
   static constexpr bool kColSums = false;
+  static constexpr bool kTileMax = false;
   static constexpr bool kRowStats = false;
   uint16_t* dh;
   int64_t ldh;
@@ -229,6 +290,7 @@ struct EpiGradHidden {
 // dW[m, n] = (overwrite ? 0 : dW[m, n]) + coef · acc.
 struct EpiGradWeight {
   static constexpr bool kColSums = false;
+  static constexpr bool kTileMax = false;
   static constexpr bool kRowStats = false;
   float* dw;
   int64_t ldw;
@@ -337,6 +399,7 @@ __global__ void __launch_bounds__(256) onehot_segments_kernel(
 
 struct EpiPartial {
   static constexpr bool kColSums = false;
+  static constexpr bool kTileMax = false;
   static constexpr bool kRowStats = false;
   float* slice;
   int64_t M, N;
@@ -446,13 +509,14 @@ __global__ void __launch_bounds__(kRowThreads) slice_row_lse_kernel(
 
 // lse of each labelled row from the logits GEMM's per-tile (max, Σ exp) pairs, merged in a
 // fixed order; loss term lse − z[y] and lse_out. z[y] comes from zy when given, else from the
-// fp32 slice; the lse goes to lse_c in the layout lse_gap names (lse_off). One wavefront per
-// row.
+// fp32 slice; zy and row_loss may be the same array (each row reads its label logit before
+// writing its term). The lse goes to lse_c in the layout lse_gap names (lse_off). One
+// wavefront per row.
 __global__ void __launch_bounds__(256) lse_merge_rows_kernel(
     const float2* __restrict__ part, int64_t tiles, const float* __restrict__ z, int64_t ldz,
-    const float* __restrict__ zy, int64_t rows, int64_t v, const int32_t* __restrict__ labels,
+    const float* zy, int64_t rows, int64_t v, const int32_t* __restrict__ labels,
     int32_t ignore_index, float* __restrict__ lse_c, int64_t lse_gap,
-    float* __restrict__ row_loss, float* __restrict__ lse_out) {
+    float* row_loss, float* __restrict__ lse_out) {
   const int64_t i = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (i >= rows) return;
@@ -549,6 +613,59 @@ __global__ void __launch_bounds__(256) slice_to_probs_kernel(float* z, int64_t l
   o.x = pack_bf16x2(p[0], p[1]);
   o.y = pack_bf16x2(p[2], p[3]);
   *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(row) + g * (2 * kGroup) + 4 * L) = o;
+}
+
+// In place over a 16-bit [rows, ldz] array of shifted logits d = fp16(z − m_t) (EpiLogits16):
+// P = bf16(exp(d + (m_t − lse))), m_t = part[i · tiles + t].x for the column's 256-wide tile
+// t; 0 for rows without a label and for the padding columns v .. ldz − 1. Each lane converts
+// 8 consecutive elements (one 16-byte load, one 16-byte store at the same address).
+__global__ void __launch_bounds__(256) shifted_to_probs_kernel(
+    uint16_t* z, int64_t ldz, int64_t v, const int32_t* __restrict__ labels, int32_t ignore_index,
+    const float* __restrict__ lse_c, const float2* __restrict__ part, int64_t tiles) {
+  const int64_t i = blockIdx.y;
+  const int64_t col = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (col >= ldz) return;
+  uint16_t* p = z + i * ldz + col;
+  uint4 o = {0u, 0u, 0u, 0u};
+  if (has_label(labels[i], v, ignore_index) && col < v) {
+    const uint4 x = *reinterpret_cast<const uint4*>(p);
+    const float sh = part[i * tiles + (col >> 8)].x - lse_c[i];
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    float r[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float d = f16_to_f32(w[k >> 1] >> (16 * (k & 1)));
+      r[k] = col + k < v ? fast_exp2((d + sh) * kLog2e) : 0.f;
+    }
+    o = uint4{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]), pack_bf16x2(r[4], r[5]),
+              pack_bf16x2(r[6], r[7])};
+  }
+  *reinterpret_cast<uint4*>(p) = o;
+}
+
+// grad_bias[v] (=|+=) coef · (Σ_{labelled i} p_iv − #{i: y_i = v}) from the shifted 16-bit
+// logits, p = exp(d + m_t − lse) in fp32 (the probability before its bf16 rounding). A
+// workgroup's 256 columns are one lse tile.
+__global__ void __launch_bounds__(256) shifted_bias_grad_kernel(
+    const uint16_t* __restrict__ z, int64_t ldz, int64_t rows, int64_t v,
+    const int32_t* __restrict__ labels, int32_t ignore_index, const float* __restrict__ lse_c,
+    const float2* __restrict__ part, int64_t tiles, float* __restrict__ grad_bias, int overwrite,
+    const long long* count_dev, long long count_host, const float* gout) {
+  const int64_t col = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (col >= v) return;
+  const int64_t t = col >> 8;
+  float sp = 0.f;
+  int cnt = 0;
+  for (int64_t i = 0; i < rows; ++i) {
+    const int32_t y = labels[i];
+    if (!has_label(y, v, ignore_index)) continue;
+    const float d = f16_to_f32(z[i * ldz + col]);
+    sp += fast_exp2((d + (part[i * tiles + t].x - lse_c[i])) * kLog2e);
+    cnt += (int64_t(y) == col);
+  }
+  const float coef = flce_coef(count_dev, count_host, gout);
+  const float dv = coef * (sp - float(cnt));
+  grad_bias[col] = overwrite ? dv : grad_bias[col] + dv;
 }
 
 // dW[y] −= coef · Σ_{i in chunk, y_i = y} h_i. The first chunk row carrying label y owns that
@@ -725,6 +842,169 @@ FlceWs flce_carve(void* base, int64_t h, int64_t v, int64_t c) {
   return w;
 }
 
+// Stored-logits schedule of the compact layout, two chunks per slice. The logits GEMM writes a
+// chunk's logits as 16-bit shifted values (EpiLogits16) into one half of the slice, a
+// [C, ldz] 16-bit array, converted in place to bf16 probabilities. Chunk A (half 0) and the
+// chunk after it, B (half 1), then share one grad_weight product over K = rows_A + rows_B
+// (their probability rows are contiguous), so the fp32 accumulator is read and written once
+// per two chunks. Per pair:
+//   A: logits → lse and loss terms → (grad_bias) → probabilities → grad_hidden, its split
+//      partials in half 1
+//   B: logits into half 1 → lse and loss terms → (grad_bias) → probabilities
+//   grad_weight over A ∪ B; its one-hot term over A ∪ B (sorted labels at the start of half 0)
+//   B: grad_hidden, its split partials in half 0
+// A chunk's tile pairs, lse and label logits / loss terms sit in its own grad_hidden rows
+// until its grad_hidden product overwrites them. The call state starts in the last 16 bytes
+// of grad_hidden (`st`) and moves, just before the last chunk's grad_hidden product, to the
+// end of the half that takes that product's partials; the partials stop short of it.
+hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceState* st,
+                       hipStream_t s) {
+  const int64_t n = a.n, h = a.h, v = a.v;
+  const long long th = a.num_label_tokens >= 0 ? a.num_label_tokens : -1;
+  const bool accumulate = (a.flags & FLCE_ACCUMULATE) != 0;
+  uint16_t* const half[2] = {reinterpret_cast<uint16_t*>(ws.slice),
+                             reinterpret_cast<uint16_t*>(ws.slice) + chunk * ws.ldz};
+  const int64_t half_bytes = chunk * ws.ldz * 2;
+  constexpr int64_t kStateReserve = 256;  // end of a half kept for the moved call state
+  hipError_t e;
+
+  // logits → lse, loss terms → grad_bias → probabilities, for rows [c0, c0 + rows) in half hf
+  auto front = [&](int64_t c0, int64_t rows, int hf, bool first) -> hipError_t {
+    const int32_t* lab = a.labels + c0;
+    float* scr = reinterpret_cast<float*>(a.grad_hidden + c0 * h);
+    float2* part = reinterpret_cast<float2*>(scr);
+    float* lse_c = scr + 2 * rows * ws.tiles;
+    float* term = lse_c + rows;  // first the label logits, then the loss terms
+    View Ah{a.hidden + c0 * h, h, kGroup, rows, h};
+    View Bw{a.weight, h, kGroup, v, h};
+    EpiLogits16 el{half[hf], ws.ldz, a.bias, part, ws.tiles, lab, term};
+    {
+      TimedLaunch t(s, K_FLCE_GEMM_LOGITS);
+      hipError_t r = gemm::v2::launch<Wide, true, true>(Ah, Bw, rows, v, h, 1, true, el, s);
+      if (r != hipSuccess) return r;
+    }
+    {
+      TimedLaunch t(s, K_FLCE_ROW_LSE);
+      hipLaunchKernelGGL(lse_merge_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s,
+                         part, ws.tiles, nullptr, int64_t(0), term, rows, v, lab,
+                         a.ignore_index, lse_c, int64_t(-1), term,
+                         a.lse_out ? a.lse_out + c0 : nullptr);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    {
+      TimedLaunch t(s, K_FLCE_LOSS_ACC);
+      hipLaunchKernelGGL(loss_accumulate_kernel, dim3(1), dim3(256), 0, s, term, rows, st,
+                         int(first));
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (a.grad_bias) {
+      TimedLaunch t(s, K_FLCE_BIAS_GRAD);
+      hipLaunchKernelGGL(shifted_bias_grad_kernel, dim3(unsigned((v + 255) / 256)), dim3(256), 0,
+                         s, half[hf], ws.ldz, rows, v, lab, a.ignore_index, lse_c, part,
+                         ws.tiles, a.grad_bias, int(first && !accumulate), &st->count, th,
+                         a.grad_output);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    TimedLaunch t(s, K_FLCE_TO_PROBS);
+    hipLaunchKernelGGL(shifted_to_probs_kernel,
+                       dim3(unsigned((ws.ldz / 8 + 255) / 256), unsigned(rows)), dim3(256), 0, s,
+                       half[hf], ws.ldz, v, lab, a.ignore_index, lse_c, part, ws.tiles);
+    return hipGetLastError();
+  };
+
+  // grad_hidden of rows [c0, c0 + rows), probabilities in half hf, split partials in the
+  // other half
+  auto grad_hidden = [&](int64_t c0, int64_t rows, int hf, bool last) -> hipError_t {
+    float* other = reinterpret_cast<float*>(half[1 - hf]);
+    if (last) {
+      FlceState* dst = reinterpret_cast<FlceState*>(reinterpret_cast<char*>(other) + half_bytes - 16);
+      TimedLaunch t(s, K_FLCE_LOSS_ACC);
+      hipLaunchKernelGGL(state_move_kernel, dim3(1), dim3(64), 0, s, st, dst);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      st = dst;
+    }
+    const int32_t* lab = a.labels + c0;
+    View Ap{half[hf], ws.ldz, kGroup, rows, v};  // P: rows = chunk rows, cols = vocab (K-major)
+    View Bw2{a.weight, h, kGroup, v, h};         // W: rows = k (vocab), cols = n (hidden)
+    const int64_t tiles = row_tiles(rows) * ((h + Wide::BN - 1) / Wide::BN);
+    // partial element e of split z sits at float gap_index(z · rows · h + e) of `other`
+    const int64_t gap_cap = (half_bytes - kStateReserve) / (8 * rows * h);
+    int64_t splits = 256 / tiles;
+    if (splits > gap_cap) splits = gap_cap;
+    if (splits > (v + 2047) / 2048) splits = (v + 2047) / 2048;  // keep >= 2048 of K per split
+    if (splits < 1) splits = 1;
+    const long long* cnt = &st->count;
+    uint16_t* dh = a.grad_hidden + c0 * h;
+    {
+      TimedLaunch t(s, K_FLCE_GEMM_GRAD_HIDDEN);
+      hipError_t r;
+      if (splits == 1) {
+        EpiGradHidden eh{dh, h, lab, a.weight, h, v, a.ignore_index, cnt, th, a.grad_output, 0.f};
+        r = gemm::v2::launch<Wide, true, false>(Ap, Bw2, rows, h, v, 1, true, eh, s);
+      } else {
+        EpiPartial ep{other, rows, h, 0};
+        r = gemm::v2::launch<Wide, true, false>(Ap, Bw2, rows, h, v, splits, true, ep, s);
+      }
+      if (r != hipSuccess) return r;
+    }
+    if (splits == 1) return hipSuccess;
+    TimedLaunch t(s, K_FLCE_GRAD_HIDDEN_REDUCE);
+    hipLaunchKernelGGL(grad_hidden_reduce_kernel, dim3(unsigned((rows * h + 255) / 256)),
+                       dim3(256), 0, s, other, rows, h, splits, dh, lab, a.weight, v,
+                       a.ignore_index, cnt, th, a.grad_output);
+    return hipGetLastError();
+  };
+
+  // grad_weight over K = rows of the pair starting at c0 (probabilities from half 0 on), then
+  // its one-hot term
+  auto grad_weight = [&](int64_t c0, int64_t rows, bool first) -> hipError_t {
+    const int32_t* lab = a.labels + c0;
+    const uint16_t* hid = a.hidden + c0 * h;
+    const long long* cnt = &st->count;
+    View Ap{half[0], ws.ldz, kGroup, rows, v};  // Pᵀ: rows = k (chunk rows), cols = vocab
+    View Bh{hid, h, kGroup, rows, h};           // hidden rows: rows = k, cols = n
+    EpiGradWeight ew{a.grad_weight, h, int(first && !accumulate), cnt, th, a.grad_output, 0.f};
+    {
+      TimedLaunch t(s, K_FLCE_GEMM_GRAD_WEIGHT);
+      hipError_t r = gemm::v2::launch<Pair, false, false>(Ap, Bh, v, h, rows, 1, false, ew, s, true);
+      if (r != hipSuccess) return r;
+    }
+    if (rows <= kSortMax) {
+      int32_t* slab = reinterpret_cast<int32_t*>(half[0]);
+      int32_t* srow = slab + rows;
+      {
+        TimedLaunch t(s, K_FLCE_LABEL_SORT);
+        hipLaunchKernelGGL(label_rank_kernel, dim3(unsigned((rows + 63) / 64)), dim3(256), 0, s,
+                           lab, rows, v, a.ignore_index, slab, srow);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
+      TimedLaunch t(s, K_FLCE_ONEHOT_FIX);
+      hipLaunchKernelGGL(onehot_segments_kernel, dim3(unsigned(rows)), dim3(256), 0, s, hid, h,
+                         rows, slab, srow, v, a.grad_weight, cnt, th, a.grad_output);
+    } else {
+      TimedLaunch t(s, K_FLCE_ONEHOT_FIX);
+      hipLaunchKernelGGL(onehot_weight_fix_kernel, dim3(unsigned(rows)), dim3(256), 0, s, hid, h,
+                         rows, lab, a.ignore_index, v, a.grad_weight, cnt, th, a.grad_output);
+    }
+    return hipGetLastError();
+  };
+
+  for (int64_t c0 = 0; c0 < n; c0 += 2 * chunk) {
+    const int64_t ra = n - c0 < chunk ? n - c0 : chunk;
+    const int64_t rest = n - c0 - ra;
+    const int64_t rb = rest < chunk ? rest : chunk;
+    const bool first = c0 == 0;
+    if ((e = front(c0, ra, 0, first)) != hipSuccess) return e;
+    if ((e = grad_hidden(c0, ra, 0, rb == 0)) != hipSuccess) return e;
+    if (rb > 0 && (e = front(c0 + ra, rb, 1, false)) != hipSuccess) return e;
+    if (a.grad_weight && (e = grad_weight(c0, ra + rb, first)) != hipSuccess) return e;
+    if (rb > 0 && (e = grad_hidden(c0 + ra, rb, 1, c0 + ra + rb >= n)) != hipSuccess) return e;
+  }
+  TimedLaunch t(s, K_LOSS_REDUCE);
+  hipLaunchKernelGGL(loss_finish_kernel, dim3(1), dim3(64), 0, s, st, th, n, a.loss_out);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int flce_check_shape(int64_t n, int64_t h, int64_t v, int64_t chunk_size, uint32_t flags) {
@@ -787,9 +1067,11 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     }
   }
 
+  if (ws.compact && !recompute) return flce_paired(a, ws, chunk, st, s);
+
   for (int64_t c0 = 0; c0 < n; c0 += chunk) {
     const int64_t rows = (n - c0) < chunk ? (n - c0) : chunk;
-    const bool first = c0 == 0, last = c0 + rows >= n;
+    const bool first = c0 == 0;
     const int32_t* lab = a.labels + c0;
     const uint16_t* hid = a.hidden + c0 * h;
 
@@ -803,19 +1085,14 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     const bool recompute_chunk =
         recompute && (ws.compact || !a.grad_bias || 2 * row_tiles(rows) * v + 64 <= chunk * ws.ldz);
 
-    // the chunk's bookkeeping (see compact_layout)
+    // the chunk's bookkeeping (see compact_layout; the compact layout's stored-logits
+    // schedule is flce_paired)
     float2* part = ws.part;
     float* lse_c = ws.lse_c;
     int64_t lse_gap = -1;
     float* zy = ws.zy;
     float* term = ws.term;
-    if (ws.compact && !recompute_chunk) {
-      float* scr = reinterpret_cast<float*>(a.grad_hidden + c0 * h);
-      part = reinterpret_cast<float2*>(scr);
-      lse_c = scr + 2 * rows * ws.tiles;
-      term = lse_c + rows;
-      zy = nullptr;
-    } else if (ws.compact) {
+    if (ws.compact) {
       part = reinterpret_cast<float2*>(ws.slice);
       zy = ws.slice + 2 * rows * ws.tiles;
       term = zy + rows;
@@ -875,14 +1152,6 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
                            dim3(unsigned((groups + 15) / 16), unsigned(rows)), dim3(256), 0, s,
                            ws.slice, ws.ldz, v, lab, a.ignore_index, lse_c);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-      }
-      // the last chunk's grad_hidden rows are about to be written: the state moves into the
-      // slice's reserved free halves, free now that the slice holds probabilities
-      if (ws.compact && last) {
-        TimedLaunch t(s, K_FLCE_LOSS_ACC);
-        hipLaunchKernelGGL(state_move_kernel, dim3(1), dim3(64), 0, s, st, st_slice);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        st = st_slice;
       }
     } else {
       if (!bwd_only) {

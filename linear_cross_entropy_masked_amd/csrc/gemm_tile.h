@@ -572,6 +572,52 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
   // Epilogues with kRowStats also get, per output row, the (max, sum of exp(x - max)) of the
   // values they store over this tile's valid columns (value4 says what those values are).
   epi.begin(kz);
+  // Epilogues with kTileMax store values relative to their row's maximum over this tile's
+  // valid columns: that maximum is reduced first (over the four lanes sharing a row, then
+  // over the WN wavefronts through LDS) and handed to every store of the row.
+  float tmax[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) tmax[i] = -INFINITY;
+  if constexpr (Epi::kTileMax) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int64_t gm = m0 + wm * (C::BM / C::WM) + 16 * i + (lane & 15);
+      float mx = -INFINITY;
+      if (gm < M) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int64_t gn = n0 + wn * (C::BN / C::WN) + 16 * j + 4 * (lane >> 4);
+          if (gn + 4 <= N) {
+            const f32x4_t z = epi.value4(acc[i][j], epi.load4(gm, gn));
+            mx = fmaxf(mx, fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (gn + q < N) mx = fmaxf(mx, epi.value1(gn + q, acc[i][j][q]));
+          }
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      tmax[i] = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    }
+    __syncthreads();  // every wavefront is past the main loop: the LDS ring is free
+    float* red = reinterpret_cast<float*>(lds);  // [WN][BM]
+    if ((lane >> 4) == 0) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) red[wn * C::BM + wm * (C::BM / C::WM) + 16 * i + lane] = tmax[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = wm * (C::BM / C::WM) + 16 * i + (lane & 15);
+      float m = red[r];
+#pragma unroll
+      for (int w = 1; w < C::WN; ++w) m = fmaxf(m, red[w * C::BM + r]);
+      tmax[i] = m;
+    }
+    // the row-stats reduction below writes the same LDS only after its own barrier, which
+    // every wavefront reaches after these reads
+  }
   float rm[TM], rs[TM];
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
@@ -601,7 +647,10 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
       for (int j = 0; j < TN; ++j) {
         const int64_t gn = n0 + wn * (C::BN / C::WN) + 16 * j + 4 * (lane >> 4);
         if (gn + 4 <= N) {
-          epi.store4(gm, gn, acc[i0 + di][j], aux[di][j]);
+          if constexpr (Epi::kTileMax)
+            epi.store4m(gm, gn, acc[i0 + di][j], aux[di][j], tmax[i0 + di]);
+          else
+            epi.store4(gm, gn, acc[i0 + di][j], aux[di][j]);
           if constexpr (Epi::kColSums) cs[j] += epi.colvalue4(acc[i0 + di][j], aux[di][j]);
           if constexpr (Epi::kRowStats) {
             const f32x4_t z = epi.value4(acc[i0 + di][j], aux[di][j]);
@@ -619,7 +668,10 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
 #pragma unroll
           for (int q = 0; q < 4; ++q)
             if (gn + q < N) {
-              epi(gm, gn + q, acc[i0 + di][j][q]);
+              if constexpr (Epi::kTileMax)
+                epi.put1m(gm, gn + q, acc[i0 + di][j][q], tmax[i0 + di]);
+              else
+                epi(gm, gn + q, acc[i0 + di][j][q]);
               if constexpr (Epi::kRowStats) {
                 const float z = epi.value1(gn + q, acc[i0 + di][j][q]);
                 float m1 = rm[i0 + di], s1 = rs[i0 + di];

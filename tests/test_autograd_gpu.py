@@ -157,16 +157,17 @@ def _flce_leaves(inp, dev):
 @pytest.mark.parametrize("bias", [False, True])
 def test_linear_ce_matches_fused_call(dev, bias):
     """The autograd function (forward = flce_fwd, backward = flce_bwd) against one fused
-    call of the library on the same inputs: loss, grad_hidden and grad_weight (in the
-    weight's dtype) bitwise; grad_bias (summed in another order by the recomputing backward)
-    normwise to the oracle."""
+    call of the library with the recomputing schedule on the same inputs: loss, grad_hidden
+    and grad_weight (in the weight's dtype) bitwise; grad_bias (summed in another order by the
+    recomputing backward) normwise to the oracle."""
     inp = random_flce(96, 64, 1000, bias=bias, seed=40)
     hid, w, b = _flce_leaves(inp, dev)
     lab = torch.from_numpy(inp.labels).to(dev)
     loss = ag.linear_cross_entropy(hid, w, lab, b, chunk_size=40, reduction="mean")
     loss.backward()
     l2, gh, gw, gb, _ = lce.flce_fwd_bwd(hid.detach(), w.detach(), lab,
-                                         None if b is None else b.detach(), chunk_size=40)
+                                         None if b is None else b.detach(), chunk_size=40,
+                                         recompute=True)
     assert loss.item() == l2.item()
     assert torch.equal(hid.grad.view(torch.int16), gh.view(torch.int16))
     assert torch.equal(w.grad.view(torch.int16), gw.to(torch.bfloat16).view(torch.int16))
