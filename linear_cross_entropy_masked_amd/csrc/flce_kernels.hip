@@ -100,7 +100,7 @@ __device__ __forceinline__ float f16_to_f32(uint32_t bits) {
 // [rows, ldz] array, m_t = the row's maximum over this 256-column tile (known before the
 // stores, see kTileMax). The per-tile (max, Σ exp(z − max)) pairs come from the fp32 values
 // as in EpiLogits (so the lse is unchanged), and the label logit is kept in fp32 in zy[m]
-// (the loss term is then exact). exp(d + m_t − lse) is within 2^-11 · |z − m_t| relative of
+// (the loss term is then exact); the row's label is its row_tag. exp(d + m_t − lse) is within 2^-11 · |z − m_t| relative of
 // the exact probability, and a chunk's logits take half the bytes of the fp32 slice.
 struct EpiLogits16 {
   static constexpr bool kColSums = false;
@@ -115,20 +115,22 @@ struct EpiLogits16 {
   float* zy;
   __device__ void begin(int64_t) {}
   __device__ __forceinline__ void operator()(int64_t, int64_t, float) {}  // put1m instead
-  __device__ __forceinline__ void put1m(int64_t m, int64_t n, float a, float mx) {
+  __device__ __forceinline__ int row_tag(int64_t m) const { return labels[m]; }
+  __device__ __forceinline__ void put1m(int64_t m, int64_t n, float a, float mx, int y) {
     const float x = bias ? a + bias[n] : a;
     z[m * ldz + n] = uint16_t(pack_f16x2(x - mx, 0.f) & 0xffffu);
-    if (int64_t(labels[m]) == n) zy[m] = x;
+    if (int64_t(y) == n) zy[m] = x;
   }
   using Aux = gemm::f32x4_t;
   __device__ __forceinline__ Aux load4(int64_t, int64_t n) const {
     return bias ? Aux{bias[n], bias[n + 1], bias[n + 2], bias[n + 3]} : Aux{0.f, 0.f, 0.f, 0.f};
   }
-  __device__ __forceinline__ void store4m(int64_t m, int64_t n, gemm::f32x4_t a, Aux b, float mx) {
+  __device__ __forceinline__ void store4m(int64_t m, int64_t n, gemm::f32x4_t a, Aux b, float mx,
+                                          int y) {
     const gemm::f32x4_t x = a + b;
     *reinterpret_cast<uint2*>(z + m * ldz + n) =
         uint2{pack_f16x2(x[0] - mx, x[1] - mx), pack_f16x2(x[2] - mx, x[3] - mx)};
-    const int64_t d = int64_t(labels[m]) - n;
+    const int64_t d = int64_t(y) - n;
     if (d >= 0 && d < 4) zy[m] = d == 0 ? x[0] : d == 1 ? x[1] : d == 2 ? x[2] : x[3];
   }
   __device__ __forceinline__ gemm::f32x4_t value4(gemm::f32x4_t a, Aux b) const { return a + b; }

@@ -575,10 +575,21 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
   // Epilogues with kTileMax store values relative to their row's maximum over this tile's
   // valid columns: that maximum is reduced first (over the four lanes sharing a row, then
   // over the WN wavefronts through LDS) and handed to every store of the row.
+  // They also get a per-row tag (row_tag, e.g. the row's label), loaded here ahead of the
+  // stores that use it.
   float tmax[TM];
+  int rtag[TM];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) tmax[i] = -INFINITY;
+  for (int i = 0; i < TM; ++i) {
+    tmax[i] = -INFINITY;
+    rtag[i] = -1;
+  }
   if constexpr (Epi::kTileMax) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int64_t gm = m0 + wm * (C::BM / C::WM) + 16 * i + (lane & 15);
+      if (gm < M) rtag[i] = epi.row_tag(gm);
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int64_t gm = m0 + wm * (C::BM / C::WM) + 16 * i + (lane & 15);
@@ -648,7 +659,7 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
         const int64_t gn = n0 + wn * (C::BN / C::WN) + 16 * j + 4 * (lane >> 4);
         if (gn + 4 <= N) {
           if constexpr (Epi::kTileMax)
-            epi.store4m(gm, gn, acc[i0 + di][j], aux[di][j], tmax[i0 + di]);
+            epi.store4m(gm, gn, acc[i0 + di][j], aux[di][j], tmax[i0 + di], rtag[i0 + di]);
           else
             epi.store4(gm, gn, acc[i0 + di][j], aux[di][j]);
           if constexpr (Epi::kColSums) cs[j] += epi.colvalue4(acc[i0 + di][j], aux[di][j]);
@@ -669,7 +680,7 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
           for (int q = 0; q < 4; ++q)
             if (gn + q < N) {
               if constexpr (Epi::kTileMax)
-                epi.put1m(gm, gn + q, acc[i0 + di][j][q], tmax[i0 + di]);
+                epi.put1m(gm, gn + q, acc[i0 + di][j][q], tmax[i0 + di], rtag[i0 + di]);
               else
                 epi(gm, gn + q, acc[i0 + di][j][q]);
               if constexpr (Epi::kRowStats) {
