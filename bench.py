@@ -72,7 +72,8 @@ KERNEL_NAMES = [
     ("EpiProbs", "flce_gemm_probs"), ("EpiGradHidden", "flce_gemm_grad_hidden"),
     ("EpiPartial", "flce_gemm_grad_hidden"), ("EpiGradWeight", "flce_gemm_grad_weight"),
     ("slice_row_lse_kernel", "flce_row_lse"), ("slice_bias_grad_kernel", "flce_bias_grad"),
-    ("slice_to_probs_kernel", "flce_to_probs"), ("onehot_weight_fix_kernel", "flce_onehot_fix"),
+    ("slice_to_probs_kernel", "flce_to_probs"), ("shifted_to_probs_kernel", "flce_to_probs"),
+    ("shifted_bias_grad_kernel", "flce_bias_grad"), ("onehot_weight_fix_kernel", "flce_onehot_fix"),
     ("grad_hidden_reduce_kernel", "flce_grad_hidden_reduce"), ("fill_zero", "fill_zero"),
     ("label_rank_kernel", "flce_label_sort"), ("label_prep_kernel", "label_prep"),
     ("loss_finish_kernel", "loss_reduce"), ("loss_accumulate_kernel", "flce_loss_acc"),

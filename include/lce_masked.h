@@ -69,7 +69,7 @@ extern "C" {
 #define LCE_STATUS_BAD_LABEL     1  /* some label was neither ignore_index nor in [0, V)          */
 
 /* flce flags */
-#define FLCE_RECOMPUTE           1u /* do not store the fp32 logits slice; recompute the logits
+#define FLCE_RECOMPUTE           1u /* do not store the chunk's logits; recompute the logits
                                        tile by tile for the gradients (the fully recomputed
                                        schedule of Liger-Kernel issue #533's comments)           */
 #define FLCE_ACCUMULATE          2u /* add into grad_weight / grad_bias instead of overwriting
@@ -170,11 +170,13 @@ int ce_rows_bwd(const uint16_t* logits, int64_t n, int64_t v, int64_t ld, uint16
  * C = min(chunk_size, n), rows padded to a multiple of 64 columns. The fp32 working set of
  * one chunk is that slice (NeMo Automodel PR #2996, Motivation), and with h a multiple of 64
  * and C >= 64 it is the whole workspace: the call's other state (lse, loss terms, per-tile
- * (max, sum) pairs, label count, sorted labels) then lives in the halves of the slice that
- * the bf16 probabilities leave free, or in rows of grad_hidden before the call writes them.
- * Otherwise a few words per chunk row sit beside the slice (lse, label logit, loss term and
- * one (max, sum) pair per 256-column tile); nothing grows with n. Host-only; safe without a
- * GPU. */
+ * (max, sum) pairs, label count, sorted labels) then lives in parts of the slice the
+ * schedule leaves free, or in rows of grad_hidden before the call writes them. In that
+ * layout the stored-logits schedule keeps two chunks in the slice at once, each chunk's
+ * logits as 16-bit values (fp16 of z minus the row's maximum over a 256-column tile), and
+ * forms grad_weight once per two chunks. Otherwise a few words per chunk row sit beside the
+ * slice (lse, label logit, loss term and one (max, sum) pair per 256-column tile); nothing
+ * grows with n. Host-only; safe without a GPU. */
 int flce_workspace_size(int64_t n, int64_t h, int64_t v, int64_t chunk_size, uint32_t flags,
                         size_t* bytes);
 
@@ -189,8 +191,11 @@ int flce_workspace_size(int64_t n, int64_t h, int64_t v, int64_t chunk_size, uin
  * where P is the row softmax of z = hidden·weightᵀ + bias and Y the one-hot labels.
  * h must be a multiple of 8 (16-byte rows). Matrix products run on bf16 MFMA with fp32
  * accumulation; the probabilities enter the gradient products as bf16, the one-hot term and
- * the scale g·s are applied in fp32. The loss adds the rows' terms in row order in fp64, so
- * it does not depend on chunk_size.
+ * the scale g·s are applied in fp32. Where the logits are kept as 16-bit shifted values (see
+ * flce_workspace_size) a probability also carries the fp16 rounding of its shifted logit,
+ * a relative error of at most exp(2^-11 · (max_v z − z)) − 1; lse and loss always come from
+ * the fp32 logits. The loss adds the rows' terms in row order in fp64, so it does not
+ * depend on chunk_size.
  * grad_hidden also serves as scratch before its rows are written (see flce_workspace_size):
  * it must not overlap any input, and its contents are defined only once the call has run. */
 int flce_fwd_bwd(const uint16_t* hidden, const uint16_t* weight, const float* bias,
