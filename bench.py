@@ -158,6 +158,68 @@ def record_traffic(workload, fetch_dir, write_dir):
     print(json.dumps({k: v for k, v in table.items() if k.endswith("@" + workload)}, indent=1))
 
 
+N_XCD = 8  # GRBM_GUI_ACTIVE is summed over the XCDs: per-XCD active cycles = value / 8
+N_SIMD = 1024  # 256 CUs x 4 SIMDs
+
+
+def stored_mfma(kernel: str, workload: str):
+    """MFMA counters of a kernel from the committed rocprofv3 summary, if still current."""
+    path = os.path.join(PROFILE_DIR, "mfma.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(f"{kernel}@{workload}")
+    if not rec or rec.get("source_digest") != source_digest():
+        return None
+    return {k: rec[k] for k in ("flops_per_launch", "mfma_busy_frac", "clock_ghz")}
+
+
+def record_mfma(workload, pmc_dir, trace_dir):
+    """Turn one rocprofv3 --pmc run (SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES,
+    GRBM_GUI_ACTIVE) and one --kernel-trace run of `bench.py --only <layer>` into, per MFMA
+    kernel: executed bf16 flops per launch (MOPS x 512), the fraction of SIMD cycles its MFMA
+    pipes were busy, and the clock the active cycles imply over the traced duration."""
+    import csv
+    import glob
+    sums, disp = {}, {}
+    for f in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                k = r["Kernel_Name"]
+                d = sums.setdefault(k, {})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+                disp.setdefault(k, set()).add(r["Dispatch_Id"])
+    durs = {}
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                durs.setdefault(r["Kernel_Name"], []).append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    path = os.path.join(PROFILE_DIR, "mfma.json")
+    table = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            table = json.load(f)
+    digest = source_digest()
+    for k, d in sums.items():
+        mops = d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+        name = next((n for sub, n in KERNEL_NAMES if sub in k), None)
+        if name is None or mops <= 0 or k not in durs:
+            continue
+        n = len(disp[k])
+        active = d["GRBM_GUI_ACTIVE"] / n / N_XCD
+        busy = d["SQ_VALU_MFMA_BUSY_CYCLES"] / n
+        t = sorted(durs[k])[len(durs[k]) // 2]
+        table[f"{name}@{workload}"] = {
+            "flops_per_launch": mops / n * 512, "mfma_busy_frac": round(busy / (active * N_SIMD), 4),
+            "clock_ghz": round(active / t / 1e9, 3), "median_launch_ms": round(t * 1e3, 4),
+            "dispatches": n, "source_digest": digest}
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+    print(json.dumps({k: v for k, v in table.items() if k.endswith("@" + workload)}, indent=1))
+
+
 def ce_algorithmic_bytes(n, v, nvalid):
     """Bytes the method must move: forward reads each labelled row once; the in-place backward
     reads each labelled row and writes every row (ignored rows are zero-filled)."""
@@ -297,6 +359,7 @@ def run_flce(args, torch, lce, workloads, name=None, recompute=False, steps=None
         roof = gemm_roofline(dom[0], per_launch[dom[0]],
                              gemm_bytes(dom[0], w, stored_slice=not recompute), avg_ms)
         roof["traffic"] = stored_traffic(dom[0], w.name)
+        roof["mfma_counters"] = stored_mfma(dom[0], w.name)
     executed = (8.0 if recompute else 6.0) * w.n * w.h * w.v
     return {
         "workload": w, "ms": ms, "wall_s": wall, "tokens_per_s": w.n / (ms * 1e-3),
@@ -477,7 +540,16 @@ def main(argv=None) -> int:
     ap.add_argument("--record-traffic", nargs=3, metavar=("LAYER", "FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: store HBM bytes per launch from two rocprofv3 --pmc runs "
                          "(FETCH_SIZE, WRITE_SIZE) of --only LAYER --copy-calibration")
+    ap.add_argument("--record-mfma", nargs=3, metavar=("LAYER", "PMC_DIR", "TRACE_DIR"),
+                    help="no GPU: store MFMA flops, busy fraction and clock per launch from a "
+                         "rocprofv3 --pmc run (SQ_INSTS_VALU_MFMA_MOPS_BF16, "
+                         "SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE) and a --kernel-trace run")
     args = ap.parse_args(argv)
+    if args.record_mfma:
+        layer, pdir, tdir = args.record_mfma
+        record_mfma({"flce": FLCE_WORKLOAD, "long": LONG_WORKLOAD, "ce": CE_WORKLOAD}[layer],
+                    pdir, tdir)
+        return 0
     if args.record_traffic:
         layer, fdir, wdir = args.record_traffic
         record_traffic({"flce": FLCE_WORKLOAD, "long": LONG_WORKLOAD, "ce": CE_WORKLOAD}[layer],
