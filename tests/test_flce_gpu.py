@@ -186,6 +186,50 @@ def test_two_chunks_per_slice(dev, n, chunk):
     assert np.array_equal(res["lse"], rec["lse"])
 
 
+@pytest.mark.parametrize("n,chunk", [(150, 64), (300, 128)])
+def test_two_chunks_per_slice_accumulate(dev, n, chunk):
+    """Paired chunks adding into existing fp32 grad_weight and grad_bias (FLCE_ACCUMULATE):
+    the first grad_weight product accumulates too."""
+    h, v = 192, 1100
+    assert stores_16bit_logits(n, h, v, chunk)
+    inp = random_flce(n, h, v, weight_sigma=0.2, bias=True, ignore_frac=0.1, seed=7 * n)
+    rng = np.random.default_rng(n)
+    init = (rng.normal(0, 0.01, (v, h)), rng.normal(0, 0.01, v))
+    res = run_flce(dev, inp, chunk, accumulate_init=init)
+    check(inp, res, init=init)
+
+
+def test_two_chunks_per_slice_without_grad_weight(dev):
+    """Paired chunks when only grad_hidden is asked for: the grad_weight product and its
+    one-hot term are skipped; grad_hidden, loss and lse are the full call's."""
+    n, h, v, chunk = 200, 128, 900, 64
+    assert stores_16bit_logits(n, h, v, chunk)
+    inp = random_flce(n, h, v, weight_sigma=0.2, ignore_frac=0.1, seed=71)
+    full = run_flce(dev, inp, chunk)
+    hid = bits_to_device(inp.hidden, dev)
+    w = bits_to_device(inp.weight, dev)
+    lab = torch.from_numpy(inp.labels.astype(np.int32)).to(dev)
+    loss, gh, gw, _, lse = lce.flce_fwd_bwd(hid, w, lab, chunk_size=chunk, grad_weight=False,
+                                            return_lse=True)
+    torch.cuda.synchronize()
+    assert gw is None
+    assert float(loss.item()) == full["loss"]
+    assert np.array_equal(lse.cpu().numpy(), full["lse"])
+    assert torch.equal(gh, full["gh"])
+
+
+def test_two_chunks_per_slice_bad_labels(dev):
+    """Labels outside [0, v) (other than ignore_index) in paired chunks: flagged, treated as
+    ignored, never matched as a label column by the logits epilogue."""
+    n, h, v, chunk = 190, 128, 700, 64
+    inp = random_flce(n, h, v, weight_sigma=0.2, bias=True, ignore_frac=0.05, seed=72)
+    inp.labels[[3, 70, 150]] = [v, v + 3, -7]
+    res = run_flce(dev, inp, chunk)
+    assert res["status"] & lce.LCE_STATUS_BAD_LABEL
+    check(inp, res)
+    assert not res["gh"][torch.tensor([3, 70, 150], device=dev)].any().item()
+
+
 @pytest.mark.parametrize("recompute", [False, True])
 def test_one_slice_workspace_and_chunk_independent_loss(dev, recompute):
     """With h a multiple of 64 and chunks of 64 rows or more the workspace is one fp32
