@@ -249,10 +249,10 @@ def timed_kernels(torch, lce, stream, step, steps):
 def gemm_bytes(kernel, w, stored_slice=True):
     """Algorithmic HBM bytes of one launch of an FLCE product: each operand read once, each
     result written once. The stored-logits schedule writes each chunk's logits as 16-bit
-    shifted values and runs grad_weight once per two chunks (K = 2C); the recomputing schedule
-    writes bf16 probabilities and runs grad_weight once per chunk. grad_weight adds its fp32
-    accumulator: written by the first launch, read and written by the others (averaged over
-    the launches)."""
+    shifted values; the recomputing schedule stores none. At the benchmark's workloads both
+    run grad_weight once per two chunks (K = 2C). grad_weight adds its fp32 accumulator:
+    written by the first launch, read and written by the others (averaged over the
+    launches)."""
     c, h, v = w.chunk_size, w.h, w.v
     if kernel == "flce_gemm_logits":  # W and the hidden chunk in; 16-bit logits out (stored)
         return 2 * v * h + 2 * c * h + (2 * c * v if stored_slice else 0)
@@ -261,16 +261,18 @@ def gemm_bytes(kernel, w, stored_slice=True):
     if kernel == "flce_gemm_grad_hidden":  # probabilities and W in; grad_hidden rows out
         return 2 * c * v + 2 * v * h + 2 * c * h
     if kernel == "flce_gemm_grad_weight":  # probabilities and hidden in; fp32 accumulator
-        launches = grad_weight_launches(w, stored_slice)
+        launches = grad_weight_launches(w)
         k = w.n / launches
         acc = (4 + 8 * (launches - 1)) * v * h / launches
         return 2 * k * v + 2 * k * h + acc
     raise KeyError(kernel)
 
 
-def grad_weight_launches(w, stored_slice):
+def grad_weight_launches(w):
+    """Both schedules keep two chunks per slice here (h a multiple of 64, chunk >= 64,
+    grad_hidden asked for, no grad_bias): one grad_weight launch per two chunks."""
     chunks = -(-w.n // w.chunk_size)
-    return -(-chunks // 2) if stored_slice else chunks
+    return -(-chunks // 2)
 
 
 def gemm_roofline(kernel, flops, nbytes, avg_ms):
@@ -346,11 +348,10 @@ def run_flce(args, torch, lce, workloads, name=None, recompute=False, steps=None
     chunks = -(-w.n // w.chunk_size)
     one = 2.0 * w.chunk_size * w.h * w.v  # one chunk's product (every chunk is full here)
     # algorithmic flops per launch of each MFMA kernel: one chunk's product, grad_weight's
-    # over the rows of its launch (two chunks in the stored-logits schedule)
+    # over the rows of its launch (two chunks)
     per_launch = {"flce_gemm_logits": one, "flce_gemm_probs": one,
                   "flce_gemm_grad_hidden": one,
-                  "flce_gemm_grad_weight": 2.0 * w.n * w.h * w.v
-                  / grad_weight_launches(w, not recompute)}
+                  "flce_gemm_grad_weight": 2.0 * w.n * w.h * w.v / grad_weight_launches(w)}
     gemms = [k for k in kernels if k[0] in per_launch]
     dom = max(gemms, key=lambda k: k[1]) if gemms else None
     roof = None

@@ -172,11 +172,13 @@ int ce_rows_bwd(const uint16_t* logits, int64_t n, int64_t v, int64_t ld, uint16
  * and C >= 64 it is the whole workspace: the call's other state (lse, loss terms, per-tile
  * (max, sum) pairs, label count, sorted labels) then lives in parts of the slice the
  * schedule leaves free, or in rows of grad_hidden before the call writes them. In that
- * layout the stored-logits schedule keeps two chunks in the slice at once, each chunk's
- * logits as 16-bit values (fp16 of z minus the row's maximum over a 256-column tile), and
- * forms grad_weight once per two chunks. Otherwise a few words per chunk row sit beside the
- * slice (lse, label logit, loss term and one (max, sum) pair per 256-column tile); nothing
- * grows with n. Host-only; safe without a GPU. */
+ * layout two chunks share the slice and grad_weight is formed once per two chunks: the
+ * stored-logits schedule keeps each chunk's logits as 16-bit values (fp16 of z minus the
+ * row's maximum over a 256-column tile); the recomputing schedule (and flce_bwd) keeps each
+ * chunk's bf16 probabilities, when grad_hidden is asked for and grad_bias is not. Otherwise
+ * a few words per chunk row sit beside the slice (lse, label logit, loss term and one
+ * (max, sum) pair per 256-column tile); nothing grows with n. Host-only; safe without a
+ * GPU. */
 int flce_workspace_size(int64_t n, int64_t h, int64_t v, int64_t chunk_size, uint32_t flags,
                         size_t* bytes);
 

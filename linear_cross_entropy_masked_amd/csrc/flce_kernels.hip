@@ -189,14 +189,16 @@ struct EpiLseOnly {
 };
 
 // Pass 2 of the recomputing schedule: the recomputed logits tile becomes bf16 probabilities
-// P = exp(z − lse) in the slice's probability layout (first half of every 64-column group),
+// P = exp(z − lse) in the slice's probability layout (first half of every 64-column group,
+// p_gs = 128; or a dense [rows, ldz] array, p_gs = 64, when two chunks share the slice),
 // 0 for rows without a label and for the padding columns v .. ldz − 1 (the GEMM runs over
 // N = ldz; weight rows past v read as zero). With grad_bias it also leaves, per 256-row tile
 // mt and column n, Σ_m p (the fp32 values, before rounding) as flat element mt · v + n of the
 // slice's free halves.
 struct EpiProbs {
   uint16_t* p;
-  int64_t p_ld;  // elements between rows (2 · ldz)
+  int64_t p_ld;  // elements between rows (2 · ldz, or ldz when dense)
+  int64_t p_gs;  // elements between 64-column groups (128, or 64 when dense)
   const float* bias;
   const float* lse;
   int64_t lse_gap;  // lse layout (lse_off)
@@ -209,7 +211,7 @@ struct EpiProbs {
   static constexpr bool kTileMax = false;
   __device__ void begin(int64_t) {}
   __device__ __forceinline__ int64_t at(int64_t m, int64_t n) const {
-    return m * p_ld + (n >> 6) * (2 * kGroup) + (n & 63);
+    return m * p_ld + (n >> 6) * p_gs + (n & 63);
   }
   struct Aux {
     gemm::f32x4_t b;
@@ -844,23 +846,28 @@ FlceWs flce_carve(void* base, int64_t h, int64_t v, int64_t c) {
   return w;
 }
 
-// Stored-logits schedule of the compact layout, two chunks per slice. The logits GEMM writes a
-// chunk's logits as 16-bit shifted values (EpiLogits16) into one half of the slice, a
-// [C, ldz] 16-bit array, converted in place to bf16 probabilities. Chunk A (half 0) and the
-// chunk after it, B (half 1), then share one grad_weight product over K = rows_A + rows_B
-// (their probability rows are contiguous), so the fp32 accumulator is read and written once
-// per two chunks. Per pair:
-//   A: logits → lse and loss terms → (grad_bias) → probabilities → grad_hidden, its split
-//      partials in half 1
-//   B: logits into half 1 → lse and loss terms → (grad_bias) → probabilities
+// Two chunks per slice in the compact layout. Each half of the slice is a [C, ldz] 16-bit
+// array that ends up holding one chunk's bf16 probabilities:
+//   stored logits (kPairStored): the logits GEMM writes the chunk's logits as 16-bit shifted
+//     values (EpiLogits16), then lse and loss terms, grad_bias, and the conversion in place;
+//   recomputing (kPairRecompute): a first GEMM pass reduces the logits to lse and loss terms
+//     (EpiLseOnly), a second writes the probabilities (EpiProbs, dense);
+//   backward only (kPairBwdOnly): the second pass alone, from the caller's lse.
+// Chunk A (half 0) and the chunk after it, B (half 1), then share one grad_weight product
+// over K = rows_A + rows_B (their probability rows are contiguous), so the fp32 accumulator
+// is read and written once per two chunks. Per pair:
+//   A: probabilities into half 0 → grad_hidden, its split partials in half 1
+//   B: probabilities into half 1
 //   grad_weight over A ∪ B; its one-hot term over A ∪ B (sorted labels at the start of half 0)
 //   B: grad_hidden, its split partials in half 0
 // A chunk's tile pairs, lse and label logits / loss terms sit in its own grad_hidden rows
 // until its grad_hidden product overwrites them. The call state starts in the last 16 bytes
 // of grad_hidden (`st`) and moves, just before the last chunk's grad_hidden product, to the
 // end of the half that takes that product's partials; the partials stop short of it.
+enum PairMode { kPairStored, kPairRecompute, kPairBwdOnly };
+
 hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceState* st,
-                       hipStream_t s) {
+                       PairMode mode, hipStream_t s) {
   const int64_t n = a.n, h = a.h, v = a.v;
   const long long th = a.num_label_tokens >= 0 ? a.num_label_tokens : -1;
   const bool accumulate = (a.flags & FLCE_ACCUMULATE) != 0;
@@ -870,7 +877,8 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
   constexpr int64_t kStateReserve = 256;  // end of a half kept for the moved call state
   hipError_t e;
 
-  // logits → lse, loss terms → grad_bias → probabilities, for rows [c0, c0 + rows) in half hf
+  // the probabilities of rows [c0, c0 + rows) into half hf (with lse, loss terms and
+  // grad_bias on the way, as the mode has them)
   auto front = [&](int64_t c0, int64_t rows, int hf, bool first) -> hipError_t {
     const int32_t* lab = a.labels + c0;
     float* scr = reinterpret_cast<float*>(a.grad_hidden + c0 * h);
@@ -879,6 +887,34 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
     float* term = lse_c + rows;  // first the label logits, then the loss terms
     View Ah{a.hidden + c0 * h, h, kGroup, rows, h};
     View Bw{a.weight, h, kGroup, v, h};
+    if (mode != kPairStored) {
+      if (mode == kPairRecompute) {
+        EpiLseOnly e1{a.bias, part, ws.tiles, lab, term};
+        {
+          TimedLaunch t(s, K_FLCE_GEMM_LOGITS);
+          hipError_t r = gemm::v2::launch<Wide, true, true>(Ah, Bw, rows, v, h, 1, true, e1, s);
+          if (r != hipSuccess) return r;
+        }
+        {
+          TimedLaunch t(s, K_FLCE_ROW_LSE);
+          hipLaunchKernelGGL(lse_merge_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0,
+                             s, part, ws.tiles, nullptr, int64_t(0), term, rows, v, lab,
+                             a.ignore_index, lse_c, int64_t(-1), term,
+                             a.lse_out ? a.lse_out + c0 : nullptr);
+          if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        TimedLaunch t(s, K_FLCE_LOSS_ACC);
+        hipLaunchKernelGGL(loss_accumulate_kernel, dim3(1), dim3(256), 0, s, term, rows, st,
+                           int(first));
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
+      const float* lse = mode == kPairBwdOnly ? a.lse_in + c0 : lse_c;
+      // the GEMM runs over N = ldz: weight rows past v read as zero, their columns become 0
+      EpiProbs e2{half[hf], ws.ldz, kGroup, a.bias, lse, int64_t(-1), lab, v, a.ignore_index,
+                  nullptr};
+      TimedLaunch t(s, K_FLCE_GEMM_PROBS);
+      return gemm::v2::launch<Wide, true, true>(Ah, Bw, rows, ws.ldz, h, 1, true, e2, s);
+    }
     EpiLogits16 el{half[hf], ws.ldz, a.bias, part, ws.tiles, lab, term};
     {
       TimedLaunch t(s, K_FLCE_GEMM_LOGITS);
@@ -1002,6 +1038,7 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
     if (a.grad_weight && (e = grad_weight(c0, ra + rb, first)) != hipSuccess) return e;
     if (rb > 0 && (e = grad_hidden(c0 + ra, rb, 1, c0 + ra + rb >= n)) != hipSuccess) return e;
   }
+  if (mode == kPairBwdOnly) return hipSuccess;
   TimedLaunch t(s, K_LOSS_REDUCE);
   hipLaunchKernelGGL(loss_finish_kernel, dim3(1), dim3(64), 0, s, st, th, n, a.loss_out);
   return hipGetLastError();
@@ -1048,8 +1085,12 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
   FlceState* st_slice =
       ws.compact ? reinterpret_cast<FlceState*>(ws.slice + gap_index(chunk * ws.ldz / 2 - 32))
                  : ws.state;
+  // two chunks per slice (flce_paired): the stored-logits schedule of the compact layout, and
+  // its recomputing schedule when grad_hidden rows can take the bookkeeping and no grad_bias
+  // is asked for (its column sums need the room the second chunk takes)
+  const bool paired = ws.compact && (!recompute || (gh_scratch && !fwd_only && !a.grad_bias));
   FlceState* st = st_slice;  // where the state is now
-  if (ws.compact && !recompute)
+  if (paired)
     st = reinterpret_cast<FlceState*>(reinterpret_cast<char*>(a.grad_hidden + n * h) - 16);
   hipError_t e;
 
@@ -1069,7 +1110,9 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     }
   }
 
-  if (ws.compact && !recompute) return flce_paired(a, ws, chunk, st, s);
+  if (paired)
+    return flce_paired(a, ws, chunk, st,
+                       !recompute ? kPairStored : (bwd_only ? kPairBwdOnly : kPairRecompute), s);
 
   for (int64_t c0 = 0; c0 < n; c0 += chunk) {
     const int64_t rows = (n - c0) < chunk ? (n - c0) : chunk;
@@ -1182,8 +1225,8 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
       if (!a.grad_hidden && !a.grad_weight && !a.grad_bias) continue;
       // 3'. pass 2: the logits are recomputed tile by tile and leave as bf16 probabilities in
       //     the slice (and, for grad_bias, as fp32 column sums)
-      EpiProbs e2{reinterpret_cast<uint16_t*>(ws.slice), 2 * ws.ldz, a.bias, lse_c, lse_gap, lab,
-                  v, a.ignore_index, a.grad_bias ? ws.slice : nullptr};
+      EpiProbs e2{reinterpret_cast<uint16_t*>(ws.slice), 2 * ws.ldz, 2 * kGroup, a.bias, lse_c,
+                  lse_gap, lab, v, a.ignore_index, a.grad_bias ? ws.slice : nullptr};
       {
         TimedLaunch t(s, K_FLCE_GEMM_PROBS);
         if ((e = gemm::v2::launch<Wide, true, true>(Ah, Bw, rows, ws.ldz, h, 1, true, e2, s)) !=

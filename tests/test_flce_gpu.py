@@ -174,7 +174,7 @@ def test_recompute_matches_stored_slice(dev, n, h, v, chunk, bias):
 def test_two_chunks_per_slice(dev, n, chunk):
     """The stored-logits schedule pairs chunks: an even and an odd number of chunks, a short
     last chunk alone or as the second of a pair; with grad_bias, and with an upstream gradient
-    and a caller's normaliser."""
+    and a caller's normaliser. Loss and lse are the recomputing schedule's bit for bit."""
     h, v = 128, 1500
     assert stores_16bit_logits(n, h, v, chunk)
     inp = random_flce(n, h, v, weight_sigma=0.2, bias=True, ignore_frac=0.1, seed=n + chunk)
@@ -184,6 +184,32 @@ def test_two_chunks_per_slice(dev, n, chunk):
     rec = run_flce(dev, inp, chunk, count=n - 3, g=0.75, recompute=True)
     assert res["loss"] == rec["loss"]
     assert np.array_equal(res["lse"], rec["lse"])
+
+
+@pytest.mark.parametrize("n,chunk", [(64, 64), (192, 64), (200, 64), (513, 128)])
+def test_two_chunks_per_slice_recompute(dev, n, chunk):
+    """The recomputing schedule pairs chunks too when grad_hidden rows can hold the
+    bookkeeping and no grad_bias is asked for (a bias still enters the logits): against the
+    oracle, and the split forward / backward calls bit for bit."""
+    h, v = 128, 1500
+    inp = random_flce(n, h, v, weight_sigma=0.2, bias=True, ignore_frac=0.1, seed=3 * n + chunk)
+    res = run_flce(dev, inp, chunk, count=n + 1, g=1.25, recompute=True, want_bias_grad=False)
+    assert res["gb"] is None
+    check(inp, res, count=n + 1, g=1.25)
+    hid = bits_to_device(inp.hidden, dev)
+    w = bits_to_device(inp.weight, dev)
+    lab = torch.from_numpy(inp.labels.astype(np.int32)).to(dev)
+    b = torch.from_numpy(inp.bias).to(dev)
+    gout = torch.tensor(1.25, dtype=torch.float32, device=dev)
+    loss, lse = lce.flce_fwd(hid, w, lab, b, chunk_size=chunk, num_label_tokens=n + 1)
+    gh, gw, gb = lce.flce_bwd(hid, w, lab, lse, b, chunk_size=chunk, num_label_tokens=n + 1,
+                              grad_output=gout, grad_bias=False)
+    torch.cuda.synchronize()
+    assert gb is None
+    assert float(loss.item()) == res["loss"]
+    assert np.array_equal(lse.cpu().numpy(), res["lse"])
+    assert torch.equal(gh, res["gh"])
+    assert torch.equal(gw, res["gw"])
 
 
 @pytest.mark.parametrize("n,chunk", [(150, 64), (300, 128)])
@@ -236,8 +262,9 @@ def test_one_slice_workspace_and_chunk_independent_loss(dev, recompute):
     [chunk, ldz] slice and nothing else: the bookkeeping sits in the slice's free halves and
     in grad_hidden rows not yet written. Loss and lse are bitwise the same on either side of
     that threshold (the loss is summed row by row in fp64). grad_weight asked for without
-    grad_hidden takes the recomputing passes: bitwise the one computed with grad_hidden by
-    the recomputing schedule, within the rounding budget of the stored-logits one."""
+    grad_hidden takes the recomputing passes one chunk at a time (no grad_hidden rows to
+    keep the bookkeeping of two chunks per slice): within the rounding budget of the call
+    with grad_hidden."""
     n, h, v = 333, 128, 3001
     ldz = (v + 63) // 64 * 64
     flags = lce.FLCE_RECOMPUTE if recompute else 0
@@ -259,10 +286,7 @@ def test_one_slice_workspace_and_chunk_independent_loss(dev, recompute):
     torch.cuda.synchronize()
     assert gh is None
     assert float(loss.item()) == res[100]["loss"]
-    if recompute:
-        assert torch.equal(gw, res[100]["gw"])
-    else:
-        check(inp, dict(res[100], gw=gw))
+    check(inp, dict(res[100], gw=gw))
 
 
 def test_caller_normaliser_and_upstream_grad(dev):
