@@ -54,7 +54,10 @@ void timing_start(hipStream_t stream, int id) {
   std::lock_guard<std::mutex> lk(g_mu);
   hipEvent_t e = take_event();
   if (!e) return;
-  hipEventRecord(e, stream);
+  if (hipEventRecord(e, stream) != hipSuccess) {  // this launch goes untimed
+    g_free.push_back(e);
+    return;
+  }
   g_open[id] = e;
 }
 
@@ -69,7 +72,11 @@ void timing_stop(hipStream_t stream, int id) {
     g_free.push_back(s);
     return;
   }
-  hipEventRecord(e, stream);
+  if (hipEventRecord(e, stream) != hipSuccess) {  // this launch goes untimed
+    g_free.push_back(s);
+    g_free.push_back(e);
+    return;
+  }
   g_pending.push_back(Pending{id, s, e});
 }
 
