@@ -82,8 +82,10 @@ def test_single_pass_ce_graph_replays_match_eager(dev):
         assert torch.equal(logits.view(torch.int16), ref_grad.view(torch.int16)), f"replay {k}"
 
 
-@pytest.mark.parametrize("recompute", [False, True])
-def test_flce_graph_replays_match_eager(dev, recompute):
+@pytest.mark.parametrize("recompute,bias_grad", [(False, True), (True, True), (True, False)])
+def test_flce_graph_replays_match_eager(dev, recompute, bias_grad):
+    """Both schedules with two chunks per slice (stored logits; recomputing without grad_bias)
+    and the recomputing schedule one chunk at a time (with grad_bias)."""
     inp = random_flce(333, 128, 3001, bias=True, seed=53)
     hid = bits_to_device(inp.hidden, dev)
     w = bits_to_device(inp.weight, dev)
@@ -91,7 +93,7 @@ def test_flce_graph_replays_match_eager(dev, recompute):
     lab = torch.from_numpy(inp.labels).to(dev)
     gh = torch.empty((333, 128), dtype=torch.bfloat16, device=dev)
     gw = torch.empty((3001, 128), dtype=torch.float32, device=dev)
-    gb = torch.empty(3001, dtype=torch.float32, device=dev)
+    gb = torch.empty(3001, dtype=torch.float32, device=dev) if bias_grad else False
     flags = lce.FLCE_RECOMPUTE if recompute else 0
     ws = torch.empty(lce.flce_workspace_size(333, 128, 3001, 100, flags), dtype=torch.uint8,
                      device=dev)
@@ -104,14 +106,16 @@ def test_flce_graph_replays_match_eager(dev, recompute):
 
     step()
     torch.cuda.synchronize()
-    ref = [out["loss"].clone(), gh.clone(), gw.clone(), gb.clone()]
+    outs = [gh, gw] + ([gb] if bias_grad else [])
+    ref = [out["loss"].clone()] + [t.clone() for t in outs]
     g = _capture(step, dev)
     for k in range(4):
-        for t in (gh, gw, gb):
+        for t in outs:
             t.fill_(0)
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out["loss"], ref[0]), f"replay {k}: loss"
         assert torch.equal(gh.view(torch.int16), ref[1].view(torch.int16)), f"replay {k}: gh"
         assert torch.equal(gw, ref[2]), f"replay {k}: gw"
-        assert torch.equal(gb, ref[3]), f"replay {k}: gb"
+        if bias_grad:
+            assert torch.equal(gb, ref[3]), f"replay {k}: gb"
