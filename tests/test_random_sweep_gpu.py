@@ -81,12 +81,48 @@ def test_ce_random_case(dev, c):
                                  count=c["count"], g=c["g"], ld=ld)
 
 
+def _flce_paired_cases(k=10, seed=2026):
+    """Shapes of the compact workspace (h a multiple of 64, chunks of 64 rows or more, usually
+    several of them), where two chunks share the slice; grad_bias is asked for or not, which
+    decides whether the recomputing schedule pairs chunks."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < k:
+        h = 64 * int(rng.integers(1, 6))
+        chunk = int(rng.integers(64, 200))
+        n = int(rng.integers(chunk, 4 * chunk + 1))
+        v = int(np.exp(rng.uniform(np.log(2), np.log(9000))))
+        if n * h * v > 300_000_000:
+            continue
+        bias = bool(rng.random() < 0.5)
+        out.append(dict(
+            n=n, h=h, v=v, chunk=chunk, bias=bias, bias_grad=bias and bool(rng.random() < 0.5),
+            recompute=bool(rng.random() < 0.5), ignore=float(rng.uniform(0, 0.4)),
+            count=None if rng.random() < 0.6 else int(rng.integers(1, 2 * n + 2)),
+            g=None if rng.random() < 0.6 else float(rng.normal(0, 2)),
+            wsig=float(rng.uniform(0.01, 0.2)), seed=int(rng.integers(1 << 30))))
+    return out
+
+
 @pytest.mark.parametrize("c", _flce_cases(),
                          ids=lambda c: f"n{c['n']}_h{c['h']}_v{c['v']}_c{c['chunk']}")
 def test_flce_random_case(dev, c):
+    _check_flce_case(dev, c)
+
+
+@pytest.mark.parametrize("c", _flce_paired_cases(),
+                         ids=lambda c: f"n{c['n']}_h{c['h']}_v{c['v']}_c{c['chunk']}"
+                                       f"{'_rec' if c['recompute'] else ''}"
+                                       f"{'_bias' if c['bias'] else ''}{'_gb' if c['bias_grad'] else ''}")
+def test_flce_random_paired_case(dev, c):
+    _check_flce_case(dev, c)
+
+
+def _check_flce_case(dev, c):
     inp = random_flce(c["n"], c["h"], c["v"], weight_sigma=c["wsig"], bias=c["bias"],
                       ignore_frac=c["ignore"], seed=c["seed"])
-    res = run_flce(dev, inp, c["chunk"], count=c["count"], g=c["g"], recompute=c["recompute"])
+    res = run_flce(dev, inp, c["chunk"], count=c["count"], g=c["g"], recompute=c["recompute"],
+                   want_bias_grad=c.get("bias_grad", True))
     assert res["status"] == 0
     g = 1.0 if c["g"] is None else c["g"]
     ref = oracle.flce(inp.hidden, inp.weight, inp.labels, bias=inp.bias,
@@ -102,5 +138,5 @@ def test_flce_random_case(dev, c):
                   + 1e-7 * abs(g) * ref.scale)
     ulp_h = np.ldexp(1.0, np.floor(np.log2(np.maximum(np.abs(ref.grad_hidden), 1e-30))).astype(int) - 8)
     assert np.all(np.abs(gh - ref.grad_hidden) <= bh + ulp_h + 1e-6 * np.abs(ref.grad_hidden) + 1e-9)
-    if inp.bias is not None and ref.grad_bias is not None and np.any(ref.grad_bias):
+    if res["gb"] is not None and ref.grad_bias is not None and np.any(ref.grad_bias):
         assert normwise_rel(device_to_f64(res["gb"]), ref.grad_bias) <= 1e-4
