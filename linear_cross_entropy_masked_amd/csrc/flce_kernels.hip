@@ -420,23 +420,34 @@ struct EpiPartial {
   }
 };
 
-// dH[m, n] = coef · (Σ_z partial_z[m, n] − W[y_m, n]), summed in split order; bf16 out.
+// dH[m, n] = coef · (Σ_z partial_z[m, n] − W[y_m, n]), summed in split order; bf16 out. Each
+// lane takes 4 consecutive elements (N % 4 == 0: a 16-byte read of each split's partials,
+// which stay inside one 32-float gap, 8-byte accesses to W and dH).
 __global__ void __launch_bounds__(256) grad_hidden_reduce_kernel(
     const float* __restrict__ slice, int64_t M, int64_t N, int64_t splits,
     uint16_t* __restrict__ dh, const int32_t* __restrict__ labels, const uint16_t* __restrict__ w,
     int64_t v, int32_t ignore_index, const long long* count_dev, long long count_host,
     const float* gout) {
-  const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t e = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
   if (e >= M * N) return;
   const int64_t m = e / N, n = e % N;
   const int32_t y = labels[m];
-  float r = 0.f;
+  uint2 o = {0u, 0u};
   if (has_label(y, v, ignore_index)) {
-    float acc = 0.f;
-    for (int64_t z = 0; z < splits; ++z) acc += slice[gap_index(z * M * N + e)];
-    r = flce_coef(count_dev, count_host, gout) * (acc - bf16_to_f32(w[int64_t(y) * N + n]));
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t z = 0; z < splits; ++z) {
+      const float4 p = *reinterpret_cast<const float4*>(slice + gap_index(z * M * N + e));
+      acc.x += p.x;
+      acc.y += p.y;
+      acc.z += p.z;
+      acc.w += p.w;
+    }
+    const float coef = flce_coef(count_dev, count_host, gout);
+    const uint2 wy = *reinterpret_cast<const uint2*>(w + int64_t(y) * N + n);
+    o.x = pack_bf16x2(coef * (acc.x - bf16_lo(wy.x)), coef * (acc.y - bf16_hi(wy.x)));
+    o.y = pack_bf16x2(coef * (acc.z - bf16_lo(wy.y)), coef * (acc.w - bf16_hi(wy.y)));
   }
-  dh[e] = f32_to_bf16(r);
+  *reinterpret_cast<uint2*>(dh + e) = o;
 }
 
 // ------------------------------------------------------------------ row / column passes
@@ -987,7 +998,7 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
     }
     if (splits == 1) return hipSuccess;
     TimedLaunch t(s, K_FLCE_GRAD_HIDDEN_REDUCE);
-    hipLaunchKernelGGL(grad_hidden_reduce_kernel, dim3(unsigned((rows * h + 255) / 256)),
+    hipLaunchKernelGGL(grad_hidden_reduce_kernel, dim3(unsigned((rows * h / 4 + 255) / 256)),
                        dim3(256), 0, s, other, rows, h, splits, dh, lab, a.weight, v,
                        a.ignore_index, cnt, th, a.grad_output);
     return hipGetLastError();
@@ -1277,7 +1288,7 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     }
     if (a.grad_hidden && splits > 1) {
       TimedLaunch t(s, K_FLCE_GRAD_HIDDEN_REDUCE);
-      hipLaunchKernelGGL(grad_hidden_reduce_kernel, dim3(unsigned((rows * h + 255) / 256)),
+      hipLaunchKernelGGL(grad_hidden_reduce_kernel, dim3(unsigned((rows * h / 4 + 255) / 256)),
                          dim3(256), 0, s, ws.slice, rows, h, splits, a.grad_hidden + c0 * h, lab,
                          a.weight, v, a.ignore_index, cnt, th, a.grad_output);
       if ((e = hipGetLastError()) != hipSuccess) return e;
