@@ -43,6 +43,17 @@
  *   - Return value: LCE_OK or an error code. Argument errors are reported before any device
  *     work is enqueued; LCE_ERR_HIP means a launch failed (the stream state is then the
  *     caller's to inspect).
+ *   - Aliasing: every buffer a call writes (its outputs, status_out and the workspace) must be
+ *     disjoint from every other buffer of the call, checked on the host from the pointers and
+ *     sizes (LCE_ERR_OVERLAP). The one exception is the in-place CE backward, where the
+ *     gradient occupies exactly the logits' rows (same pointer, same row stride).
+ *
+ * Where the signatures differ from the plain interface of the pages (logits, labels,
+ * num_label_tokens, chunk_size for the CE; hidden, targets, weight, bias for the fused layer),
+ * the additions are optional outputs or device-side conditions: lse_out (the per-row
+ * logsumexp, so a backward need not recompute it), status_out (out-of-range labels reported
+ * without a host synchronisation), grad_output (the chain rule's upstream factor) and the
+ * caller-provided workspace (the library never allocates).
  */
 #ifndef LCE_MASKED_H
 #define LCE_MASKED_H
@@ -64,6 +75,9 @@ extern "C" {
 #define LCE_ERR_DEVICE           6  /* the current device is not gfx950                           */
 #define LCE_ERR_BAD_FLAGS        7  /* unknown flag bits                                          */
 #define LCE_ERR_ALIGNMENT        8  /* a pointer is not aligned to its element size               */
+#define LCE_ERR_OVERLAP          9  /* an output (or the workspace) shares bytes with another
+                                       buffer of the call, other than the documented in-place
+                                       case of the CE backward                                   */
 
 /* bits of *status_out */
 #define LCE_STATUS_BAD_LABEL     1  /* some label was neither ignore_index nor in [0, V)          */
@@ -83,13 +97,17 @@ const char* flce_status_str(int status);
 
 /* ------------------------------------------------------------------ chunked CE */
 
-/* Workspace bytes needed by ce_chunked_fwd / ce_chunked_bwd* for n rows. O(n): the CE kernels
+/* Workspace bytes needed by ce_chunked_fwd / ce_chunked_bwd* for n rows. NeMo Automodel PR
+ * #2996, *Motivation*: the chunked path bounds the fp32 working set by one [chunk_size, V]
+ * slice; here it is smaller still. O(n): the CE kernels
  * stream each row through registers and never build an fp32 [chunk_size, V] slice, so the
  * size does not depend on v or chunk_size. Returns LCE_ERR_BAD_SHAPE / LCE_ERR_BAD_CHUNK /
  * LCE_ERR_NULL_ARG on bad input. Host-only; safe without a GPU. */
 int ce_chunked_workspace_size(int64_t n, int64_t v, int64_t chunk_size, size_t* bytes);
 
-/* Forward: loss_out = s · Σ_i (lse_i − z_{i,y_i}) over labelled rows.
+/* Forward: loss_out = s · Σ_i (lse_i − z_{i,y_i}) over labelled rows. NeMo Automodel PR
+ * #2996, first commit message: per-row fp32 logsumexp plus the label-logit gather,
+ * accumulated into one scalar divided by num_label_tokens (zero guard: T == 0 gives 0).
  *   logits      bf16 [n, ld] row-major, first v columns used, read only. Rows without a label
  *               are not read.
  *   labels      int32 [n]
@@ -105,10 +123,14 @@ int ce_chunked_fwd(const uint16_t* logits, int64_t n, int64_t v, int64_t ld,
                    int32_t* status_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Backward, out of place: grad[i, :] = g · s · (softmax(z_i) − onehot(y_i)) for labelled rows,
- * exactly 0 for the others; fp32 math, rounded to bf16 (nearest even).
+ * exactly 0 for the others; fp32 math, rounded to bf16 (nearest even). NeMo Automodel PR
+ * #2996, first commit message (the softmax recomputed in the backward, minus the one-hot,
+ * times 1/num_label_tokens) and seventh commit message (the logits left intact unless the
+ * caller opts in to the in-place form).
  *   logits      bf16 [n, ld] (read)
  *   grad        bf16 [n, ldg] (written, first v columns). grad == logits with ldg == ld is the
- *               in-place case; any other overlap of the two ranges is undefined.
+ *               in-place case; any other overlap of the two ranges is refused
+ *               (LCE_ERR_OVERLAP).
  *   lse         fp32 [n] from ce_chunked_fwd, or NULL to recompute each row's logsumexp
  *               (one more read of every labelled row). */
 int ce_chunked_bwd(const uint16_t* logits, int64_t n, int64_t v, int64_t ld,
@@ -166,7 +188,9 @@ int ce_rows_bwd(const uint16_t* logits, int64_t n, int64_t v, int64_t ld, uint16
 
 /* ------------------------------------------------------------------ fused linear CE */
 
-/* Workspace bytes for flce_fwd_bwd, flce_fwd and flce_bwd: one fp32 [C, V] logits slice,
+/* Workspace bytes for flce_fwd_bwd, flce_fwd and flce_bwd (NeMo Automodel PR #2996,
+ * *Motivation*, for the one-slice bound; Liger-Kernel issue #941, the reply that sizes a
+ * chunk's fp32 logits as rows · V · 4 bytes): one fp32 [C, V] logits slice,
  * C = min(chunk_size, n), rows padded to a multiple of 64 columns. The fp32 working set of
  * one chunk is that slice (NeMo Automodel PR #2996, Motivation), and with h a multiple of 64
  * and C >= 64 it is the whole workspace: the call's other state (lse, loss terms, per-tile
@@ -182,7 +206,12 @@ int ce_rows_bwd(const uint16_t* logits, int64_t n, int64_t v, int64_t ld, uint16
 int flce_workspace_size(int64_t n, int64_t h, int64_t v, int64_t chunk_size, uint32_t flags,
                         size_t* bytes);
 
-/* Fused linear CE forward + backward in one call, one chunk of rows at a time.
+/* Fused linear CE forward + backward in one call, one chunk of rows at a time. Liger-Kernel
+ * issue #533, feature pitch (per chunk: logits = input · weightᵀ, the CE gradient of those
+ * logits, grad_input, and grad_weight += gradientᵀ · input) and comments (the fully
+ * recomputed variant: FLCE_RECOMPUTE); Liger-Kernel issue #941, the opening post (the loss
+ * takes hidden states, targets, the lm_head weight and an optional bias; the lm_head weight
+ * may be tied to the embedding, which FLCE_ACCUMULATE serves).
  *   hidden       bf16 [n, h] row-major            weight  bf16 [v, h] row-major
  *   bias         fp32 [v] or NULL                 labels  int32 [n]
  *   loss_out     fp32 scalar (required)
@@ -199,7 +228,9 @@ int flce_workspace_size(int64_t n, int64_t h, int64_t v, int64_t chunk_size, uin
  * the fp32 logits. The loss adds the rows' terms in row order in fp64, so it does not
  * depend on chunk_size.
  * grad_hidden also serves as scratch before its rows are written (see flce_workspace_size):
- * it must not overlap any input, and its contents are defined only once the call has run. */
+ * its contents are defined only once the call has run, and a grad_hidden that overlaps any
+ * other buffer of the call (hidden included: there is no in-place form) is refused with
+ * LCE_ERR_OVERLAP. */
 int flce_fwd_bwd(const uint16_t* hidden, const uint16_t* weight, const float* bias,
                  const int32_t* labels, int64_t n, int64_t h, int64_t v, int32_t ignore_index,
                  int64_t chunk_size, int64_t num_label_tokens, uint32_t flags,

@@ -125,16 +125,30 @@ def _require(t, name, dtype, dims, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
-def _labels_i32(labels, n, device):
+def _labels_i32(labels, n, device, ignore_index=-100):
+    """int32 labels for the C ABI. An int64 label outside the int32 range is not a vocabulary
+    index: it becomes a negative value other than ignore_index, so the library flags it
+    (LCE_STATUS_BAD_LABEL) and treats the row as unlabelled instead of wrapping it onto a
+    class."""
     import torch
     _require(labels, "labels", None, 1, device)
     if labels.shape[0] != n:
         raise ValueError(f"labels has {labels.shape[0]} entries, expected {n}")
     if labels.dtype == torch.int64:
-        labels = labels.to(torch.int32)
+        bad = -1 if int(ignore_index) != -1 else -2
+        wide = (labels > 2 ** 31 - 1) | (labels < -(2 ** 31))
+        labels = torch.where(wide, torch.full_like(labels, bad), labels).to(torch.int32)
     elif labels.dtype != torch.int32:
         raise TypeError("labels must be int32 or int64")
     return labels.contiguous()
+
+
+def _require_lse(lse, n, device):
+    import torch
+    _require(lse, "lse", torch.float32, 1, device)
+    if lse.shape[0] != n or (n > 1 and lse.stride(0) != 1):
+        raise ValueError(f"lse must be a contiguous float32 [{n}] tensor, got shape "
+                         f"{tuple(lse.shape)} stride {tuple(lse.stride())}")
 
 
 def _workspace(nbytes, device, workspace=None):
@@ -183,7 +197,7 @@ def ce_chunked_fwd(logits, labels, *, ignore_index: int = -100, chunk_size: int 
     lib = load_library()
     n, v, ld = _logits_2d(logits)
     dev = logits.device
-    labels = _labels_i32(labels, n, dev)
+    labels = _labels_i32(labels, n, dev, ignore_index)
     nbytes = ce_chunked_workspace_size(n, v, chunk_size)
     ws = _workspace(nbytes, dev, workspace)
     loss = torch.empty((), dtype=torch.float32, device=dev)
@@ -203,7 +217,7 @@ def ce_chunked_bwd(logits, labels, *, out=None, ignore_index: int = -100, chunk_
     lib = load_library()
     n, v, ld = _logits_2d(logits)
     dev = logits.device
-    labels = _labels_i32(labels, n, dev)
+    labels = _labels_i32(labels, n, dev, ignore_index)
     if out is None:
         out = torch.empty((n, v), dtype=torch.bfloat16, device=dev)
     _require(out, "out", torch.bfloat16, 2, dev)
@@ -213,7 +227,7 @@ def ce_chunked_bwd(logits, labels, *, out=None, ignore_index: int = -100, chunk_
     if grad_output is not None:
         _require(grad_output, "grad_output", torch.float32, 0, dev)
     if lse is not None:
-        _require(lse, "lse", torch.float32, 1, dev)
+        _require_lse(lse, n, dev)
     ws = _workspace(ce_chunked_workspace_size(n, v, chunk_size), dev, workspace)
     _check("ce_chunked_bwd", lib.ce_chunked_bwd(
         _ptr(logits), n, v, ld, _ptr(out), ldg, _ptr(labels), ignore_index, chunk_size,
@@ -230,11 +244,11 @@ def ce_chunked_bwd_inplace(logits, labels, *, ignore_index: int = -100, chunk_si
     lib = load_library()
     n, v, ld = _logits_2d(logits)
     dev = logits.device
-    labels = _labels_i32(labels, n, dev)
+    labels = _labels_i32(labels, n, dev, ignore_index)
     if grad_output is not None:
         _require(grad_output, "grad_output", torch.float32, 0, dev)
     if lse is not None:
-        _require(lse, "lse", torch.float32, 1, dev)
+        _require_lse(lse, n, dev)
     ws = _workspace(ce_chunked_workspace_size(n, v, chunk_size), dev, workspace)
     _check("ce_chunked_bwd_inplace", lib.ce_chunked_bwd_inplace(
         _ptr(logits), n, v, ld, _ptr(labels), ignore_index, chunk_size,
@@ -255,7 +269,7 @@ def ce_chunked_fwd_bwd_inplace(logits, labels, *, ignore_index: int = -100,
     lib = load_library()
     n, v, ld = _logits_2d(logits)
     dev = logits.device
-    labels = _labels_i32(labels, n, dev)
+    labels = _labels_i32(labels, n, dev, ignore_index)
     if grad_output is not None:
         _require(grad_output, "grad_output", torch.float32, 0, dev)
     ws = _workspace(ce_chunked_workspace_size(n, v, chunk_size), dev, workspace)
@@ -276,7 +290,7 @@ def ce_rows_fwd(logits, labels, *, ignore_index: int = -100, chunk_size: int = 1
     lib = load_library()
     n, v, ld = _logits_2d(logits)
     dev = logits.device
-    labels = _labels_i32(labels, n, dev)
+    labels = _labels_i32(labels, n, dev, ignore_index)
     ws = _workspace(ce_chunked_workspace_size(n, v, chunk_size), dev, workspace)
     rows = torch.empty(n, dtype=torch.float32, device=dev)
     lse = torch.empty(n, dtype=torch.float32, device=dev) if return_lse else None
@@ -296,12 +310,12 @@ def ce_rows_bwd(logits, labels, grad_rows, *, out=None, inplace: bool = False,
     lib = load_library()
     n, v, ld = _logits_2d(logits)
     dev = logits.device
-    labels = _labels_i32(labels, n, dev)
+    labels = _labels_i32(labels, n, dev, ignore_index)
     _require(grad_rows, "grad_rows", torch.float32, 1, dev)
     if grad_rows.numel() != n or (n > 1 and grad_rows.stride(0) != 1):
         raise ValueError("grad_rows must be a contiguous fp32 [n] tensor")
     if lse is not None:
-        _require(lse, "lse", torch.float32, 1, dev)
+        _require_lse(lse, n, dev)
     if inplace:
         out, ldg = logits, ld
     else:
@@ -341,7 +355,7 @@ def flce_fwd_bwd(hidden, weight, labels, bias=None, *, ignore_index: int = -100,
         raise ValueError(f"hidden has {h} columns but weight has {h2}")
     hidden = hidden.contiguous()
     weight = weight.contiguous()
-    labels = _labels_i32(labels, n, dev)
+    labels = _labels_i32(labels, n, dev, ignore_index)
     if bias is not None:
         _require(bias, "bias", torch.float32, 1, dev)
         if bias.shape[0] != v:
@@ -379,7 +393,7 @@ def flce_fwd_bwd(hidden, weight, labels, bias=None, *, ignore_index: int = -100,
     return loss, gh, gw, gb, lse
 
 
-def _flce_inputs(hidden, weight, labels, bias):
+def _flce_inputs(hidden, weight, labels, bias, ignore_index):
     import torch
     _require(hidden, "hidden", torch.bfloat16, 2)
     dev = hidden.device
@@ -388,7 +402,7 @@ def _flce_inputs(hidden, weight, labels, bias):
     v, h2 = weight.shape
     if h2 != h:
         raise ValueError(f"hidden has {h} columns but weight has {h2}")
-    labels = _labels_i32(labels, n, dev)
+    labels = _labels_i32(labels, n, dev, ignore_index)
     if bias is not None:
         _require(bias, "bias", torch.float32, 1, dev)
         if bias.shape[0] != v:
@@ -403,7 +417,8 @@ def flce_fwd(hidden, weight, labels, bias=None, *, ignore_index: int = -100,
     """Fused linear CE forward only. Returns (loss, lse); keep lse for :func:`flce_bwd`."""
     import torch
     lib = load_library()
-    hidden, weight, labels, bias, dev, n, h, v = _flce_inputs(hidden, weight, labels, bias)
+    hidden, weight, labels, bias, dev, n, h, v = _flce_inputs(
+        hidden, weight, labels, bias, ignore_index)
     loss = torch.empty((), dtype=torch.float32, device=dev)
     lse = torch.empty(n, dtype=torch.float32, device=dev)
     ws = _workspace(flce_workspace_size(n, h, v, chunk_size, 0), dev, workspace)
@@ -422,7 +437,8 @@ def flce_bwd(hidden, weight, labels, lse, bias=None, *, ignore_index: int = -100
     Output arguments as in :func:`flce_fwd_bwd`. Returns (grad_hidden, grad_weight, grad_bias)."""
     import torch
     lib = load_library()
-    hidden, weight, labels, bias, dev, n, h, v = _flce_inputs(hidden, weight, labels, bias)
+    hidden, weight, labels, bias, dev, n, h, v = _flce_inputs(
+        hidden, weight, labels, bias, ignore_index)
     _require(lse, "lse", torch.float32, 1, dev)
     if lse.shape[0] != n or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous [n] float32 tensor")

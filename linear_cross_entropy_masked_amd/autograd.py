@@ -12,7 +12,8 @@ Behaviour follows NeMo Automodel PR #2996 (the masked CE loss with a chunk_size)
     once-differentiable, so a double backward raises, and after an in-place backward the
     logits' version counter is bumped, so any other autograd user of the logits fails loudly
     instead of reading the gradient as logits; a second backward through the same graph
-    (``retain_graph=True``) raises too, since the logits are gone (commit message 8);
+    (``retain_graph=True``) raises too, since the logits are gone (seventh commit message:
+    the keyword-only opt-in, the once-differentiable backward and the retain_graph hazard);
   * ``reduction``: "sum" is the method's sum over labelled rows, divided by
     ``num_label_tokens`` when it is given; "mean" divides by the number of labelled rows
     (counted on the device); "none" returns the per-row terms (0 for rows without a label).
@@ -158,17 +159,22 @@ class _LinearCE(torch.autograd.Function):
         if g.dtype != torch.float32:
             g = g.to(torch.float32)
         need_h, need_w, need_b = ctx.needs_input_grad[:3]
+        need_b = bool(need_b and bias is not None)
         to_buffer = grad_buffer is not None and need_w
         # each output: True = allocate, False = not computed, a tensor = written (or, with
-        # accumulate, added) in place
+        # accumulate, added) in place. The accumulate flag covers grad_bias too, so with the
+        # weight buffer the bias gradient is added into a zeroed tensor of its own.
+        gb_spec = need_b
+        if to_buffer and need_b:
+            gb_spec = torch.zeros(bias.shape[0], dtype=torch.float32, device=bias.device)
         gh, gw, gb = flce_bwd(
             hidden, weight, labels, lse, bias, ignore_index=ignore_index, chunk_size=chunk_size,
             num_label_tokens=count, grad_output=g, accumulate=to_buffer,
             grad_hidden=bool(need_h), grad_weight=grad_buffer if to_buffer else bool(need_w),
-            grad_bias=bool(need_b and bias is not None))
+            grad_bias=gb_spec)
         return (gh if need_h else None,
                 None if (to_buffer or not need_w) else gw,
-                gb if (need_b and bias is not None) else None,
+                gb if need_b else None,
                 None, None, None, None, None)
 
 

@@ -44,6 +44,35 @@ int ce_check_shape(int64_t n, int64_t v, int64_t ld, int64_t chunk_size) {
   return LCE_OK;
 }
 
+// Byte range [lo, hi) a call reads or writes; empty for a NULL pointer or no bytes.
+struct Span {
+  uintptr_t lo, hi;
+};
+Span span(const void* p, int64_t bytes) {
+  if (!p || bytes <= 0) return Span{0, 0};
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Span{a, a + uintptr_t(bytes)};
+}
+// Bytes of a row-major [n, ld] matrix whose first `cols` columns are used.
+int64_t matrix_bytes(int64_t n, int64_t ld, int64_t cols, int64_t elem) {
+  return n > 0 ? ((n - 1) * ld + cols) * elem : 0;
+}
+bool spans_meet(Span a, Span b) {
+  return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+// Every written range must be disjoint from every read range and from the other written
+// ranges (inputs may share memory with each other).
+template <size_t NW, size_t NR>
+int check_disjoint(const Span (&wr)[NW], const Span (&rd)[NR]) {
+  for (size_t i = 0; i < NW; ++i) {
+    for (size_t j = 0; j < NR; ++j)
+      if (spans_meet(wr[i], rd[j])) return LCE_ERR_OVERLAP;
+    for (size_t j = i + 1; j < NW; ++j)
+      if (spans_meet(wr[i], wr[j])) return LCE_ERR_OVERLAP;
+  }
+  return LCE_OK;
+}
+
 #define LCE_TRY_HIP(expr)                        \
   do {                                           \
     if ((expr) != hipSuccess) return LCE_ERR_HIP; \
@@ -64,6 +93,7 @@ const char* lce_status_str(int status) {
     case LCE_ERR_DEVICE: return "the current device is not gfx950 (MI355X)";
     case LCE_ERR_BAD_FLAGS: return "unknown flag bits";
     case LCE_ERR_ALIGNMENT: return "a pointer is not aligned to its element size";
+    case LCE_ERR_OVERLAP: return "an output or the workspace overlaps another buffer of the call";
     default: return "unknown status";
   }
 }
@@ -89,6 +119,12 @@ int ce_chunked_fwd(const uint16_t* logits, int64_t n, int64_t v, int64_t ld,
   if (!aligned(logits, 2) || !aligned(labels, 4) || !aligned(loss_out, 4) ||
       !aligned(lse_out, 4) || !aligned(status_out, 4) || !aligned(workspace, 256))
     return LCE_ERR_ALIGNMENT;
+  {
+    const Span wr[] = {span(workspace, int64_t(lce::ce_workspace_bytes(n))), span(loss_out, 4),
+                       span(lse_out, 4 * n), span(status_out, 4)};
+    const Span rd[] = {span(logits, matrix_bytes(n, ld, v, 2)), span(labels, 4 * n)};
+    if ((rc = check_disjoint(wr, rd)) != LCE_OK) return rc;
+  }
   if ((rc = check_device()) != LCE_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   CeWorkspace ws = lce::ce_workspace_carve(workspace, n);
@@ -113,6 +149,15 @@ int ce_chunked_bwd(const uint16_t* logits, int64_t n, int64_t v, int64_t ld, uin
       !aligned(grad_output, 4) || !aligned(lse, 4) || !aligned(status_out, 4) ||
       !aligned(workspace, 256))
     return LCE_ERR_ALIGNMENT;
+  {
+    // grad == logits with ldg == ld is the in-place case; any other overlap is refused
+    const bool inplace = grad == logits && ldg == ld;
+    const Span wr[] = {span(workspace, int64_t(lce::ce_workspace_bytes(n))), span(status_out, 4),
+                       span(grad, matrix_bytes(n, ldg, v, 2))};
+    const Span rd[] = {span(inplace ? nullptr : logits, matrix_bytes(n, ld, v, 2)),
+                       span(labels, 4 * n), span(grad_output, 4), span(lse, 4 * n)};
+    if ((rc = check_disjoint(wr, rd)) != LCE_OK) return rc;
+  }
   if ((rc = check_device()) != LCE_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   CeWorkspace ws = lce::ce_workspace_carve(workspace, n);
@@ -146,6 +191,13 @@ int ce_chunked_fwd_bwd_inplace(uint16_t* logits_inout, int64_t n, int64_t v, int
       !aligned(loss_out, 4) || !aligned(lse_out, 4) || !aligned(status_out, 4) ||
       !aligned(workspace, 256))
     return LCE_ERR_ALIGNMENT;
+  {
+    const Span wr[] = {span(workspace, int64_t(lce::ce_workspace_bytes(n))), span(loss_out, 4),
+                       span(lse_out, 4 * n), span(status_out, 4),
+                       span(logits_inout, matrix_bytes(n, ld, v, 2))};
+    const Span rd[] = {span(labels, 4 * n), span(grad_output, 4)};
+    if ((rc = check_disjoint(wr, rd)) != LCE_OK) return rc;
+  }
   if ((rc = check_device()) != LCE_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   CeWorkspace ws = lce::ce_workspace_carve(workspace, n);
@@ -177,6 +229,12 @@ int ce_rows_fwd(const uint16_t* logits, int64_t n, int64_t v, int64_t ld, const 
   if (!aligned(logits, 2) || !aligned(labels, 4) || !aligned(row_loss_out, 4) ||
       !aligned(lse_out, 4) || !aligned(status_out, 4) || !aligned(workspace, 256))
     return LCE_ERR_ALIGNMENT;
+  {
+    const Span wr[] = {span(workspace, int64_t(lce::ce_workspace_bytes(n))),
+                       span(row_loss_out, 4 * n), span(lse_out, 4 * n), span(status_out, 4)};
+    const Span rd[] = {span(logits, matrix_bytes(n, ld, v, 2)), span(labels, 4 * n)};
+    if ((rc = check_disjoint(wr, rd)) != LCE_OK) return rc;
+  }
   if ((rc = check_device()) != LCE_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   CeWorkspace ws = lce::ce_workspace_carve(workspace, n);
@@ -198,6 +256,14 @@ int ce_rows_bwd(const uint16_t* logits, int64_t n, int64_t v, int64_t ld, uint16
   if (!aligned(logits, 2) || !aligned(grad, 2) || !aligned(labels, 4) || !aligned(grad_rows, 4) ||
       !aligned(lse, 4) || !aligned(status_out, 4) || !aligned(workspace, 256))
     return LCE_ERR_ALIGNMENT;
+  {
+    const bool inplace = grad == logits && ldg == ld;
+    const Span wr[] = {span(workspace, int64_t(lce::ce_workspace_bytes(n))), span(status_out, 4),
+                       span(grad, matrix_bytes(n, ldg, v, 2))};
+    const Span rd[] = {span(inplace ? nullptr : logits, matrix_bytes(n, ld, v, 2)),
+                       span(labels, 4 * n), span(grad_rows, 4 * n), span(lse, 4 * n)};
+    if ((rc = check_disjoint(wr, rd)) != LCE_OK) return rc;
+  }
   if ((rc = check_device()) != LCE_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   CeWorkspace ws = lce::ce_workspace_carve(workspace, n);
@@ -233,6 +299,16 @@ int flce_fwd_bwd(const uint16_t* hidden, const uint16_t* weight, const float* bi
       !aligned(grad_hidden, 16) || !aligned(grad_weight, 16) || !aligned(grad_bias, 4) ||
       !aligned(status_out, 4) || !aligned(workspace, 256))
     return LCE_ERR_ALIGNMENT;
+  {
+    // grad_hidden and the workspace are scratch during the call: nothing may share them
+    const Span wr[] = {span(workspace, int64_t(lce::flce_workspace_bytes(n, h, v, chunk_size, flags))),
+                       span(grad_hidden, 2 * n * h), span(grad_weight, 4 * v * h),
+                       span(grad_bias, 4 * v), span(loss_out, 4), span(lse_out, 4 * n),
+                       span(status_out, 4)};
+    const Span rd[] = {span(hidden, 2 * n * h), span(weight, 2 * v * h), span(bias, 4 * v),
+                       span(labels, 4 * n), span(grad_output, 4)};
+    if ((rc = check_disjoint(wr, rd)) != LCE_OK) return rc;
+  }
   if ((rc = check_device()) != LCE_OK) return rc;
   lce::FlceArgs a{hidden, weight, bias, labels, n, h, v, ignore_index, chunk_size,
                   num_label_tokens, flags, grad_output, loss_out, lse_out, grad_hidden,
@@ -253,6 +329,13 @@ int flce_fwd(const uint16_t* hidden, const uint16_t* weight, const float* bias,
       !aligned(loss_out, 4) || !aligned(lse_out, 4) || !aligned(status_out, 4) ||
       !aligned(workspace, 256))
     return LCE_ERR_ALIGNMENT;
+  {
+    const Span wr[] = {span(workspace, int64_t(lce::flce_workspace_bytes(n, h, v, chunk_size, 0))),
+                       span(loss_out, 4), span(lse_out, 4 * n), span(status_out, 4)};
+    const Span rd[] = {span(hidden, 2 * n * h), span(weight, 2 * v * h), span(bias, 4 * v),
+                       span(labels, 4 * n)};
+    if ((rc = check_disjoint(wr, rd)) != LCE_OK) return rc;
+  }
   if ((rc = check_device()) != LCE_OK) return rc;
   lce::FlceArgs a{hidden, weight, bias, labels, n, h, v, ignore_index, chunk_size,
                   num_label_tokens, 0, nullptr, loss_out, lse_out, nullptr, nullptr, nullptr,
@@ -278,6 +361,14 @@ int flce_bwd(const uint16_t* hidden, const uint16_t* weight, const float* bias,
       !aligned(grad_weight, 16) || !aligned(grad_bias, 4) || !aligned(status_out, 4) ||
       !aligned(workspace, 256))
     return LCE_ERR_ALIGNMENT;
+  {
+    const Span wr[] = {span(workspace, int64_t(lce::flce_workspace_bytes(n, h, v, chunk_size, flags))),
+                       span(grad_hidden, 2 * n * h), span(grad_weight, 4 * v * h),
+                       span(grad_bias, 4 * v), span(status_out, 4)};
+    const Span rd[] = {span(hidden, 2 * n * h), span(weight, 2 * v * h), span(bias, 4 * v),
+                       span(labels, 4 * n), span(lse, 4 * n), span(grad_output, 4)};
+    if ((rc = check_disjoint(wr, rd)) != LCE_OK) return rc;
+  }
   if ((rc = check_device()) != LCE_OK) return rc;
   lce::FlceArgs a{hidden, weight, bias, labels, n, h, v, ignore_index, chunk_size,
                   num_label_tokens, flags, grad_output, nullptr, nullptr, grad_hidden,

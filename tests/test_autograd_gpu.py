@@ -179,23 +179,34 @@ def test_linear_ce_matches_fused_call(dev, bias):
         assert np.linalg.norm(got - ref.grad_bias) <= 1e-4 * np.linalg.norm(ref.grad_bias)
 
 
-def test_linear_ce_fp32_grad_buffer_accumulates(dev):
-    inp = random_flce(64, 64, 517, seed=41)
-    hid, w, _ = _flce_leaves(inp, dev)
+@pytest.mark.parametrize("bias", [False, True])
+def test_linear_ce_fp32_grad_buffer_accumulates(dev, bias):
+    """weight_grad_buffer takes the fp32 weight gradient (added to what it holds); a bias that
+    requires grad still gets its own gradient, not added to anything stale."""
+    inp = random_flce(64, 64, 517, bias=bias, seed=41)
+    hid, w, b = _flce_leaves(inp, dev)
     lab = torch.from_numpy(inp.labels).to(dev)
     buf = torch.full(tuple(w.shape), 0.25, dtype=torch.float32, device=dev)
-    loss = ag.linear_cross_entropy(hid, w, lab, weight_grad_buffer=buf, num_label_tokens=100)
+    loss = ag.linear_cross_entropy(hid, w, lab, b, weight_grad_buffer=buf, num_label_tokens=100)
     (3.0 * loss).backward()
     assert w.grad is None, "with a buffer the weight gradient goes only into the buffer"
     g = torch.tensor(3.0, dtype=torch.float32, device=dev)
+    bd = None if b is None else b.detach()
     _, gw, _ = lce.flce_bwd(hid.detach(), w.detach(), lab,
-                            lce.flce_fwd(hid.detach(), w.detach(), lab, num_label_tokens=100)[1],
-                            num_label_tokens=100, grad_output=g, grad_hidden=False)
+                            lce.flce_fwd(hid.detach(), w.detach(), lab, bd,
+                                         num_label_tokens=100)[1],
+                            bd, num_label_tokens=100, grad_output=g, grad_hidden=False,
+                            grad_bias=False)
     assert torch.allclose(buf, gw + 0.25, rtol=0, atol=1e-6)
     ref = oracle.flce(oracle.bf16_bits_to_f64(inp.hidden), oracle.bf16_bits_to_f64(inp.weight),
-                      inp.labels, None, num_label_tokens=100, grad_output=3.0)
+                      inp.labels, None if inp.bias is None else inp.bias.astype(np.float64),
+                      num_label_tokens=100, grad_output=3.0)
     got = buf.double().cpu().numpy() - 0.25
     assert np.linalg.norm(got - ref.grad_weight) <= 1e-4 * np.linalg.norm(ref.grad_weight)
+    if bias:
+        assert b.grad is not None and b.grad.dtype == torch.float32
+        gotb = device_to_f64(b.grad)
+        assert np.linalg.norm(gotb - ref.grad_bias) <= 1e-4 * np.linalg.norm(ref.grad_bias)
 
 
 def test_interface_aliases_vs_oracle(dev):

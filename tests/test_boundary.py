@@ -17,7 +17,7 @@ import linear_cross_entropy_masked_amd as lce
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-OK, NULL_ARG, BAD_SHAPE, BAD_CHUNK, WORKSPACE, HIP, DEVICE, BAD_FLAGS, ALIGN = range(9)
+OK, NULL_ARG, BAD_SHAPE, BAD_CHUNK, WORKSPACE, HIP, DEVICE, BAD_FLAGS, ALIGN, OVERLAP = range(10)
 
 
 def _declared_functions():
@@ -45,8 +45,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(9):
-        assert lce.lce_status_str(code)
+    for code in range(10):
+        assert lce.lce_status_str(code) != lce.lce_status_str(12345)
     assert lce.lce_status_str(0) == "ok"
     assert "unknown" in lce.lce_status_str(12345)
 
@@ -69,6 +69,9 @@ def test_ce_workspace_size_is_small_and_validated(lib):
 
 
 FAKE = 0x10000  # a 256-aligned non-null address; never dereferenced (validation fails first)
+# distinct 256-aligned fake buffers, 256 MiB apart, for calls whose arguments must pass the
+# overlap check
+A1, A2, A3, A4, A5, A6, A7, A8, A9, A10, A11, A12 = (0x10000000 * (k + 1) for k in range(12))
 
 
 AT_DEVICE_CHECK = (HIP, DEVICE)
@@ -128,7 +131,7 @@ def test_ce_fused_argument_errors(lib):
     assert _fused(labels=None) == NULL_ARG
     assert _fused(loss=None) == NULL_ARG
     if _no_gpu():  # n == 0 needs no rows: accepted, then stopped at the device check
-        assert _fused(n=0, logits=None, labels=None) in AT_DEVICE_CHECK
+        assert _fused(n=0, logits=None, labels=None, loss=A1, ws=A2) in AT_DEVICE_CHECK
     assert _fused(ws=None) == WORKSPACE
     assert _fused(wsb=16) == WORKSPACE
     assert _fused(logits=FAKE + 1) == ALIGN
@@ -139,7 +142,7 @@ def test_ce_fused_argument_errors(lib):
 def test_ce_rows_argument_errors(lib):
     f, b = lib.ce_rows_fwd, lib.ce_rows_bwd
     if _no_gpu():
-        assert f(FAKE, 4, 8, 8, FAKE, -100, 2, FAKE, None, None, FAKE, 1 << 20, None) in AT_DEVICE_CHECK
+        assert f(A1, 4, 8, 8, A2, -100, 2, A3, None, None, A4, 1 << 20, None) in AT_DEVICE_CHECK
     assert f(FAKE, 4, 8, 8, FAKE, -100, 2, None, None, None, FAKE, 1 << 20, None) == NULL_ARG
     assert f(FAKE, 4, 0, 8, FAKE, -100, 2, FAKE, None, None, FAKE, 1 << 20, None) == BAD_SHAPE
     assert f(FAKE, 4, 8, 8, FAKE, -100, 0, FAKE, None, None, FAKE, 1 << 20, None) == BAD_CHUNK
@@ -227,7 +230,8 @@ def test_flce_split_argument_errors(lib):
     assert cf(lse=None) == NULL_ARG                  # the backward needs it
     assert cf(loss=None) == NULL_ARG
     if _no_gpu():
-        assert cf(n=0, hidden=None, labels=None, lse=None) in AT_DEVICE_CHECK
+        assert cf(n=0, hidden=None, labels=None, lse=None, weight=A1, loss=A2,
+                  ws=A3) in AT_DEVICE_CHECK
     assert cf(h=12) == BAD_SHAPE
     assert cf(chunk=0) == BAD_CHUNK
     assert cf(wsb=64) == WORKSPACE
@@ -247,3 +251,77 @@ def test_flce_split_argument_errors(lib):
     assert cb(h=12) == BAD_SHAPE
     assert cb(ws=None) == WORKSPACE
     assert cb(gw=FAKE + 4) == ALIGN
+
+
+# ---- aliasing: every buffer a call writes must be disjoint from the call's other buffers ----
+
+def test_ce_overlapping_buffers_are_refused(lib):
+    n, v = 4, 8
+    fwd = lib.ce_chunked_fwd
+    # workspace inside the logits, the loss inside the labels, lse over the workspace
+    assert fwd(A1, n, v, v, A2, -100, 2, -1, A3, None, None, A1, 1 << 20, None) == OVERLAP
+    assert fwd(A1, n, v, v, A2, -100, 2, -1, A2 + 4, None, None, A4, 1 << 20, None) == OVERLAP
+    assert fwd(A1, n, v, v, A2, -100, 2, -1, A3, A4, None, A4, 1 << 20, None) == OVERLAP
+    if _no_gpu():
+        assert fwd(A1, n, v, v, A2, -100, 2, -1, A3, A5, A6, A4, 1 << 20, None) in AT_DEVICE_CHECK
+    bwd = lib.ce_chunked_bwd
+    # the gradient one row into the logits (same stride, different start): refused; exactly
+    # the logits rows: the in-place case
+    assert bwd(A1, n, v, v, A1 + 2 * v, v, A2, -100, 2, -1, None, None, None, A4, 1 << 20,
+               None) == OVERLAP
+    assert bwd(A1, n, v, 16, A1, 8, A2, -100, 2, -1, None, None, None, A4, 1 << 20,
+               None) == OVERLAP  # same start, different row stride
+    assert bwd(A1, n, v, v, A5, v, A2, -100, 2, -1, None, A5 + 8, None, A4, 1 << 20,
+               None) == OVERLAP  # lse inside the gradient
+    if _no_gpu():
+        assert bwd(A1, n, v, v, A1, v, A2, -100, 2, -1, None, A3, None, A4, 1 << 20,
+                   None) in AT_DEVICE_CHECK
+        assert lib.ce_chunked_bwd_inplace(A1, n, v, v, A2, -100, 2, -1, None, A3, None, A4,
+                                          1 << 20, None) in AT_DEVICE_CHECK
+    fused = lib.ce_chunked_fwd_bwd_inplace
+    assert fused(A1, n, v, v, A2, -100, 2, -1, None, A1 + 4, None, None, A4, 1 << 20,
+                 None) == OVERLAP  # the loss inside the logits it overwrites
+    assert fused(A1, n, v, v, A2, -100, 2, -1, A4 + 8, A3, None, None, A4, 1 << 20,
+                 None) == OVERLAP  # the upstream gradient inside the workspace
+    rows_f, rows_b = lib.ce_rows_fwd, lib.ce_rows_bwd
+    assert rows_f(A1, n, v, v, A2, -100, 2, A2, None, None, A4, 1 << 20, None) == OVERLAP
+    assert rows_b(A1, n, v, v, A5, v, A2, -100, 2, A5 + 4, None, None, A4, 1 << 20,
+                  None) == OVERLAP  # grad_rows inside the gradient
+
+
+def _flce_args(**kw):
+    a = dict(hidden=A1, weight=A2, bias=None, labels=A3, n=4, h=16, v=10, ign=-100, chunk=2,
+             t=-1, flags=0, gout=None, loss=A4, lse=None, gh=A5, gw=A6, gb=None, status=None,
+             ws=A7, wsb=1 << 22, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+def test_flce_overlapping_buffers_are_refused(lib):
+    f = lib.flce_fwd_bwd
+    # grad_hidden as scratch: never the hidden rows (no in-place form), never another buffer
+    assert f(*_flce_args(gh=A1)) == OVERLAP
+    assert f(*_flce_args(gh=A1 + 64)) == OVERLAP
+    assert f(*_flce_args(gh=A2 + 16)) == OVERLAP
+    assert f(*_flce_args(gh=A3)) == OVERLAP
+    assert f(*_flce_args(bias=A8, gh=A8)) == OVERLAP
+    assert f(*_flce_args(gh=A7 + 256)) == OVERLAP     # inside the workspace
+    assert f(*_flce_args(gw=A5 + 16 * 2)) == OVERLAP   # grad_weight over grad_hidden
+    assert f(*_flce_args(ws=A2)) == OVERLAP            # the workspace over the weight
+    assert f(*_flce_args(loss=A5 + 4)) == OVERLAP
+    assert f(*_flce_args(lse=A1 + 4)) == OVERLAP
+    assert f(*_flce_args(status=A6)) == OVERLAP
+    assert f(*_flce_args(gout=A6 + 8)) == OVERLAP
+    if _no_gpu():
+        assert f(*_flce_args(bias=A8, gb=A9, lse=A10, status=A11, gout=A12)) in AT_DEVICE_CHECK
+    fwd = lib.flce_fwd
+    assert fwd(A1, A2, None, A3, 4, 16, 10, -100, 2, -1, A4, A1 + 8, None, A7, 1 << 22,
+               None) == OVERLAP  # lse inside hidden
+    bwd = lib.flce_bwd
+    base = [A1, A2, None, A3, A4, 4, 16, 10, -100, 2, -1, 0, None, A5, A6, None, None, A7,
+            1 << 22, None]
+    if _no_gpu():
+        assert bwd(*base) in AT_DEVICE_CHECK
+    hit = list(base)
+    hit[13] = A4  # grad_hidden over the saved lse
+    assert bwd(*hit) == OVERLAP

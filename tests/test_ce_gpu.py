@@ -11,10 +11,10 @@ import torch
 
 import linear_cross_entropy_masked_amd as lce
 import oracle
-from workloads import WORKLOADS, make_ce_inputs, random_ce
+from workloads import WORKLOADS, make_ce_inputs, random_ce, random_flce
 
-from _helpers import (assert_close_rel, assert_faithful_bf16, bits_to_device, device_to_f64,
-                      gpu_device, oracle_ce_rows_parallel)
+from _helpers import (assert_close_rel, assert_faithful_bf16, bf16_ulp, bits_to_device,
+                      device_to_f64, gpu_device, oracle_ce_rows_parallel)
 
 pytestmark = pytest.mark.gpu
 
@@ -172,10 +172,42 @@ def test_out_of_range_labels_flagged_and_ignored(dev):
     assert ref.bad_label and ref.count == 8
 
 
+def all_rows_invariants(grad, labels, count, rows_per_copy=512):
+    """Every row of a [n, v] bf16 gradient, checked on the host block by block: rows without
+    a label exactly zero; for a labelled row the exact gradient sums to zero (softmax minus
+    one-hot), so |Σ_v g_v| can only be the rounding of its elements: at most Σ_v ½ ulp(g_v)
+    (round to nearest) plus fp32 slack. (A fixed bar such as |Σ_v T·g| <= 4e-3 is not a
+    bound: rounding the oracle's exact gradient to nearest already reaches 4.3e-3 at the
+    [16384, 128256] statistics.) Returns the largest |Σ_v T·g| and the largest ratio of
+    |Σ_v g| to its bound."""
+    n = grad.shape[0]
+    ok = labels != -100
+    worst = ratio = 0.0
+    for r0 in range(0, n, rows_per_copy):
+        r1 = min(n, r0 + rows_per_copy)
+        blk = grad[r0:r1].view(torch.int16).cpu().numpy()
+        g = oracle.bf16_bits_to_f64(blk)
+        okb = ok[r0:r1]
+        assert not g[~okb].any(), f"a row without a label is nonzero in rows {r0}..{r1}"
+        gl = g[okb]
+        if not gl.size:
+            continue
+        sums = np.abs(gl.sum(axis=1))
+        bound = 0.5 * bf16_ulp(gl).sum(axis=1) + 2.0 ** -20 * np.abs(gl).sum(axis=1)
+        bad = sums > bound
+        assert not bad.any(), (r0 + np.nonzero(okb)[0][np.argmax(bad)], sums.max(), bound.min())
+        worst = max(worst, float(sums.max()) * count)
+        ratio = max(ratio, float((sums / np.maximum(bound, 1e-300)).max()))
+    return worst, ratio
+
+
 @pytest.mark.timeout(600)
 def test_large_vocab_workload_full_size(dev):
     """[16384, 128256] in the launch configuration the benchmark times: full loss and every
-    row's lse against the oracle, plus the complete gradient of sampled rows."""
+    row's lse against the oracle; every row of the gradient checked on the host (zero rows
+    without a label, rows of labelled tokens summing to zero within rounding); 512 and more
+    complete gradient rows (random, spiked, ignored, first and last) within one bf16 ulp of
+    the oracle, element by element."""
     w = WORKLOADS["ce_16384x128256"]
     inp = make_ce_inputs(w, seed=0)
     labels = inp.labels
@@ -187,10 +219,13 @@ def test_large_vocab_workload_full_size(dev):
     assert_close_rel(loss, math.fsum(row_loss) / count, 1e-5)
     ok = labels != -100
     assert np.all(np.abs(lse[ok] - ref_lse[ok]) <= 2e-6 * np.abs(ref_lse[ok]))
+    assert not lse[~ok].any()
+    worst, ratio = all_rows_invariants(grad, labels, count)
     rng = np.random.default_rng(0)
     rows = np.unique(np.concatenate([
-        [0, w.n - 1], rng.choice(w.n, 24, replace=False), inp.draw.spike_rows[:8],
-        inp.draw.ignored_rows[:4]]))
+        [0, w.n - 1], rng.choice(w.n, 512, replace=False), inp.draw.spike_rows[:32],
+        inp.draw.ignored_rows[:16]]))
+    assert rows.size >= 512
     got = device_to_f64(grad[torch.from_numpy(rows).to(dev)])
     for k, r in enumerate(rows):
         z = oracle.bf16_bits_to_f64(inp.logits[r:r + 1])
@@ -198,6 +233,9 @@ def test_large_vocab_workload_full_size(dev):
         assert_faithful_bf16(got[k:k + 1], one.grad, what=f"grad row {r}")
         if labels[r] == -100:
             assert not got[k].any()
+    print(f"\n[{w.name}] max |sum_v T*g| over all labelled rows {worst:.3e} "
+          f"(largest fraction of its rounding bound {ratio:.3f}); {rows.size} rows within one "
+          f"bf16 ulp")
 
 
 # ---- single pass (ce_chunked_fwd_bwd_inplace) --------------------------------------------
@@ -288,5 +326,61 @@ def test_fused_large_vocab_workload_full_size(dev):
     (whose values the full-size two-pass test pins to the oracle)."""
     w = WORKLOADS["ce_16384x128256"]
     inp = make_ce_inputs(w, seed=0)
-    _, _, _, status = assert_fused_equals_two_pass(dev, inp.logits, inp.labels, chunk=w.chunk_size)
+    _, _, grad, status = assert_fused_equals_two_pass(dev, inp.logits, inp.labels,
+                                                      chunk=w.chunk_size)
     assert status == 0
+    all_rows_invariants(grad, inp.labels, int((inp.labels != -100).sum()))
+
+
+def test_binding_rejects_short_or_strided_lse(dev):
+    """The CE backward bindings pass lse to the kernels as a plain [n] array: a shorter or
+    strided tensor is refused before any launch."""
+    inp = random_ce(8, 100, seed=30)
+    logits = bits_to_device(inp.logits, dev)
+    lab = torch.from_numpy(inp.labels).to(dev)
+    short = torch.zeros(7, dtype=torch.float32, device=dev)
+    strided = torch.zeros(16, dtype=torch.float32, device=dev)[::2]
+    grad_rows = torch.ones(8, dtype=torch.float32, device=dev)
+    for lse in (short, strided):
+        with pytest.raises(ValueError):
+            lce.ce_chunked_bwd(logits, lab, lse=lse)
+        with pytest.raises(ValueError):
+            lce.ce_chunked_bwd_inplace(logits, lab, lse=lse)
+        with pytest.raises(ValueError):
+            lce.ce_rows_bwd(logits, lab, grad_rows, lse=lse)
+
+
+def test_int64_labels_outside_int32_are_flagged_not_wrapped(dev):
+    """An int64 label such as 2**32 + 5 is not class 5: the binding keeps it out of range, so
+    the row is unlabelled and the status bit is set (both layers)."""
+    inp = random_ce(10, 100, seed=31, ignore_frac=0.0)
+    lab64 = torch.from_numpy(inp.labels.astype(np.int64))
+    lab64[3] = 2 ** 32 + 5
+    lab64[6] = -(2 ** 33)
+    ref_labels = inp.labels.copy()
+    ref_labels[3] = 100   # any out-of-range label: the oracle flags it and ignores the row
+    ref_labels[6] = -7
+    for ignore_index in (-100, -1):
+        status = torch.full((), -1, dtype=torch.int32, device=dev)
+        logits = bits_to_device(inp.logits, dev)
+        loss, lse = lce.ce_chunked_fwd(logits, lab64.to(dev), ignore_index=ignore_index,
+                                       status=status)
+        torch.cuda.synchronize()
+        assert int(status.item()) & lce.LCE_STATUS_BAD_LABEL
+        ref = oracle.ce_masked_sum(oracle.bf16_bits_to_f64(inp.logits), ref_labels,
+                                   ignore_index=ignore_index)
+        assert ref.count == 8
+        assert_close_rel(float(loss.item()), ref.loss, 1e-5)
+    f = random_flce(12, 16, 50, seed=32, ignore_frac=0.0)
+    fl = torch.from_numpy(f.labels.astype(np.int64))
+    fl[2] = 2 ** 31
+    status = torch.full((), -1, dtype=torch.int32, device=dev)
+    loss, gh, _, _, _ = lce.flce_fwd_bwd(bits_to_device(f.hidden, dev), bits_to_device(f.weight, dev),
+                                         fl.to(dev), status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & lce.LCE_STATUS_BAD_LABEL
+    assert not gh[2].any().item()
+    ref_l = f.labels.copy()
+    ref_l[2] = 50
+    r = oracle.flce(f.hidden, f.weight, ref_l)
+    assert_close_rel(float(loss.item()), r.loss, 1e-5)

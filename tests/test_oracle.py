@@ -232,6 +232,28 @@ def test_blocked_bits_version_matches_dense():
     np.testing.assert_array_equal(dense.grad[rows], blk.grad)
 
 
+def test_blocked_bits_version_upstream_grad_and_normaliser_vs_torch():
+    """The row-block reader with an upstream gradient g != 1, a caller's T different from the
+    count, and a row selection that includes ignored rows: pinned to torch's fp64
+    cross_entropy (sum reduction) and its autograd on the CPU, not to the dense oracle."""
+    from workloads import random_ce
+    inp = random_ce(300, 517, sigma=3.0, ignore_frac=0.1, seed=4)
+    z = oracle.bf16_bits_to_f64(inp.logits)
+    t, g_out = 777, -1.75
+    zt = torch.tensor(z, dtype=torch.float64, requires_grad=True)
+    yt = torch.tensor(inp.labels.astype(np.int64))
+    lt = F.cross_entropy(zt, yt, ignore_index=-100, reduction="sum") / t
+    (lt * g_out).backward()
+    ignored = np.nonzero(inp.labels == -100)[0]
+    rows = np.array([0, 5, 299, 150, int(ignored[0]), int(ignored[-1])])
+    blk = oracle.ce_masked_sum_bits(inp.logits, inp.labels, num_label_tokens=t,
+                                    grad_output=g_out, grad_rows=rows, row_block=37)
+    assert blk.count == t and blk.scale == 1.0 / t
+    assert math.isclose(blk.loss, lt.item(), rel_tol=1e-13)
+    np.testing.assert_allclose(blk.grad, zt.grad.numpy()[rows], rtol=1e-11, atol=1e-18)
+    assert not blk.grad[-2:].any()
+
+
 # ---------------------------------------------------------------- FLCE pins
 
 
