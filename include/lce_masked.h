@@ -78,6 +78,7 @@ extern "C" {
 #define LCE_ERR_OVERLAP          9  /* an output (or the workspace) shares bytes with another
                                        buffer of the call, other than the documented in-place
                                        case of the CE backward                                   */
+#define LCE_ERR_SCRATCH_LIMIT   10  /* n > LCE_NOALLOC_MAX_ROWS (allocation-free call only)      */
 
 /* bits of *status_out */
 #define LCE_STATUS_BAD_LABEL     1  /* some label was neither ignore_index nor in [0, V)          */
@@ -168,6 +169,26 @@ int ce_chunked_fwd_bwd_inplace(uint16_t* logits_inout, int64_t n, int64_t v, int
                                int64_t num_label_tokens, const float* grad_output,
                                float* loss_out, float* lse_out, int32_t* status_out,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Rows the allocation-free call below can take: its static scratch is a 256-byte header and
+ * one fp32 term per row, 256 + 4 · LCE_NOALLOC_MAX_ROWS bytes (4 MiB + 256 B) per GPU. */
+#define LCE_NOALLOC_MAX_ROWS 1048576
+
+/* ce_chunked_fwd_bwd_inplace without a workspace argument, for callers that cannot allocate
+ * device memory around the call (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). The library keeps the step's O(n) workspace in a static device
+ * array of fixed size, one per GPU, held until the process ends; the call itself allocates
+ * and frees nothing. Every other argument, every result and every error code is that of
+ * ce_chunked_fwd_bwd_inplace (bit for bit the same kernels and values), plus
+ * LCE_ERR_SCRATCH_LIMIT when n > LCE_NOALLOC_MAX_ROWS. All calls on one GPU share its array:
+ * calls that may run at the same time on one GPU (different streams, or different host
+ * threads without ordering) race on it and must be serialised by the caller; calls ordered
+ * on one stream are safe. */
+int ce_chunked_fwd_bwd_inplace_noalloc(uint16_t* logits_inout, int64_t n, int64_t v, int64_t ld,
+                                       const int32_t* labels, int32_t ignore_index,
+                                       int64_t chunk_size, int64_t num_label_tokens,
+                                       const float* grad_output, float* loss_out,
+                                       float* lse_out, int32_t* status_out, void* stream);
 
 /* Unreduced loss (the per-row terms before the sum of NeMo Automodel PR #2996, first commit
  * message; a framework's reduction="none"). No normaliser T is involved.

@@ -18,7 +18,8 @@ import os
 __all__ = [
     "LceError", "library_path", "load_library",
     "ce_chunked_workspace_size", "ce_chunked_fwd", "ce_chunked_bwd", "ce_chunked_bwd_inplace",
-    "ce_chunked_fwd_bwd_inplace", "ce_rows_fwd", "ce_rows_bwd",
+    "ce_chunked_fwd_bwd_inplace", "ce_chunked_fwd_bwd_inplace_noalloc", "ce_rows_fwd",
+    "ce_rows_bwd", "LCE_NOALLOC_MAX_ROWS",
     "flce_workspace_size", "flce_fwd_bwd", "flce_fwd", "flce_bwd", "lce_status_str",
     "flce_status_str",
     "FLCE_RECOMPUTE", "FLCE_ACCUMULATE", "LCE_STATUS_BAD_LABEL",
@@ -28,6 +29,7 @@ __all__ = [
 FLCE_RECOMPUTE = 1
 FLCE_ACCUMULATE = 2
 LCE_STATUS_BAD_LABEL = 1
+LCE_NOALLOC_MAX_ROWS = 1 << 20  # rows the allocation-free CE step's static scratch holds
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -65,6 +67,8 @@ def load_library() -> ctypes.CDLL:
         "ce_chunked_bwd_inplace": (ctypes.c_int, [vp, i64, i64, i64, vp, i32, i64, i64, vp, vp, vp, vp, sz, vp]),
         "ce_chunked_fwd_bwd_inplace": (ctypes.c_int, [vp, i64, i64, i64, vp, i32, i64, i64, vp, vp, vp,
                                                       vp, vp, sz, vp]),
+        "ce_chunked_fwd_bwd_inplace_noalloc": (ctypes.c_int, [vp, i64, i64, i64, vp, i32, i64, i64,
+                                                              vp, vp, vp, vp, vp]),
         "ce_rows_fwd": (ctypes.c_int, [vp, i64, i64, i64, vp, i32, i64, vp, vp, vp, vp, sz, vp]),
         "ce_rows_bwd": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, vp, i32, i64, vp, vp, vp, vp, sz,
                                        vp]),
@@ -279,6 +283,33 @@ def ce_chunked_fwd_bwd_inplace(logits, labels, *, ignore_index: int = -100,
         _ptr(logits), n, v, ld, _ptr(labels), ignore_index, chunk_size,
         _count_arg(num_label_tokens), _ptr(grad_output), _ptr(loss), _ptr(lse), _ptr(status),
         _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)))
+    return loss, lse
+
+
+def ce_chunked_fwd_bwd_inplace_noalloc(logits, labels, *, ignore_index: int = -100,
+                                       chunk_size: int = 1024,
+                                       num_label_tokens: int | None = None, grad_output=None,
+                                       loss=None, lse=None, status=None):
+    """:func:`ce_chunked_fwd_bwd_inplace` without a workspace: the library keeps the step's
+    O(n) scratch in a static per-GPU array (n <= LCE_NOALLOC_MAX_ROWS). Pass ``loss`` (fp32
+    0-d) and optionally ``lse`` (fp32 [n]) to have nothing allocated here either; calls that
+    may overlap on one GPU must be serialised by the caller. Returns (loss, lse)."""
+    import torch
+    lib = load_library()
+    n, v, ld = _logits_2d(logits)
+    dev = logits.device
+    labels = _labels_i32(labels, n, dev, ignore_index)
+    if grad_output is not None:
+        _require(grad_output, "grad_output", torch.float32, 0, dev)
+    if loss is None:
+        loss = torch.empty((), dtype=torch.float32, device=dev)
+    _require(loss, "loss", torch.float32, 0, dev)
+    if lse is not None:
+        _require_lse(lse, n, dev)
+    _check("ce_chunked_fwd_bwd_inplace_noalloc", lib.ce_chunked_fwd_bwd_inplace_noalloc(
+        _ptr(logits), n, v, ld, _ptr(labels), ignore_index, chunk_size,
+        _count_arg(num_label_tokens), _ptr(grad_output), _ptr(loss), _ptr(lse), _ptr(status),
+        _stream(dev)))
     return loss, lse
 
 

@@ -4,6 +4,7 @@
 #include <atomic>
 #include <cstring>
 #include <limits>
+#include <mutex>
 
 #include "common.h"
 #include "flce.h"
@@ -78,6 +79,74 @@ int check_disjoint(const Span (&wr)[NW], const Span (&rd)[NR]) {
     if ((expr) != hipSuccess) return LCE_ERR_HIP; \
   } while (0)
 
+// ---- static scratch of the allocation-free CE step -------------------------------------
+//
+// The CE step's workspace is a 256-byte header (the label count) and one fp32 term per row.
+// ce_chunked_fwd_bwd_inplace_noalloc keeps it in this device array instead of a caller's
+// allocation: every GPU the library runs on holds its own copy, for the life of the process.
+// The kernels overwrite every word of it they later read (the count, each row's term), so
+// nothing is cleared between calls. In host code `scratch` names a host-side stand-in: its
+// device address comes from hipGetSymbolAddress, once per device, and only that address is
+// ever handed to a kernel.
+constexpr size_t kScratchBytes = 256 + size_t(LCE_NOALLOC_MAX_ROWS) * sizeof(float);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];  // device address of `scratch`, per device (NULL: not yet)
+
+// The current device's address of `scratch`, looked up on the first call on that device.
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LCE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return LCE_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LCE_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return LCE_OK;
+}
+
+// Argument checks of the single-pass CE step (everything but the workspace).
+int ce_fused_check(const uint16_t* logits_inout, int64_t n, int64_t v, int64_t ld,
+                   const int32_t* labels, int64_t chunk_size, const float* grad_output,
+                   const float* loss_out, const float* lse_out, const int32_t* status_out) {
+  int rc = ce_check_shape(n, v, ld, chunk_size);
+  if (rc != LCE_OK) return rc;
+  if (!loss_out || (n > 0 && (!logits_inout || !labels))) return LCE_ERR_NULL_ARG;
+  if (!aligned(logits_inout, 2) || !aligned(labels, 4) || !aligned(grad_output, 4) ||
+      !aligned(loss_out, 4) || !aligned(lse_out, 4) || !aligned(status_out, 4))
+    return LCE_ERR_ALIGNMENT;
+  return LCE_OK;
+}
+
+// The single-pass CE step's launches with its workspace at `workspace`.
+int ce_fused_launch(uint16_t* logits_inout, int64_t n, int64_t v, int64_t ld,
+                    const int32_t* labels, int32_t ignore_index, int64_t num_label_tokens,
+                    const float* grad_output, float* loss_out, float* lse_out,
+                    int32_t* status_out, void* workspace, hipStream_t s) {
+  CeWorkspace ws = lce::ce_workspace_carve(workspace, n);
+  const long long th = num_label_tokens >= 0 ? num_label_tokens : -1;
+  LCE_TRY_HIP(lce::launch_label_prep(labels, n, v, ignore_index, ws.count, status_out, s));
+  if (lce::ce_fused_fits(v)) {
+    LCE_TRY_HIP(lce::launch_ce_fused_rows(logits_inout, n, v, ld, labels, ignore_index, ws.count,
+                                          th, grad_output, ws.row_loss, lse_out, s));
+  } else {
+    // rows too long to hold in registers: the forward pass, then the in-place backward (which
+    // reads each row again, and once more to rebuild its lse when lse_out is NULL)
+    LCE_TRY_HIP(lce::launch_ce_fwd_rows(logits_inout, n, v, ld, labels, ignore_index,
+                                        ws.row_loss, lse_out, s));
+    LCE_TRY_HIP(lce::launch_ce_bwd_rows(logits_inout, ld, logits_inout, ld, n, v, labels,
+                                        ignore_index, lse_out, ws.count, th, grad_output,
+                                        nullptr, s));
+  }
+  LCE_TRY_HIP(lce::launch_loss_reduce(ws.row_loss, n, ws.count, th, loss_out, s));
+  return LCE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -94,6 +163,8 @@ const char* lce_status_str(int status) {
     case LCE_ERR_BAD_FLAGS: return "unknown flag bits";
     case LCE_ERR_ALIGNMENT: return "a pointer is not aligned to its element size";
     case LCE_ERR_OVERLAP: return "an output or the workspace overlaps another buffer of the call";
+    case LCE_ERR_SCRATCH_LIMIT:
+      return "n exceeds LCE_NOALLOC_MAX_ROWS, the rows the allocation-free call's static scratch holds";
     default: return "unknown status";
   }
 }
@@ -183,14 +254,11 @@ int ce_chunked_fwd_bwd_inplace(uint16_t* logits_inout, int64_t n, int64_t v, int
                                int64_t num_label_tokens, const float* grad_output,
                                float* loss_out, float* lse_out, int32_t* status_out,
                                void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = ce_check_shape(n, v, ld, chunk_size);
+  int rc = ce_fused_check(logits_inout, n, v, ld, labels, chunk_size, grad_output, loss_out,
+                          lse_out, status_out);
   if (rc != LCE_OK) return rc;
-  if (!loss_out || (n > 0 && (!logits_inout || !labels))) return LCE_ERR_NULL_ARG;
   if (!workspace || workspace_bytes < lce::ce_workspace_bytes(n)) return LCE_ERR_WORKSPACE;
-  if (!aligned(logits_inout, 2) || !aligned(labels, 4) || !aligned(grad_output, 4) ||
-      !aligned(loss_out, 4) || !aligned(lse_out, 4) || !aligned(status_out, 4) ||
-      !aligned(workspace, 256))
-    return LCE_ERR_ALIGNMENT;
+  if (!aligned(workspace, 256)) return LCE_ERR_ALIGNMENT;
   {
     const Span wr[] = {span(workspace, int64_t(lce::ce_workspace_bytes(n))), span(loss_out, 4),
                        span(lse_out, 4 * n), span(status_out, 4),
@@ -199,24 +267,32 @@ int ce_chunked_fwd_bwd_inplace(uint16_t* logits_inout, int64_t n, int64_t v, int
     if ((rc = check_disjoint(wr, rd)) != LCE_OK) return rc;
   }
   if ((rc = check_device()) != LCE_OK) return rc;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  CeWorkspace ws = lce::ce_workspace_carve(workspace, n);
-  const long long th = num_label_tokens >= 0 ? num_label_tokens : -1;
-  LCE_TRY_HIP(lce::launch_label_prep(labels, n, v, ignore_index, ws.count, status_out, s));
-  if (lce::ce_fused_fits(v)) {
-    LCE_TRY_HIP(lce::launch_ce_fused_rows(logits_inout, n, v, ld, labels, ignore_index, ws.count,
-                                          th, grad_output, ws.row_loss, lse_out, s));
-  } else {
-    // rows too long to hold in registers: the forward pass, then the in-place backward (which
-    // reads each row again, and once more to rebuild its lse when lse_out is NULL)
-    LCE_TRY_HIP(lce::launch_ce_fwd_rows(logits_inout, n, v, ld, labels, ignore_index,
-                                        ws.row_loss, lse_out, s));
-    LCE_TRY_HIP(lce::launch_ce_bwd_rows(logits_inout, ld, logits_inout, ld, n, v, labels,
-                                        ignore_index, lse_out, ws.count, th, grad_output,
-                                        nullptr, s));
+  return ce_fused_launch(logits_inout, n, v, ld, labels, ignore_index, num_label_tokens,
+                         grad_output, loss_out, lse_out, status_out, workspace,
+                         static_cast<hipStream_t>(stream));
+}
+
+int ce_chunked_fwd_bwd_inplace_noalloc(uint16_t* logits_inout, int64_t n, int64_t v, int64_t ld,
+                                       const int32_t* labels, int32_t ignore_index,
+                                       int64_t chunk_size, int64_t num_label_tokens,
+                                       const float* grad_output, float* loss_out,
+                                       float* lse_out, int32_t* status_out, void* stream) {
+  int rc = ce_fused_check(logits_inout, n, v, ld, labels, chunk_size, grad_output, loss_out,
+                          lse_out, status_out);
+  if (rc != LCE_OK) return rc;
+  if (n > LCE_NOALLOC_MAX_ROWS) return LCE_ERR_SCRATCH_LIMIT;
+  {
+    const Span wr[] = {span(loss_out, 4), span(lse_out, 4 * n), span(status_out, 4),
+                       span(logits_inout, matrix_bytes(n, ld, v, 2))};
+    const Span rd[] = {span(labels, 4 * n), span(grad_output, 4)};
+    if ((rc = check_disjoint(wr, rd)) != LCE_OK) return rc;
   }
-  LCE_TRY_HIP(lce::launch_loss_reduce(ws.row_loss, n, ws.count, th, loss_out, s));
-  return LCE_OK;
+  if ((rc = check_device()) != LCE_OK) return rc;
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws)) != LCE_OK) return rc;
+  return ce_fused_launch(logits_inout, n, v, ld, labels, ignore_index, num_label_tokens,
+                         grad_output, loss_out, lse_out, status_out, ws,
+                         static_cast<hipStream_t>(stream));
 }
 
 int ce_rows_fwd(const uint16_t* logits, int64_t n, int64_t v, int64_t ld, const int32_t* labels,

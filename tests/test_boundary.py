@@ -18,6 +18,7 @@ import linear_cross_entropy_masked_amd as lce
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 OK, NULL_ARG, BAD_SHAPE, BAD_CHUNK, WORKSPACE, HIP, DEVICE, BAD_FLAGS, ALIGN, OVERLAP = range(10)
+SCRATCH_LIMIT = 10
 
 
 def _declared_functions():
@@ -45,7 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(10):
+    for code in range(11):
         assert lce.lce_status_str(code) != lce.lce_status_str(12345)
     assert lce.lce_status_str(0) == "ok"
     assert "unknown" in lce.lce_status_str(12345)
@@ -325,3 +326,22 @@ def test_flce_overlapping_buffers_are_refused(lib):
     hit = list(base)
     hit[13] = A4  # grad_hidden over the saved lse
     assert bwd(*hit) == OVERLAP
+
+
+def test_noalloc_step_argument_errors(lib):
+    f = lib.ce_chunked_fwd_bwd_inplace_noalloc
+
+    def call(logits=A1, n=4, v=8, ld=8, labels=A2, chunk=2, gout=None, loss=A3, lse=None,
+             status=None):
+        return f(logits, n, v, ld, labels, -100, chunk, -1, gout, loss, lse, status, None)
+
+    assert call(n=-1) == BAD_SHAPE
+    assert call(ld=7) == BAD_SHAPE
+    assert call(chunk=0) == BAD_CHUNK
+    assert call(loss=None) == NULL_ARG
+    assert call(logits=A1 + 1) == ALIGN
+    assert call(n=lce.LCE_NOALLOC_MAX_ROWS + 1) == SCRATCH_LIMIT
+    assert call(loss=A1 + 4) == OVERLAP                           # the loss inside the logits
+    if _no_gpu():
+        assert call(n=lce.LCE_NOALLOC_MAX_ROWS, v=1, ld=1) in AT_DEVICE_CHECK
+        assert call(lse=A4, status=A5, gout=A6) in AT_DEVICE_CHECK
