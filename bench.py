@@ -12,13 +12,19 @@ synthetic input already resident in HBM:
     in-place backward) — reported under "ce_only" with its HBM roofline, as the two calls
     (forward, then in-place backward) and, under "ce_only.single_pass", as the one call that
     does both when the upstream gradient is known (each labelled row read once);
+  * fused linear CE on the small model (hidden [2048, 768], weight [32777, 768], bias, chunk
+    512; loss and all four gradients) — reported under "small_model" with the oracle timed on
+    the whole workload beside it;
   * fused linear CE on the long-context packed workload (hidden [32768, 8192], weight
     [128256, 8192], 8 documents, chunk 2048) with the recomputing schedule — reported under
     "long_context" (at most 3 timed steps; --no-long-context skips it).
 
 Prints one JSON line. Timing uses hipEvents recorded on the stream the library launches on;
 the in-place CE backward destroys its input, so the logits are restored from a pristine copy
-between steps, outside the timed events.
+between steps, outside the timed events. `value` and `ms_per_step` time the K steps back to
+back; each workload's "timing" also gives the median / min / mean of the steps timed one by
+one, warm (back to back) and cold (the 256 MB MALL and the L2s flushed by a 512 MB write before
+each step, outside the events).
 """
 from __future__ import annotations
 
@@ -38,6 +44,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "FLCE fwd+bwd tokens/s (H4096,V128256) % MFMA peak; CE-only HBM GB/s % peak"
 
 FLCE_WORKLOAD = "flce_8192x4096x128256"
+SMALL_WORKLOAD = "flce_2048x768x32777"
 LONG_WORKLOAD = "flce_32768x8192x128256_packed"
 CE_WORKLOAD = "ce_16384x128256"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
@@ -246,6 +253,44 @@ def timed_kernels(torch, lce, stream, step, steps):
     return steps, ev[0].elapsed_time(ev[1]) / steps, kernels
 
 
+FLUSH_BYTES = 512 << 20  # twice the MI355X's 256 MB MALL: a write of this size evicts it
+
+
+def per_step_times(torch, stream, step, steps, flush=None):
+    """Each of `steps` steps timed alone with a hipEvent pair on `stream`; `flush` (run before
+    each step, outside the events) makes every step start with cold caches. Returns
+    {median_ms, min_ms, mean_ms, steps}."""
+    evs = []
+    for _ in range(steps):
+        if flush is not None:
+            flush()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        step()
+        e[1].record(stream)
+        evs.append(e)
+    torch.cuda.synchronize()
+    return step_stats([e[0].elapsed_time(e[1]) for e in evs])
+
+
+def step_stats(times_ms):
+    t = sorted(times_ms)
+    med = t[len(t) // 2] if len(t) % 2 else 0.5 * (t[len(t) // 2 - 1] + t[len(t) // 2])
+    return {"median_ms": round(med, 4), "min_ms": round(t[0], 4),
+            "mean_ms": round(sum(t) / len(t), 4), "steps": len(t)}
+
+
+def make_flush(torch, dev):
+    """A 512 MB device buffer rewritten by each call (a plain fill kernel)."""
+    buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+    counter = [0]
+
+    def flush():
+        counter[0] += 1
+        buf.fill_(counter[0])
+    return flush
+
+
 def gemm_bytes(kernel, w, stored_slice=True):
     """Algorithmic HBM bytes of one launch of an FLCE product: each operand read once, each
     result written once. The stored-logits schedule writes each chunk's logits as 16-bit
@@ -306,8 +351,10 @@ def run_flce(args, torch, lce, workloads, name=None, recompute=False, steps=None
     hid = torch.from_numpy(inp.hidden.view(np.int16)).view(torch.bfloat16).to(dev)
     wt = torch.from_numpy(inp.weight.view(np.int16)).view(torch.bfloat16).to(dev)
     lab = torch.from_numpy(inp.labels).to(dev)
+    bias = None if inp.bias is None else torch.from_numpy(inp.bias).to(dev)
     gh = torch.empty((w.n, w.h), dtype=torch.bfloat16, device=dev)
     gw = torch.empty((w.v, w.h), dtype=torch.float32, device=dev)
+    gb = None if bias is None else torch.empty(w.v, dtype=torch.float32, device=dev)
     flags = lce.FLCE_RECOMPUTE if recompute else 0
     ws = torch.empty(lce.flce_workspace_size(w.n, w.h, w.v, w.chunk_size, flags),
                      dtype=torch.uint8, device=dev)
@@ -315,8 +362,9 @@ def run_flce(args, torch, lce, workloads, name=None, recompute=False, steps=None
     nvalid = int((inp.labels != -100).sum())
 
     def step():
-        return lce.flce_fwd_bwd(hid, wt, lab, None, chunk_size=w.chunk_size, grad_hidden=gh,
-                                grad_weight=gw, workspace=ws, recompute=recompute)
+        return lce.flce_fwd_bwd(hid, wt, lab, bias, chunk_size=w.chunk_size, grad_hidden=gh,
+                                grad_weight=gw, grad_bias=gb if gb is not None else False,
+                                workspace=ws, recompute=recompute)
 
     for _ in range(warmup):
         step()
@@ -339,6 +387,11 @@ def run_flce(args, torch, lce, workloads, name=None, recompute=False, steps=None
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = ev[0].elapsed_time(ev[1]) / steps
+
+    # the same K steps timed one by one, warm (back to back) and cold (the MALL and L2
+    # flushed by a 512 MB write before each, outside the events)
+    warm = per_step_times(torch, stream, step, steps)
+    cold = per_step_times(torch, stream, step, steps, flush=make_flush(torch, dev))
 
     # per-kernel breakdown: the same K steps again with a hipEvent pair around every launch,
     # recorded by the library on the stream it launches on
@@ -371,6 +424,7 @@ def run_flce(args, torch, lce, workloads, name=None, recompute=False, steps=None
                     for k in kernels},
         "peak_extra_bytes": int(peak_extra), "slice_budget_bytes": int(w.chunk_size * w.v * 4),
         "nvalid": nvalid, "gen_s": gen_s, "chunks": chunks, "inputs": inp,
+        "timing": {"back_to_back_mean_ms": round(ms, 4), "warm": warm, "cold": cold},
     }
 
 
@@ -391,8 +445,12 @@ def run_ce(args, torch, lce, workloads):
     nvalid = int((inp.labels != -100).sum())
     fwd_bytes, bwd_bytes = ce_algorithmic_bytes(w.n, w.v, nvalid)
 
-    def step(timed):
+    flush = make_flush(torch, dev)
+
+    def step(timed, cold=False):
         logits.copy_(pristine)
+        if cold:  # the copy's tail would otherwise sit in the MALL
+            flush()
         e = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if timed else None
         if timed:
             e[0].record(stream)
@@ -417,6 +475,12 @@ def run_ce(args, torch, lce, workloads):
     fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     ms = fwd_ms + bwd_ms
+    timing = {"warm": step_stats([e[0].elapsed_time(e[2]) for e in evs])}
+    cold = [step(True, cold=True)[1] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    timing["cold"] = step_stats([e[0].elapsed_time(e[2]) for e in cold])
+    timing["cold_fwd"] = step_stats([e[0].elapsed_time(e[1]) for e in cold])
+    timing["cold_bwd"] = step_stats([e[1].elapsed_time(e[2]) for e in cold])
 
     kreps, inst_ms, kernels = timed_kernels(torch, lce, stream, lambda: step(False), args.steps)
     kd = {k[0]: k for k in kernels}
@@ -432,7 +496,7 @@ def run_ce(args, torch, lce, workloads):
     fwd_gbs = fwd_bytes / (fwd_ms * 1e-3) / 1e9
     tot_gbs = (fwd_bytes + bwd_bytes) / (ms * 1e-3) / 1e9
     single = run_ce_single_pass(args, torch, lce, w, pristine, logits, lab, ws, stream,
-                                bwd_bytes)
+                                bwd_bytes, flush)
     return {
         "workload": w, "ms": ms, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "wall_s": wall,
         "tokens_per_s": w.n / (ms * 1e-3), "gbs": tot_gbs, "fwd_gbs": fwd_gbs,
@@ -441,15 +505,17 @@ def run_ce(args, torch, lce, workloads):
         "instrumented_ms": inst_ms,
         "kernels": {k[0]: {"ms_per_step": round(k[1] / kreps, 4), "launches_per_step": k[2] // kreps}
                     for k in kernels},
-        "inputs": inp, "nvalid": nvalid, "single": single,
+        "inputs": inp, "nvalid": nvalid, "single": single, "timing": timing,
     }
 
 
-def run_ce_single_pass(args, torch, lce, w, pristine, logits, lab, ws, stream, nbytes):
+def run_ce_single_pass(args, torch, lce, w, pristine, logits, lab, ws, stream, nbytes, flush):
     """The same CE step as one call (ce_chunked_fwd_bwd_inplace): each labelled row read once
     and every row written once, so its algorithmic bytes are those of the backward alone."""
-    def step(timed):
+    def step(timed, cold=False):
         logits.copy_(pristine)
+        if cold:
+            flush()
         e = [torch.cuda.Event(enable_timing=True) for _ in range(2)] if timed else None
         if timed:
             e[0].record(stream)
@@ -465,6 +531,10 @@ def run_ce_single_pass(args, torch, lce, w, pristine, logits, lab, ws, stream, n
     evs = [step(True)[1] for _ in range(args.steps)]
     torch.cuda.synchronize()
     ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    timing = {"warm": step_stats([e[0].elapsed_time(e[1]) for e in evs])}
+    cold = [step(True, cold=True)[1] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    timing["cold"] = step_stats([e[0].elapsed_time(e[1]) for e in cold])
     kreps, _, kernels = timed_kernels(torch, lce, stream, lambda: step(False), args.steps)
     kd = {k[0]: k for k in kernels}
     roof = None
@@ -479,7 +549,7 @@ def run_ce_single_pass(args, torch, lce, w, pristine, logits, lab, ws, stream, n
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.n / (ms * 1e-3), 1),
             "GB_per_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-            "algorithmic_bytes": nbytes, "roofline": roof,
+            "algorithmic_bytes": nbytes, "roofline": roof, "timing": timing,
             "kernels": {k[0]: {"ms_per_step": round(k[1] / kreps, 4),
                                "launches_per_step": k[2] // kreps} for k in kernels}}
 
@@ -510,19 +580,51 @@ def cpu_baseline_flce(res):
                       f"[{res['workload'].v}, {res['workload'].h}]: loss, grad_hidden, grad_weight in fp64"}
 
 
-def cpu_baseline_ce(res):
-    """The fp64 oracle on all 16384 rows of the same logits."""
+def host_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def cpu_baseline_flce_full(res):
+    """The fp64 oracle on the whole workload (loss, grad_hidden, grad_weight, grad_bias)."""
     import oracle
     inp = res["inputs"]
-    k = res["workload"].n
+    w = res["workload"]
     t0 = time.perf_counter()
-    oracle.ce_masked_sum_bits(inp.logits[:k], inp.labels[:k], num_label_tokens=res["nvalid"],
-                              row_block=256)
+    oracle.flce(inp.hidden, inp.weight, inp.labels, bias=inp.bias, row_block=256)
     dt = time.perf_counter() - t0
-    return {"value": round(k / dt, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": round(w.n / dt, 2), "unit": "tokens/s", "cores": blas_threads(),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"the whole workload ({w.n} tokens, weight [{w.v}, {w.h}], bias): loss "
+                      f"and every gradient in fp64"}
+
+
+def cpu_baseline_ce(res):
+    """The fp64 oracle on all 16384 rows of the same logits, row blocks spread over the host
+    cores (threads: numpy releases the interpreter lock inside its array operations; a process
+    pool would have to fork a process that holds the GPU)."""
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle
+    inp = res["inputs"]
+    n = res["workload"].n
+    cores = host_cores()
+    block = 128
+
+    def task(r0):
+        r1 = min(n, r0 + block)
+        oracle.ce_masked_sum_bits(inp.logits[r0:r1], inp.labels[r0:r1],
+                                  num_label_tokens=res["nvalid"], row_block=block)
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(cores) as ex:
+        list(ex.map(task, range(0, n, block)))
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "seconds": round(dt, 2),
-            "sample": f"first {k} of {res['workload'].n} rows of the [{res['workload'].n}, "
-                      f"{res['workload'].v}] logits: loss and full gradient rows in fp64"}
+            "sample": f"all {n} rows of the [{n}, {res['workload'].v}] logits: loss terms and "
+                      f"full gradient rows in fp64, {block}-row blocks on {cores} threads"}
 
 
 def main(argv=None) -> int:
@@ -531,9 +633,10 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["flce", "long", "ce"], default=None,
+    ap.add_argument("--only", choices=["flce", "small", "long", "ce"], default=None,
                     help="run one workload only (profiling): the Llama3-8B-shaped FLCE head, "
-                         "the long-context recompute FLCE, or the CE-only logits")
+                         "the small-model FLCE (with bias), the long-context recompute FLCE, "
+                         "or the CE-only logits")
     ap.add_argument("--no-long-context", action="store_true",
                     help="skip the [32768, 8192] x [128256, 8192] recompute workload")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -548,13 +651,13 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
     if args.record_mfma:
         layer, pdir, tdir = args.record_mfma
-        record_mfma({"flce": FLCE_WORKLOAD, "long": LONG_WORKLOAD, "ce": CE_WORKLOAD}[layer],
-                    pdir, tdir)
+        record_mfma({"flce": FLCE_WORKLOAD, "small": SMALL_WORKLOAD, "long": LONG_WORKLOAD,
+                     "ce": CE_WORKLOAD}[layer], pdir, tdir)
         return 0
     if args.record_traffic:
         layer, fdir, wdir = args.record_traffic
-        record_traffic({"flce": FLCE_WORKLOAD, "long": LONG_WORKLOAD, "ce": CE_WORKLOAD}[layer],
-                       fdir, wdir)
+        record_traffic({"flce": FLCE_WORKLOAD, "small": SMALL_WORKLOAD, "long": LONG_WORKLOAD,
+                        "ce": CE_WORKLOAD}[layer], fdir, wdir)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -595,8 +698,33 @@ def main(argv=None) -> int:
             "kernels": fl["kernels"],
             "peak_extra_bytes": fl["peak_extra_bytes"],
             "slice_budget_bytes": fl["slice_budget_bytes"],
-            "loss": fl["loss"],
+            "loss": fl["loss"], "timing": fl["timing"],
         })
+    if args.only in (None, "small"):
+        sm = run_flce(args, torch, lce, workloads, name=SMALL_WORKLOAD)
+        w = sm["workload"]
+        print(f"# flce {w.name}: {sm['ms']:.3f} ms/step, {sm['tokens_per_s']:.0f} tokens/s",
+              file=sys.stderr, flush=True)
+        small = {
+            "workload": w.name, "tokens": w.n, "hidden": w.h, "vocab": w.v,
+            "chunk_size": w.chunk_size, "bias": True,
+            "outputs": "loss, grad_hidden bf16, grad_weight fp32, grad_bias fp32",
+            "ms_per_step": round(sm["ms"], 4), "tokens_per_s": round(sm["tokens_per_s"], 1),
+            "tflops": round(sm["tflops"], 2),
+            "mfma_frac": round(sm["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+            "roofline": sm["roofline"], "kernels": sm["kernels"], "timing": sm["timing"],
+            "peak_extra_bytes": sm["peak_extra_bytes"],
+            "slice_budget_bytes": sm["slice_budget_bytes"], "loss": sm["loss"]}
+        if not args.no_cpu_baseline:
+            small["cpu_baseline"] = cpu_baseline_flce_full(sm)
+        if args.only == "small":
+            out.update({"value": small["tokens_per_s"], "ms_per_step": small["ms_per_step"],
+                        "config": {"workload": w.name, "tokens": w.n, "hidden": w.h,
+                                   "vocab": w.v, "chunk_size": w.chunk_size, "bias": True},
+                        "roofline": sm["roofline"]})
+        out["small_model"] = small
+        del sm
+        torch.cuda.empty_cache()
     if args.only == "long" or (args.only is None and not args.no_long_context):
         lc = run_flce(args, torch, lce, workloads, name=LONG_WORKLOAD, recompute=True,
                       steps=min(args.steps, 3), warmup=1)
@@ -610,7 +738,7 @@ def main(argv=None) -> int:
             "tokens_per_s": round(lc["tokens_per_s"], 1),
             "model_tflops": round(lc["tflops"], 2), "executed_tflops": round(lc["executed_tflops"], 2),
             "mfma_frac_executed": round(lc["executed_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
-            "roofline": lc["roofline"], "kernels": lc["kernels"],
+            "roofline": lc["roofline"], "kernels": lc["kernels"], "timing": lc["timing"],
             "peak_extra_bytes": lc["peak_extra_bytes"], "slice_budget_bytes": lc["slice_budget_bytes"],
             "loss": lc["loss"]}
         if args.only == "long":
@@ -634,6 +762,7 @@ def main(argv=None) -> int:
             "fwd_GB_per_s": round(ce["fwd_gbs"], 1), "bwd_GB_per_s": round(ce["bwd_gbs"], 1),
             "algorithmic_bytes": ce["algorithmic_bytes"], "roofline": ce["roofline"],
             "kernels": ce["kernels"], "loss": ce["loss"], "single_pass": ce["single"],
+            "timing": ce["timing"],
         }
         if fl is None:
             out.update({"value": round(ce["tokens_per_s"], 1), "ms_per_step": round(ce["ms"], 4),

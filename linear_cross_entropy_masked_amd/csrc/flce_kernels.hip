@@ -558,44 +558,98 @@ __global__ void __launch_bounds__(256) lse_merge_rows_kernel(
   }
 }
 
-// grad_bias[v] (=|+=) coef · (Σ_{labelled i} p_iv − #{i: y_i = v}) from the fp32 slice.
-__global__ void __launch_bounds__(256) slice_bias_grad_kernel(
+// grad_bias[v] (=|+=) coef · (Σ_{labelled i} p_iv − #{i: y_i = v}). One workgroup per 64
+// columns: each of its 16 wavefronts takes every 16th row of the chunk (lane = column, so a
+// row's 64 columns are one coalesced access and the row's label and shift are wavefront
+// uniform), then the 16 partial sums of a column are added in wavefront order through LDS:
+// the same order on every run. `prob(i, col)` is p_iv in fp32, before any bf16 rounding.
+constexpr int kBiasCols = 64, kBiasWaves = 16;
+
+template <class Prob>
+__device__ __forceinline__ void bias_grad_columns(const Prob& prob, int64_t rows, int64_t v,
+                                                  const int32_t* __restrict__ labels,
+                                                  int32_t ignore_index, float* grad_bias,
+                                                  int overwrite, const long long* count_dev,
+                                                  long long count_host, const float* gout) {
+  __shared__ float ps[kBiasWaves][kBiasCols];
+  __shared__ int pc[kBiasWaves][kBiasCols];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t col = int64_t(blockIdx.x) * kBiasCols + lane;
+  float sp = 0.f;
+  int cnt = 0;
+  if (col < v) {
+#pragma unroll 4
+    for (int64_t i = wv; i < rows; i += kBiasWaves) {
+      const int32_t y = labels[i];
+      if (has_label(y, v, ignore_index)) {
+        sp += prob(i, col);
+        cnt += (int64_t(y) == col);
+      }
+    }
+  }
+  ps[wv][lane] = sp;
+  pc[wv][lane] = cnt;
+  __syncthreads();
+  if (wv == 0 && col < v) {
+    float s = 0.f;
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kBiasWaves; ++w) {
+      s += ps[w][lane];
+      c += pc[w][lane];
+    }
+    const float d = flce_coef(count_dev, count_host, gout) * (s - float(c));
+    grad_bias[col] = overwrite ? d : grad_bias[col] + d;
+  }
+}
+
+// p from the fp32 slice: exp(z − lse).
+struct SliceProb {
+  const float* z;
+  int64_t ldz;
+  const float* lse_c;
+  __device__ __forceinline__ float operator()(int64_t i, int64_t col) const {
+    return fast_exp2((z[i * ldz + col] - lse_c[i]) * kLog2e);
+  }
+};
+
+__global__ void __launch_bounds__(64 * kBiasWaves) slice_bias_grad_kernel(
     const float* __restrict__ z, int64_t ldz, int64_t rows, int64_t v,
     const int32_t* __restrict__ labels, int32_t ignore_index, const float* __restrict__ lse_c,
     float* __restrict__ grad_bias, int overwrite, const long long* count_dev,
     long long count_host, const float* gout) {
-  const int64_t col = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (col >= v) return;
-  float sp = 0.f;
-  int cnt = 0;
-  for (int64_t i = 0; i < rows; ++i) {
-    const int32_t y = labels[i];
-    if (!has_label(y, v, ignore_index)) continue;
-    sp += fast_exp2((z[i * ldz + col] - lse_c[i]) * kLog2e);
-    cnt += (int64_t(y) == col);
-  }
-  const float coef = flce_coef(count_dev, count_host, gout);
-  const float d = coef * (sp - float(cnt));
-  grad_bias[col] = overwrite ? d : grad_bias[col] + d;
+  bias_grad_columns(SliceProb{z, ldz, lse_c}, rows, v, labels, ignore_index, grad_bias,
+                    overwrite, count_dev, count_host, gout);
 }
 
 // grad_bias[v] (=|+=) coef · (Σ_mt colsum[mt, v] − #{labelled i: y_i = v}), the column sums
-// (in the slice's free halves) added in row-tile order.
-__global__ void __launch_bounds__(256) bias_from_colsums_kernel(
+// (in the slice's free halves) added in row-tile order; the label count split over the
+// wavefronts as in bias_grad_columns.
+__global__ void __launch_bounds__(64 * kBiasWaves) bias_from_colsums_kernel(
     const float* __restrict__ colsum, int64_t mtiles, int64_t rows, int64_t v,
     const int32_t* __restrict__ labels, int32_t ignore_index, float* __restrict__ grad_bias,
     int overwrite, const long long* count_dev, long long count_host, const float* gout) {
-  const int64_t col = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (col >= v) return;
-  float sp = 0.f;
-  for (int64_t t = 0; t < mtiles; ++t) sp += colsum[gap_index(t * v + col)];
+  __shared__ int pc[kBiasWaves][kBiasCols];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t col = int64_t(blockIdx.x) * kBiasCols + lane;
   int cnt = 0;
-  for (int64_t i = 0; i < rows; ++i) {
-    const int32_t y = labels[i];
-    cnt += (has_label(y, v, ignore_index) && int64_t(y) == col);
+  if (col < v) {
+    for (int64_t i = wv; i < rows; i += kBiasWaves) {
+      const int32_t y = labels[i];
+      cnt += (has_label(y, v, ignore_index) && int64_t(y) == col);
+    }
   }
-  const float d = flce_coef(count_dev, count_host, gout) * (sp - float(cnt));
-  grad_bias[col] = overwrite ? d : grad_bias[col] + d;
+  pc[wv][lane] = cnt;
+  __syncthreads();
+  if (wv == 0 && col < v) {
+    float sp = 0.f;
+    for (int64_t t = 0; t < mtiles; ++t) sp += colsum[gap_index(t * v + col)];
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kBiasWaves; ++w) c += pc[w][lane];
+    const float d = flce_coef(count_dev, count_host, gout) * (sp - float(c));
+    grad_bias[col] = overwrite ? d : grad_bias[col] + d;
+  }
 }
 
 // In place: the fp32 logits of row i, column group g (bytes [256 g, 256 g + 256) of the row)
@@ -658,29 +712,28 @@ __global__ void __launch_bounds__(256) shifted_to_probs_kernel(
   *reinterpret_cast<uint4*>(p) = o;
 }
 
-// grad_bias[v] (=|+=) coef · (Σ_{labelled i} p_iv − #{i: y_i = v}) from the shifted 16-bit
-// logits, p = exp(d + m_t − lse) in fp32 (the probability before its bf16 rounding). A
-// workgroup's 256 columns are one lse tile.
-__global__ void __launch_bounds__(256) shifted_bias_grad_kernel(
+// p from the shifted 16-bit logits d = fp16(z − m_t): exp(d + m_t − lse) in fp32 (the
+// probability before its bf16 rounding); m_t is the row's maximum over the column's 256-wide
+// tile t, uniform over a wavefront's 64 columns.
+struct ShiftedProb {
+  const uint16_t* z;
+  int64_t ldz;
+  const float* lse_c;
+  const float2* part;
+  int64_t tiles;
+  __device__ __forceinline__ float operator()(int64_t i, int64_t col) const {
+    const float d = f16_to_f32(z[i * ldz + col]);
+    return fast_exp2((d + (part[i * tiles + (col >> 8)].x - lse_c[i])) * kLog2e);
+  }
+};
+
+__global__ void __launch_bounds__(64 * kBiasWaves) shifted_bias_grad_kernel(
     const uint16_t* __restrict__ z, int64_t ldz, int64_t rows, int64_t v,
     const int32_t* __restrict__ labels, int32_t ignore_index, const float* __restrict__ lse_c,
     const float2* __restrict__ part, int64_t tiles, float* __restrict__ grad_bias, int overwrite,
     const long long* count_dev, long long count_host, const float* gout) {
-  const int64_t col = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (col >= v) return;
-  const int64_t t = col >> 8;
-  float sp = 0.f;
-  int cnt = 0;
-  for (int64_t i = 0; i < rows; ++i) {
-    const int32_t y = labels[i];
-    if (!has_label(y, v, ignore_index)) continue;
-    const float d = f16_to_f32(z[i * ldz + col]);
-    sp += fast_exp2((d + (part[i * tiles + t].x - lse_c[i])) * kLog2e);
-    cnt += (int64_t(y) == col);
-  }
-  const float coef = flce_coef(count_dev, count_host, gout);
-  const float dv = coef * (sp - float(cnt));
-  grad_bias[col] = overwrite ? dv : grad_bias[col] + dv;
+  bias_grad_columns(ShiftedProb{z, ldz, lse_c, part, tiles}, rows, v, labels, ignore_index,
+                    grad_bias, overwrite, count_dev, count_host, gout);
 }
 
 // dW[y] −= coef · Σ_{i in chunk, y_i = y} h_i. The first chunk row carrying label y owns that
@@ -948,7 +1001,8 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
     }
     if (a.grad_bias) {
       TimedLaunch t(s, K_FLCE_BIAS_GRAD);
-      hipLaunchKernelGGL(shifted_bias_grad_kernel, dim3(unsigned((v + 255) / 256)), dim3(256), 0,
+      hipLaunchKernelGGL(shifted_bias_grad_kernel, dim3(unsigned((v + kBiasCols - 1) / kBiasCols)),
+                         dim3(64 * kBiasWaves), 0,
                          s, half[hf], ws.ldz, rows, v, lab, a.ignore_index, lse_c, part,
                          ws.tiles, a.grad_bias, int(first && !accumulate), &st->count, th,
                          a.grad_output);
@@ -1193,7 +1247,8 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
       // 3. bias gradient from the fp32 logits
       if (a.grad_bias) {
         TimedLaunch t(s, K_FLCE_BIAS_GRAD);
-        hipLaunchKernelGGL(slice_bias_grad_kernel, dim3(unsigned((v + 255) / 256)), dim3(256), 0,
+        hipLaunchKernelGGL(slice_bias_grad_kernel, dim3(unsigned((v + kBiasCols - 1) / kBiasCols)),
+                           dim3(64 * kBiasWaves), 0,
                            s, ws.slice, ws.ldz, rows, v, lab, a.ignore_index, lse_c,
                            a.grad_bias, int(first && !accumulate), &st->count, th, a.grad_output);
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1246,7 +1301,8 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
       }
       if (a.grad_bias) {
         TimedLaunch t(s, K_FLCE_BIAS_GRAD);
-        hipLaunchKernelGGL(bias_from_colsums_kernel, dim3(unsigned((v + 255) / 256)), dim3(256), 0,
+        hipLaunchKernelGGL(bias_from_colsums_kernel,
+                           dim3(unsigned((v + kBiasCols - 1) / kBiasCols)), dim3(64 * kBiasWaves), 0,
                            s, ws.slice, row_tiles(rows), rows, v, lab, a.ignore_index,
                            a.grad_bias, int(first && !accumulate), &st->count, th, a.grad_output);
         if ((e = hipGetLastError()) != hipSuccess) return e;
