@@ -271,11 +271,14 @@ def assert_fused_equals_two_pass(dev, bits, labels, chunk=16, count=None, g=None
 
 
 # rows per lane-vector count: v/8 <= 4096 (4 vectors per lane), <= 8192 (8), <= 16384 (16),
-# and past it (the two passes inside the call); ld_extra shifts each row's alignment
+# and past it (the two passes inside the call); ld_extra shifts each row's alignment. The
+# cases with more rows than the GPU has CUs keep several rows per CU in flight, ignored rows
+# among them.
 @pytest.mark.parametrize("n,v,ld_extra", [
     (1, 1, 0), (3, 7, 0), (64, 1000, 0), (17, 1000, 3), (33, 32777, 0), (5, 32775, 1),
     (9, 40000, 5), (5, 65543, 0), (7, 70001, 1), (6, 128256, 0), (4, 131079, 0),
-    (3, 131080, 2), (3, 140000, 0)])
+    (3, 131080, 2), (3, 140000, 0), (600, 1000, 0), (1100, 24, 0), (520, 32776, 8),
+    (300, 65544, 0), (290, 128256, 0), (777, 8192, 0)])
 def test_fused_bitwise_equals_two_pass(dev, n, v, ld_extra):
     inp = random_ce(n, v, sigma=2.5, ignore_frac=0.2, seed=n * 13 + v + ld_extra)
     assert_fused_equals_two_pass(dev, inp.logits, inp.labels, ld=v + ld_extra)
@@ -305,6 +308,22 @@ def test_fused_zero_count_all_ignored_and_upstream_grad(dev):
     loss, lse, grad, _ = run_fused(dev, inp.logits, inp.labels, count=1000, g=2.5)
     check_against_oracle(inp.logits, inp.labels, float(loss.item()), lse.cpu().numpy(), grad,
                          count=1000, g=2.5)
+
+
+def test_fused_row_loop_zero_count_and_upstream_grad(dev):
+    """More rows than CUs: T = 0 (lse and loss terms kept, every gradient element written as
+    +0), an all-ignored batch, and a caller's T and upstream gradient, bitwise the two
+    passes."""
+    inp = random_ce(700, 1000, seed=31, ignore_frac=0.1)
+    loss, lse, grad, _ = run_fused(dev, inp.logits, inp.labels, count=0)
+    assert float(loss.item()) == 0.0
+    assert not grad.view(torch.int16).any().item(), "T = 0 must write +0 everywhere"
+    assert np.all(lse.cpu().numpy()[inp.labels != -100] != 0)
+    labels = np.full_like(inp.labels, -100)
+    loss, lse, grad, _ = run_fused(dev, inp.logits, labels)
+    assert float(loss.item()) == 0.0 and not grad.view(torch.int16).any().item()
+    assert not lse.cpu().numpy().any()
+    assert_fused_equals_two_pass(dev, inp.logits, inp.labels, count=5000, g=0.75)
 
 
 def test_fused_bad_labels_flagged_and_empty(dev):

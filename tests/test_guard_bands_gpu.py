@@ -64,7 +64,7 @@ def assert_clean(named):
 # ------------------------------------------------------------------------------- CE layer
 
 @pytest.mark.parametrize("n,v,ld_extra", [(37, 1000, 24), (16, 32777, 7), (5, 128256, 64),
-                                          (64, 1000, 0)])
+                                          (64, 1000, 0), (600, 1000, 8), (300, 32776, 0)])
 def test_ce_calls_stay_inside_their_buffers(dev, n, v, ld_extra):
     inp = random_ce(n, v, sigma=3.0, ignore_frac=0.2, seed=n + v)
     ld = v + ld_extra
