@@ -154,6 +154,29 @@ __device__ __forceinline__ int64_t lse_off(int64_t gap, int64_t i) {
   return gap < 0 ? i : gap_index(gap + i);
 }
 
+// One fp32 value per chunk row kept in memory the call owns anyway: p[i] (layout 0), the
+// first half of a 64-float slice group, p[(i / 32) · 64 + i % 32] (layout 1: clear of the
+// split-K partials, which take the second halves), or the slice's free halves from element
+// `base` on (layout 2). p == nullptr: none.
+struct RowVec {
+  float* p;
+  int64_t base;
+  int layout;
+  __device__ __forceinline__ float& operator[](int64_t i) const {
+    if (layout == 1) return p[(i >> 5) * 64 + (i & 31)];
+    if (layout == 2) return p[gap_index(base + i)];
+    return p[i];
+  }
+};
+
+// The label's one-hot coefficient with the rounding residual of the label's bf16
+// probability: the products see q = bf16(p_y) where the gradient wants p_y, so the fp32
+// one-hot term subtracts (1 − (p_y − q)) instead of 1, which makes the label element's
+// total exactly p_y − 1 up to fp32 rounding. p − q is exact (q is p rounded, within a factor
+// of two of it). Without it the label element carries q's rounding, up to 2^-9 · p_y, which
+// for rows a model predicts well (p_y near 1) is as large as the whole label gradient.
+__device__ __forceinline__ float label_coef(float p, float q) { return 1.f - (p - q); }
+
 // Pass 1 of the recomputing schedule: the logits tile is only reduced, never stored. Leaves
 // the per-tile (max, Σ exp) pairs like EpiLogits, and zy[m] = z[m, y_m] for the tile holding
 // the label column.
@@ -206,6 +229,7 @@ struct EpiProbs {
   int64_t v;
   int32_t ignore_index;
   float* colsum;  // the slice as floats, or NULL: no column sums
+  RowVec coef_out, coef_out2;  // each labelled row's label_coef (second copy optional)
   static constexpr bool kRowStats = false;
   static constexpr bool kColSums = true;
   static constexpr bool kTileMax = false;
@@ -216,6 +240,7 @@ struct EpiProbs {
   struct Aux {
     gemm::f32x4_t b;
     float c;  // the row's lse, or NaN for a row without a label
+    int y;    // the row's label
   };
   __device__ __forceinline__ Aux load4(int64_t m, int64_t n) const {
     Aux x;
@@ -225,7 +250,8 @@ struct EpiProbs {
       for (int q = 0; q < 4; ++q)
         if (n + q < v) x.b[q] = bias[n + q];
     }
-    x.c = has_label(labels[m], v, ignore_index) ? lse[lse_off(lse_gap, m)] : __builtin_nanf("");
+    x.y = labels[m];
+    x.c = has_label(x.y, v, ignore_index) ? lse[lse_off(lse_gap, m)] : __builtin_nanf("");
     return x;
   }
   __device__ __forceinline__ gemm::f32x4_t colvalue4(gemm::f32x4_t a, Aux x) const {
@@ -241,7 +267,15 @@ struct EpiProbs {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       if (n + q >= v) r[q] = 0.f;
-    *reinterpret_cast<uint2*>(p + at(m, n)) = uint2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+    const uint2 o = {pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+    *reinterpret_cast<uint2*>(p + at(m, n)) = o;
+    const int64_t d = int64_t(x.y) - n;
+    if (coef_out.p && d >= 0 && d < 4 && x.c == x.c) {  // this row's label column
+      const float pr = r[int(d)];
+      const float q = d < 2 ? (d == 0 ? bf16_lo(o.x) : bf16_hi(o.x)) : (d == 2 ? bf16_lo(o.y) : bf16_hi(o.y));
+      coef_out[m] = label_coef(pr, q);
+      if (coef_out2.p) coef_out2[m] = label_coef(pr, q);
+    }
   }
   __device__ __forceinline__ void operator()(int64_t, int64_t, float) {}  // N % 4 == 0: unused
   __device__ __forceinline__ void col_sums(int64_t mt, int64_t n, float sum) {
@@ -264,28 +298,32 @@ struct EpiGradHidden {
   long long count_host;
   const float* gout;
   float coef;
+  RowVec ycoef;  // each labelled row's label_coef
   __device__ void begin(int64_t) { coef = flce_coef(count_dev, count_host, gout); }
   __device__ __forceinline__ void operator()(int64_t m, int64_t n, float a) {
     const int32_t y = labels[m];
     float r = 0.f;
-    if (has_label(y, v, ignore_index)) r = coef * (a - bf16_to_f32(w[int64_t(y) * ldw + n]));
+    if (has_label(y, v, ignore_index))
+      r = coef * (a - ycoef[m] * bf16_to_f32(w[int64_t(y) * ldw + n]));
     dh[m * ldh + n] = f32_to_bf16(r);
   }
-  // aux: the 4 weights W[y_m, n .. n+3] as two bf16 pairs; ok = 0 for a row without label
+  // aux: the 4 weights W[y_m, n .. n+3] as two bf16 pairs and the row's label coefficient;
+  // ok = 0 for a row without label
   struct Aux {
     uint32_t a, b, ok;
+    float c;
   };
   __device__ __forceinline__ Aux load4(int64_t m, int64_t n) const {
     const int32_t y = labels[m];
-    if (!has_label(y, v, ignore_index)) return Aux{0u, 0u, 0u};
+    if (!has_label(y, v, ignore_index)) return Aux{0u, 0u, 0u, 0.f};
     const uint2 wy = *reinterpret_cast<const uint2*>(w + int64_t(y) * ldw + n);
-    return Aux{wy.x, wy.y, 1u};
+    return Aux{wy.x, wy.y, 1u, ycoef[m]};
   }
   __device__ __forceinline__ void store4(int64_t m, int64_t n, gemm::f32x4_t a, Aux x) {
     uint2 o = {0u, 0u};
     if (x.ok) {
-      o.x = pack_bf16x2(coef * (a[0] - bf16_lo(x.a)), coef * (a[1] - bf16_hi(x.a)));
-      o.y = pack_bf16x2(coef * (a[2] - bf16_lo(x.b)), coef * (a[3] - bf16_hi(x.b)));
+      o.x = pack_bf16x2(coef * (a[0] - x.c * bf16_lo(x.a)), coef * (a[1] - x.c * bf16_hi(x.a)));
+      o.y = pack_bf16x2(coef * (a[2] - x.c * bf16_lo(x.b)), coef * (a[3] - x.c * bf16_hi(x.b)));
     }
     *reinterpret_cast<uint2*>(dh + m * ldh + n) = o;
   }
@@ -372,7 +410,8 @@ __global__ void __launch_bounds__(256) label_rank_kernel(const int32_t* __restri
 __global__ void __launch_bounds__(256) onehot_segments_kernel(
     const uint16_t* __restrict__ hidden, int64_t h, int64_t rows,
     const int32_t* __restrict__ slab, const int32_t* __restrict__ srow, int64_t v,
-    float* grad_weight, const long long* count_dev, long long count_host, const float* gout) {
+    float* grad_weight, const long long* count_dev, long long count_host, const float* gout,
+    RowVec ycoef) {
   const int64_t p = blockIdx.x;
   const int32_t y = slab[p];
   if (y >= v || (p > 0 && slab[p - 1] == y)) return;
@@ -382,14 +421,16 @@ __global__ void __launch_bounds__(256) onehot_segments_kernel(
   for (int64_t col = 4 * int64_t(threadIdx.x); col < h; col += 4 * 256) {
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
     for (int64_t e = p; e < end; ++e) {
-      const uint16_t* hr = hidden + int64_t(srow[e]) * h + col;
+      const int64_t r = srow[e];
+      const float c = ycoef[r];  // the row's label coefficient (1 − its label residual)
+      const uint16_t* hr = hidden + r * h + col;
       if (col + 4 <= h) {
         const uint2 x = *reinterpret_cast<const uint2*>(hr);
-        a0 += bf16_lo(x.x); a1 += bf16_hi(x.x); a2 += bf16_lo(x.y); a3 += bf16_hi(x.y);
+        a0 += c * bf16_lo(x.x); a1 += c * bf16_hi(x.x); a2 += c * bf16_lo(x.y); a3 += c * bf16_hi(x.y);
       } else {
-        a0 += bf16_to_f32(hr[0]);
-        if (col + 1 < h) a1 += bf16_to_f32(hr[1]);
-        if (col + 2 < h) a2 += bf16_to_f32(hr[2]);
+        a0 += c * bf16_to_f32(hr[0]);
+        if (col + 1 < h) a1 += c * bf16_to_f32(hr[1]);
+        if (col + 2 < h) a2 += c * bf16_to_f32(hr[2]);
       }
     }
     float* d = grad_weight + int64_t(y) * h + col;
@@ -427,7 +468,7 @@ __global__ void __launch_bounds__(256) grad_hidden_reduce_kernel(
     const float* __restrict__ slice, int64_t M, int64_t N, int64_t splits,
     uint16_t* __restrict__ dh, const int32_t* __restrict__ labels, const uint16_t* __restrict__ w,
     int64_t v, int32_t ignore_index, const long long* count_dev, long long count_host,
-    const float* gout) {
+    const float* gout, RowVec ycoef) {
   const int64_t e = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
   if (e >= M * N) return;
   const int64_t m = e / N, n = e % N;
@@ -443,9 +484,10 @@ __global__ void __launch_bounds__(256) grad_hidden_reduce_kernel(
       acc.w += p.w;
     }
     const float coef = flce_coef(count_dev, count_host, gout);
+    const float c = ycoef[m];
     const uint2 wy = *reinterpret_cast<const uint2*>(w + int64_t(y) * N + n);
-    o.x = pack_bf16x2(coef * (acc.x - bf16_lo(wy.x)), coef * (acc.y - bf16_hi(wy.x)));
-    o.y = pack_bf16x2(coef * (acc.z - bf16_lo(wy.y)), coef * (acc.w - bf16_hi(wy.y)));
+    o.x = pack_bf16x2(coef * (acc.x - c * bf16_lo(wy.x)), coef * (acc.y - c * bf16_hi(wy.x)));
+    o.y = pack_bf16x2(coef * (acc.z - c * bf16_lo(wy.y)), coef * (acc.w - c * bf16_hi(wy.y)));
   }
   *reinterpret_cast<uint2*>(dh + e) = o;
 }
@@ -527,11 +569,15 @@ __global__ void __launch_bounds__(kRowThreads) slice_row_lse_kernel(
 // fp32 slice; zy and row_loss may be the same array (each row reads its label logit before
 // writing its term). The lse goes to lse_c in the layout lse_gap names (lse_off). One
 // wavefront per row.
+//
+// With `yc` (the stored-logits schedule that keeps fp16(z − m_t), whose probability pass is
+// shifted_to_probs_kernel): each labelled row's label_coef, from the fp32 label logit and the
+// label's probability operand exactly as that pass will form it; also into yc2 when given.
 __global__ void __launch_bounds__(256) lse_merge_rows_kernel(
     const float2* __restrict__ part, int64_t tiles, const float* __restrict__ z, int64_t ldz,
     const float* zy, int64_t rows, int64_t v, const int32_t* __restrict__ labels,
     int32_t ignore_index, float* __restrict__ lse_c, int64_t lse_gap,
-    float* row_loss, float* __restrict__ lse_out) {
+    float* row_loss, float* __restrict__ lse_out, RowVec yc, RowVec yc2) {
   const int64_t i = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (i >= rows) return;
@@ -552,9 +598,18 @@ __global__ void __launch_bounds__(256) lse_merge_rows_kernel(
   wave_lse_reduce(m, sum);
   if (lane == 0) {
     const float lse = m + fast_log2(sum) * kLn2;
+    const float zl = zy ? zy[i] : z[i * ldz + y];
     lse_c[lse_off(lse_gap, i)] = lse;
-    row_loss[i] = lse - (zy ? zy[i] : z[i * ldz + y]);
+    row_loss[i] = lse - zl;
     if (lse_out) lse_out[i] = lse;
+    if (yc.p) {
+      const float mt = part[i * tiles + (y >> 8)].x;  // the label column's tile maximum
+      const float d = f16_to_f32(pack_f16x2(zl - mt, 0.f));
+      const float q = bf16_lo(pack_bf16x2(fast_exp2((d + (mt - lse)) * kLog2e), 0.f));
+      const float c = label_coef(fast_exp2((zl - lse) * kLog2e), q);
+      yc[i] = c;
+      if (yc2.p) yc2[i] = c;
+    }
   }
 }
 
@@ -660,7 +715,8 @@ __global__ void __launch_bounds__(64 * kBiasWaves) bias_from_colsums_kernel(
 __global__ void __launch_bounds__(256) slice_to_probs_kernel(float* z, int64_t ldz, int64_t v,
                                                              const int32_t* __restrict__ labels,
                                                              int32_t ignore_index,
-                                                             const float* __restrict__ lse_c) {
+                                                             const float* __restrict__ lse_c,
+                                                             RowVec yc) {
   const int64_t i = blockIdx.y;
   const int64_t g = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
   const int L = threadIdx.x & 15;
@@ -682,6 +738,11 @@ __global__ void __launch_bounds__(256) slice_to_probs_kernel(float* z, int64_t l
   o.x = pack_bf16x2(p[0], p[1]);
   o.y = pack_bf16x2(p[2], p[3]);
   *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(row) + g * (2 * kGroup) + 4 * L) = o;
+  const int64_t d = int64_t(y) - col;
+  if (ok && d >= 0 && d < 4) {  // the label column: its label coefficient
+    const float q = d < 2 ? (d == 0 ? bf16_lo(o.x) : bf16_hi(o.x)) : (d == 2 ? bf16_lo(o.y) : bf16_hi(o.y));
+    yc[i] = label_coef(p[int(d)], q);
+  }
 }
 
 // In place over a 16-bit [rows, ldz] array of shifted logits d = fp16(z − m_t) (EpiLogits16):
@@ -741,7 +802,7 @@ __global__ void __launch_bounds__(64 * kBiasWaves) shifted_bias_grad_kernel(
 __global__ void __launch_bounds__(256) onehot_weight_fix_kernel(
     const uint16_t* __restrict__ hidden, int64_t h, int64_t rows,
     const int32_t* __restrict__ labels, int32_t ignore_index, int64_t v, float* grad_weight,
-    const long long* count_dev, long long count_host, const float* gout) {
+    const long long* count_dev, long long count_host, const float* gout, RowVec ycoef) {
   const int64_t i = blockIdx.x;
   const int32_t y = labels[i];
   if (!has_label(y, v, ignore_index)) return;
@@ -770,7 +831,8 @@ __global__ void __launch_bounds__(256) onehot_weight_fix_kernel(
     if (cnt == 0) continue;
     for (int64_t col = threadIdx.x; col < h; col += 256) {
       float acc = 0.f;
-      for (int k = 0; k < cnt; ++k) acc += bf16_to_f32(hidden[(base + match[k]) * h + col]);
+      for (int k = 0; k < cnt; ++k)
+        acc += ycoef[base + match[k]] * bf16_to_f32(hidden[(base + match[k]) * h + col]);
       grad_weight[int64_t(y) * h + col] -= coef * acc;
     }
   }
@@ -845,14 +907,21 @@ __global__ void fill_zero_f32(float* p, int64_t count) {
     p[i] = 0.f;
 }
 
+// dst[i] = src[i] for i < n (per-row values moved out of memory that is about to be written)
+__global__ void copy_rows_kernel(RowVec src, RowVec dst, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * blockDim.x)
+    dst[i] = src[i];
+}
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int64_t lse_tiles(int64_t v) { return (v + Wide::BN - 1) / Wide::BN; }
 int64_t row_tiles(int64_t c) { return (c + Wide::BM - 1) / Wide::BM; }
 
 // Free-half elements kept at the end of the slice in the compact layout: the chunk's lse
-// (recomputing schedule), then, in the last 32, the call's FlceState.
-int64_t reserved_gap(int64_t c) { return round_up(c, 32) + 32; }
+// (recomputing schedule), its label coefficients, then, in the last 32, the call's FlceState.
+int64_t reserved_gap(int64_t c) { return 2 * round_up(c, 32) + 32; }
 
 // Compact layout: the workspace is the fp32 slice [C, ldz] and nothing else. What the call
 // keeps beside the logits lives in memory it owns anyway:
@@ -941,9 +1010,12 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
   constexpr int64_t kStateReserve = 256;  // end of a half kept for the moved call state
   hipError_t e;
 
+  const RowVec none{nullptr, 0, 0};
   // the probabilities of rows [c0, c0 + rows) into half hf (with lse, loss terms and
-  // grad_bias on the way, as the mode has them)
-  auto front = [&](int64_t c0, int64_t rows, int hf, bool first) -> hipError_t {
+  // grad_bias on the way, as the mode has them), the rows' label coefficients into yc (and
+  // yc2 when given)
+  auto front = [&](int64_t c0, int64_t rows, int hf, bool first, RowVec yc,
+                   RowVec yc2) -> hipError_t {
     const int32_t* lab = a.labels + c0;
     float* scr = reinterpret_cast<float*>(a.grad_hidden + c0 * h);
     float2* part = reinterpret_cast<float2*>(scr);
@@ -964,7 +1036,7 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
           hipLaunchKernelGGL(lse_merge_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0,
                              s, part, ws.tiles, nullptr, int64_t(0), term, rows, v, lab,
                              a.ignore_index, lse_c, int64_t(-1), term,
-                             a.lse_out ? a.lse_out + c0 : nullptr);
+                             a.lse_out ? a.lse_out + c0 : nullptr, none, none);
           if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         TimedLaunch t(s, K_FLCE_LOSS_ACC);
@@ -975,7 +1047,7 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
       const float* lse = mode == kPairBwdOnly ? a.lse_in + c0 : lse_c;
       // the GEMM runs over N = ldz: weight rows past v read as zero, their columns become 0
       EpiProbs e2{half[hf], ws.ldz, kGroup, a.bias, lse, int64_t(-1), lab, v, a.ignore_index,
-                  nullptr};
+                  nullptr, yc, yc2};
       TimedLaunch t(s, K_FLCE_GEMM_PROBS);
       return gemm::v2::launch<Wide, true, true>(Ah, Bw, rows, ws.ldz, h, 1, true, e2, s);
     }
@@ -990,7 +1062,7 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
       hipLaunchKernelGGL(lse_merge_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s,
                          part, ws.tiles, nullptr, int64_t(0), term, rows, v, lab,
                          a.ignore_index, lse_c, int64_t(-1), term,
-                         a.lse_out ? a.lse_out + c0 : nullptr);
+                         a.lse_out ? a.lse_out + c0 : nullptr, yc, yc2);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     {
@@ -1016,8 +1088,8 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
   };
 
   // grad_hidden of rows [c0, c0 + rows), probabilities in half hf, split partials in the
-  // other half
-  auto grad_hidden = [&](int64_t c0, int64_t rows, int hf, bool last) -> hipError_t {
+  // other half, label coefficients in yc
+  auto grad_hidden = [&](int64_t c0, int64_t rows, int hf, bool last, RowVec yc) -> hipError_t {
     float* other = reinterpret_cast<float*>(half[1 - hf]);
     if (last) {
       FlceState* dst = reinterpret_cast<FlceState*>(reinterpret_cast<char*>(other) + half_bytes - 16);
@@ -1042,7 +1114,8 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
       TimedLaunch t(s, K_FLCE_GEMM_GRAD_HIDDEN);
       hipError_t r;
       if (splits == 1) {
-        EpiGradHidden eh{dh, h, lab, a.weight, h, v, a.ignore_index, cnt, th, a.grad_output, 0.f};
+        EpiGradHidden eh{dh, h, lab, a.weight, h, v, a.ignore_index, cnt, th, a.grad_output, 0.f,
+                         yc};
         r = gemm::v2::launch<Wide, true, false>(Ap, Bw2, rows, h, v, 1, true, eh, s);
       } else {
         EpiPartial ep{other, rows, h, 0};
@@ -1054,13 +1127,13 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
     TimedLaunch t(s, K_FLCE_GRAD_HIDDEN_REDUCE);
     hipLaunchKernelGGL(grad_hidden_reduce_kernel, dim3(unsigned((rows * h / 4 + 255) / 256)),
                        dim3(256), 0, s, other, rows, h, splits, dh, lab, a.weight, v,
-                       a.ignore_index, cnt, th, a.grad_output);
+                       a.ignore_index, cnt, th, a.grad_output, yc);
     return hipGetLastError();
   };
 
   // grad_weight over K = rows of the pair starting at c0 (probabilities from half 0 on), then
-  // its one-hot term
-  auto grad_weight = [&](int64_t c0, int64_t rows, bool first) -> hipError_t {
+  // its one-hot term (label coefficients of the pair's rows in yc)
+  auto grad_weight = [&](int64_t c0, int64_t rows, bool first, RowVec yc) -> hipError_t {
     const int32_t* lab = a.labels + c0;
     const uint16_t* hid = a.hidden + c0 * h;
     const long long* cnt = &st->count;
@@ -1083,25 +1156,57 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
       }
       TimedLaunch t(s, K_FLCE_ONEHOT_FIX);
       hipLaunchKernelGGL(onehot_segments_kernel, dim3(unsigned(rows)), dim3(256), 0, s, hid, h,
-                         rows, slab, srow, v, a.grad_weight, cnt, th, a.grad_output);
+                         rows, slab, srow, v, a.grad_weight, cnt, th, a.grad_output, yc);
     } else {
       TimedLaunch t(s, K_FLCE_ONEHOT_FIX);
       hipLaunchKernelGGL(onehot_weight_fix_kernel, dim3(unsigned(rows)), dim3(256), 0, s, hid, h,
-                         rows, lab, a.ignore_index, v, a.grad_weight, cnt, th, a.grad_output);
+                         rows, lab, a.ignore_index, v, a.grad_weight, cnt, th, a.grad_output, yc);
     }
     return hipGetLastError();
   };
 
-  for (int64_t c0 = 0; c0 < n; c0 += 2 * chunk) {
-    const int64_t ra = n - c0 < chunk ? n - c0 : chunk;
+  // Label coefficients (label_coef) of a pair's rows: A's go to the first halves of half 1's
+  // groups (clear of the partials of A's grad_hidden, which take the second halves) and, when
+  // the pair has a B, beside B's bookkeeping in B's grad_hidden rows, where B's follow; the
+  // one-hot term of grad_weight reads them there. B's are then copied into the first halves
+  // of half 0's groups (free once grad_weight is done) for B's grad_hidden, which overwrites
+  // B's rows. A B whose rows cannot hold the pair's coefficients beside its bookkeeping (a
+  // short last chunk) starts a pair of its own.
+  for (int64_t c0 = 0, ra = 0, rb = 0; c0 < n; c0 += ra + rb) {
+    ra = n - c0 < chunk ? n - c0 : chunk;
     const int64_t rest = n - c0 - ra;
-    const int64_t rb = rest < chunk ? rest : chunk;
+    rb = rest < chunk ? rest : chunk;
+    float* pair_coef = nullptr;
+    if (rb > 0) {
+      float* scr_b = reinterpret_cast<float*>(a.grad_hidden + (c0 + ra) * h);
+      const int64_t used = (2 * ws.tiles + 2) * rb;  // B's tile pairs, lse and loss terms
+      if (used + ra + rb + 4 <= rb * h / 2)
+        pair_coef = scr_b + used;
+      else
+        rb = 0;
+    }
     const bool first = c0 == 0;
-    if ((e = front(c0, ra, 0, first)) != hipSuccess) return e;
-    if ((e = grad_hidden(c0, ra, 0, rb == 0)) != hipSuccess) return e;
-    if (rb > 0 && (e = front(c0 + ra, rb, 1, false)) != hipSuccess) return e;
-    if (a.grad_weight && (e = grad_weight(c0, ra + rb, first)) != hipSuccess) return e;
-    if (rb > 0 && (e = grad_hidden(c0 + ra, rb, 1, c0 + ra + rb >= n)) != hipSuccess) return e;
+    const RowVec in_half1{reinterpret_cast<float*>(half[1]), 0, 1};
+    const RowVec in_half0{reinterpret_cast<float*>(half[0]), 0, 1};
+    const RowVec pair_a{pair_coef, 0, 0};
+    if ((e = front(c0, ra, 0, first, in_half1, pair_coef ? pair_a : none)) != hipSuccess)
+      return e;
+    if ((e = grad_hidden(c0, ra, 0, c0 + ra >= n, in_half1)) != hipSuccess) return e;
+    if (rb > 0 && (e = front(c0 + ra, rb, 1, false, RowVec{pair_coef + ra, 0, 0}, none)) !=
+                      hipSuccess)
+      return e;
+    if (a.grad_weight &&
+        (e = grad_weight(c0, ra + rb, first, rb > 0 ? pair_a : in_half1)) != hipSuccess)
+      return e;
+    if (rb > 0) {
+      {
+        TimedLaunch t(s, K_FLCE_LOSS_ACC);
+        hipLaunchKernelGGL(copy_rows_kernel, dim3(unsigned((rb + 255) / 256)), dim3(256), 0, s,
+                           RowVec{pair_coef + ra, 0, 0}, in_half0, rb);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
+      if ((e = grad_hidden(c0 + ra, rb, 1, c0 + ra + rb >= n, in_half0)) != hipSuccess) return e;
+    }
   }
   if (mode == kPairBwdOnly) return hipSuccess;
   TimedLaunch t(s, K_LOSS_REDUCE);
@@ -1213,6 +1318,11 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
       lse_c = const_cast<float*>(a.lse_in + c0);
       lse_gap = -1;
     }
+    // the chunk's label coefficients: beside the slice (the label-logit array, free once the
+    // loss terms are formed), or in the compact layout's reserved free halves after the lse
+    const RowVec none{nullptr, 0, 0};
+    const RowVec yc = ws.compact ? RowVec{ws.slice, usable_gap + round_up(chunk, 32), 2}
+                                 : RowVec{ws.zy, 0, 0};
 
     if (!recompute_chunk) {
       // 1. logits slice (the pipelined GEMM also leaves per-tile logsumexp pairs; the
@@ -1232,7 +1342,7 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
           if (fused_lse)
             hipLaunchKernelGGL(lse_merge_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256),
                                0, s, part, ws.tiles, ws.slice, ws.ldz, nullptr, rows, v, lab,
-                               a.ignore_index, lse_c, int64_t(-1), term, lo);
+                               a.ignore_index, lse_c, int64_t(-1), term, lo, none, none);
           else
             hipLaunchKernelGGL(slice_row_lse_kernel, dim3(unsigned(rows)), dim3(kRowThreads), 0,
                                s, ws.slice, ws.ldz, v, lab, a.ignore_index, lse_c, term, lo);
@@ -1261,7 +1371,7 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
         TimedLaunch t(s, K_FLCE_TO_PROBS);
         hipLaunchKernelGGL(slice_to_probs_kernel,
                            dim3(unsigned((groups + 15) / 16), unsigned(rows)), dim3(256), 0, s,
-                           ws.slice, ws.ldz, v, lab, a.ignore_index, lse_c);
+                           ws.slice, ws.ldz, v, lab, a.ignore_index, lse_c, yc);
         if ((e = hipGetLastError()) != hipSuccess) return e;
       }
     } else {
@@ -1280,7 +1390,7 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
           TimedLaunch t(s, K_FLCE_ROW_LSE);
           hipLaunchKernelGGL(lse_merge_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0,
                              s, part, ws.tiles, nullptr, 0, zy, rows, v, lab, a.ignore_index,
-                             lse_c, lse_gap, term, lo);
+                             lse_c, lse_gap, term, lo, none, none);
           if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         TimedLaunch t(s, K_FLCE_LOSS_ACC);
@@ -1292,7 +1402,7 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
       // 3'. pass 2: the logits are recomputed tile by tile and leave as bf16 probabilities in
       //     the slice (and, for grad_bias, as fp32 column sums)
       EpiProbs e2{reinterpret_cast<uint16_t*>(ws.slice), 2 * ws.ldz, 2 * kGroup, a.bias, lse_c,
-                  lse_gap, lab, v, a.ignore_index, a.grad_bias ? ws.slice : nullptr};
+                  lse_gap, lab, v, a.ignore_index, a.grad_bias ? ws.slice : nullptr, yc, none};
       {
         TimedLaunch t(s, K_FLCE_GEMM_PROBS);
         if ((e = gemm::v2::launch<Wide, true, true>(Ah, Bw, rows, ws.ldz, h, 1, true, e2, s)) !=
@@ -1327,7 +1437,7 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     if (splits < 1) splits = 1;
     const long long* cnt = &st->count;
     EpiGradHidden eh{a.grad_hidden + c0 * h, h, lab, a.weight, h, v, a.ignore_index,
-                     cnt, th, a.grad_output, 0.f};
+                     cnt, th, a.grad_output, 0.f, yc};
     EpiPartial ep{ws.slice, rows, h, 0};
     EpiGradWeight ew{a.grad_weight, h, int(first && !accumulate), cnt, th, a.grad_output, 0.f};
     if (a.grad_hidden) {
@@ -1346,7 +1456,7 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
       TimedLaunch t(s, K_FLCE_GRAD_HIDDEN_REDUCE);
       hipLaunchKernelGGL(grad_hidden_reduce_kernel, dim3(unsigned((rows * h / 4 + 255) / 256)),
                          dim3(256), 0, s, ws.slice, rows, h, splits, a.grad_hidden + c0 * h, lab,
-                         a.weight, v, a.ignore_index, cnt, th, a.grad_output);
+                         a.weight, v, a.ignore_index, cnt, th, a.grad_output, yc);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (a.grad_weight) {
@@ -1364,12 +1474,12 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
         }
         TimedLaunch t(s, K_FLCE_ONEHOT_FIX);
         hipLaunchKernelGGL(onehot_segments_kernel, dim3(unsigned(rows)), dim3(256), 0, s, hid, h,
-                           rows, slab, srow, v, a.grad_weight, cnt, th, a.grad_output);
+                           rows, slab, srow, v, a.grad_weight, cnt, th, a.grad_output, yc);
       } else {
         TimedLaunch t(s, K_FLCE_ONEHOT_FIX);
         hipLaunchKernelGGL(onehot_weight_fix_kernel, dim3(unsigned(rows)), dim3(256), 0, s, hid,
                            h, rows, lab, a.ignore_index, v, a.grad_weight, cnt, th,
-                           a.grad_output);
+                           a.grad_output, yc);
       }
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }

@@ -12,7 +12,7 @@ import torch
 
 import linear_cross_entropy_masked_amd as lce
 import oracle
-from workloads import WORKLOADS, make_flce_inputs, random_flce
+from workloads import WORKLOADS, f32_to_bf16_bits, make_flce_inputs, random_flce
 
 from _helpers import (assert_close_rel, bits_to_device, device_to_f64, gpu_device,
                       normwise_rel)
@@ -161,6 +161,64 @@ def test_small_model_workload_parity(dev, recompute):
     print(f"\n[{w.name} {'recompute' if recompute else 'stored fp16'}] normwise grad_weight "
           f"error {err_w:.3e}, grad_bias {err_b:.3e}, grad_hidden "
           f"{normwise_rel(device_to_f64(res['gh']), ref.grad_hidden):.3e}")
+
+
+def peaked_flce(n, h, v, seed, bias=True):
+    """random_flce with the rows a trained model predicts well: half of the labelled rows are
+    moved along their label's weight row so that the label logit rises by 8, 12 or 20, which
+    puts p_y near 0.98, 0.999 and 1 − 1e-7 at these shapes. bf16(p_y) then carries a rounding
+    error as large as the label gradient 1 − p_y itself (bf16(p_y) = 1 for the largest), so
+    the label element must get its residual p_y − bf16(p_y) back in fp32."""
+    inp = random_flce(n, h, v, weight_sigma=0.05, bias=bias, ignore_frac=0.05, seed=seed)
+    rng = np.random.default_rng(seed + 100)
+    hid = oracle.bf16_bits_to_f64(inp.hidden)
+    w = oracle.bf16_bits_to_f64(inp.weight)
+    ok = np.nonzero(inp.labels != -100)[0]
+    rows = rng.choice(ok, ok.size // 2, replace=False)
+    wy = w[inp.labels[rows]]
+    rise = rng.choice([8.0, 12.0, 20.0], rows.size)[:, None]
+    hid[rows] += rise * wy / (wy * wy).sum(axis=1, keepdims=True)
+    inp.hidden = f32_to_bf16_bits(hid.astype(np.float32))
+    return inp
+
+
+@pytest.mark.parametrize("n,h,v,chunk,recompute,bias", [
+    (512, 128, 3000, 128, False, True),   # two chunks per slice, stored 16-bit logits
+    (600, 128, 3000, 128, False, False),  # ... and a last pair of one chunk
+    (394, 64, 3000, 128, False, True),    # ... a short last chunk that starts a pair of its own
+    (512, 128, 3000, 128, True, False),   # two chunks per slice, recomputing
+    (300, 128, 3000, 128, True, True),    # recomputing with grad_bias (one chunk per slice)
+    (300, 40, 2000, 32, False, True),     # workspace beside the slice, fp32 logits
+    (300, 64, 2000, 32, True, True)])     # workspace beside the slice, recomputing
+def test_peaked_rows_keep_the_label_residual(dev, n, h, v, chunk, recompute, bias):
+    """Rows with label probabilities near one: grad_weight normwise to 1e-4 (2e-4 at H = 40),
+    grad_bias to 1e-4, and every element of grad_weight / grad_hidden to the bf16 rounding
+    budget of the probabilities. The normwise bar is what needs the label element's rounding
+    residual applied in fp32 with the one-hot term: the CPU rounding model of these inputs
+    (bf16 probabilities, scale and one-hot in fp32) gives 1.4e-3 to 3.1e-3 without it and
+    3.8e-5 to 1.2e-4 with it (1.2e-4 at H = 40, where the non-label probabilities' own bf16
+    rounding weighs more; the label gradient of a p_y ~ 1 − 1e-7 row is lost entirely
+    without the residual, since bf16(p_y) = 1)."""
+    inp = peaked_flce(n, h, v, seed=n + h + v, bias=bias)
+    res = run_flce(dev, inp, chunk, recompute=recompute)
+    assert res["status"] == 0
+    check(inp, res, normwise_gw=1e-4 if h >= 64 else 2e-4)
+    check(inp, res)  # the elementwise budget
+
+
+def test_peaked_rows_split_calls(dev):
+    """flce_fwd + flce_bwd (the backward recomputes the probabilities from the saved lse) on
+    rows with label probabilities near one."""
+    inp = peaked_flce(512, 128, 3000, seed=5)
+    hid = bits_to_device(inp.hidden, dev)
+    w = bits_to_device(inp.weight, dev)
+    lab = torch.from_numpy(inp.labels.astype(np.int32)).to(dev)
+    b = torch.from_numpy(inp.bias).to(dev)
+    loss, lse = lce.flce_fwd(hid, w, lab, b, chunk_size=128)
+    gh, gw, gb = lce.flce_bwd(hid, w, lab, lse, b, chunk_size=128)
+    torch.cuda.synchronize()
+    check(inp, dict(loss=float(loss.item()), gh=gh, gw=gw, gb=gb, lse=lse.cpu().numpy()),
+          normwise_gw=1e-4)
 
 
 @pytest.mark.parametrize("n,h,v,chunk,bias", [
