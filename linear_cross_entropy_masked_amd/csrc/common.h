@@ -110,6 +110,7 @@ enum KernelId {
   K_FLCE_LABEL_SORT,
   K_CE_FUSED_ROWS,
   K_FLCE_LOSS_ACC,
+  K_FLCE_PROBS_TRANSPOSED,
   K_COUNT
 };
 

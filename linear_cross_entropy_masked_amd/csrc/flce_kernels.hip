@@ -29,6 +29,8 @@
 // chunks per slice, and runs step 6 once per two chunks (flce_paired): the fp32 accumulator
 // is then read and written half as often. The lse and the loss come from the fp32 logits in
 // either form.
+#include <algorithm>
+
 #include "common.h"
 #include "flce.h"
 #include "gemm_tile.h"
@@ -773,6 +775,53 @@ __global__ void __launch_bounds__(256) shifted_to_probs_kernel(
   *reinterpret_cast<uint4*>(p) = o;
 }
 
+// The same conversion with the result stored transposed, for the schedule that keeps every
+// row's probabilities (flce_transposed): chunk rows c0 .. c0 + rows − 1 become columns of
+// Pᵀ [v, ldp], whose rows v < seg_rows sit at pt1 + v · ldp and the others at
+// pt2 + (v − seg_rows) · ldp. Values are shifted_to_probs_kernel's bit for bit; tokens past
+// the chunk's rows (the last chunk's, up to ldp) get zeros. A workgroup converts 64 tokens ×
+// 256 columns (one logits tile, so one m_t per token): lane i takes tokens 8 (i % 8) .. + 7
+// and columns 8 (i / 8) .. + 7, with eight 16-byte loads (a wavefront reads 128 contiguous
+// bytes of each of 8 token rows) and eight 16-byte stores (128 contiguous bytes of each of
+// 8 Pᵀ rows); the 8 × 8 transpose is a renaming of registers.
+__global__ void __launch_bounds__(256) shifted_to_probs_t_kernel(
+    const uint16_t* __restrict__ z, int64_t ldz, int64_t rows, int64_t v,
+    const int32_t* __restrict__ labels, int32_t ignore_index, const float* __restrict__ lse_c,
+    const float2* __restrict__ part, int64_t tiles, uint16_t* pt1, uint16_t* pt2,
+    int64_t seg_rows, int64_t ldp, int64_t c0) {
+  const int tg = threadIdx.x & 7, g = threadIdx.x >> 3;
+  const int64_t vt = blockIdx.x;
+  const int64_t v0 = vt * 256 + 8 * g;
+  if (v0 >= v) return;  // none of the lane's columns exists; else v0 + 8 <= ldz (64 | ldz)
+  const int64_t t0 = int64_t(blockIdx.y) * 64 + 8 * tg;
+  float p[8][8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int64_t t = t0 + r;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) p[r][q] = 0.f;
+    if (t < rows && has_label(labels[t], v, ignore_index)) {
+      const uint4 x = *reinterpret_cast<const uint4*>(z + t * ldz + v0);
+      const float sh = part[t * tiles + vt].x - lse_c[t];
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float d = f16_to_f32(w[q >> 1] >> (16 * (q & 1)));
+        p[r][q] = v0 + q < v ? fast_exp2((d + sh) * kLog2e) : 0.f;
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int64_t row = v0 + q;
+    if (row >= v) break;
+    uint16_t* dst = (row < seg_rows ? pt1 + row * ldp : pt2 + (row - seg_rows) * ldp) + c0 + t0;
+    *reinterpret_cast<uint4*>(dst) =
+        uint4{pack_bf16x2(p[0][q], p[1][q]), pack_bf16x2(p[2][q], p[3][q]),
+              pack_bf16x2(p[4][q], p[5][q]), pack_bf16x2(p[6][q], p[7][q])};
+  }
+}
+
 // p from the shifted 16-bit logits d = fp16(z − m_t): exp(d + m_t − lse) in fp32 (the
 // probability before its bf16 rounding); m_t is the row's maximum over the column's 256-wide
 // tile t, uniform over a wavefront's 64 columns.
@@ -1214,6 +1263,229 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
   return hipGetLastError();
 }
 
+// Every row's probabilities kept at once, transposed (stored-logits schedule, no
+// FLCE_ACCUMULATE). Pᵀ [v, ldp] in bf16 takes 2 · ldp bytes per vocabulary row against
+// grad_weight's 4 · h, so when the batch is no longer than about 2h it fits the bytes of the
+// fp32 grad_weight the call is about to overwrite, plus the slice:
+//   - grad_weight's bytes [T0, v · 4h) hold Pᵀ rows 0 .. S − 1 (T0 = v · 4h − S · 2 ldp);
+//     the slice's start holds rows S .. v − 1, followed by every row's label coefficient
+//     and the call state;
+//   - grad_weight's bytes [0, T0) hold one chunk's 16-bit shifted logits while the chunks are
+//     formed, then grad_hidden's split partials (if any);
+//   - grad_hidden is then one product over all n rows (K = v) and grad_weight one product
+//     over all n rows (K = n) per vocabulary range: a plain store, no fp32 read-modify-write.
+//     The launch for rows [r_i, r_{i+1}) writes grad_weight bytes [r_i · 4h, r_{i+1} · 4h),
+//     which must hold no Pᵀ row >= r_i: r_{i+1} · 4h <= T0 + r_i · 2 ldp. The rows in the
+//     slice form the last range, free of that condition.
+// Each chunk's tile pairs, lse and loss terms sit in its own grad_hidden rows (flce_paired's
+// layout) until the single grad_hidden product writes them.
+constexpr int kMaxRanges = 64;
+struct TransposedPlan {
+  int64_t ldp;             // Pᵀ row length: n rounded up to 64 tokens
+  int64_t seg;             // S: Pᵀ rows [0, S) in grad_weight's bytes, [S, v) in the slice
+  int64_t t0;              // byte offset of Pᵀ row 0 in grad_weight
+  int64_t yc_off, st_off;  // slice byte offsets of the label coefficients and the call state
+  int nr;                  // grad_weight launches
+  int64_t r[kMaxRanges + 1];
+};
+
+bool plan_transposed(int64_t n, int64_t h, int64_t v, int64_t c, int64_t ldz, int64_t slice_bytes,
+                     TransposedPlan& p) {
+  if (n < 1 || c % 64 != 0 || h % Wide::BK != 0 || (c + 63) / 64 > 65535 ||
+      (v + 255) / 256 > (int64_t(1) << 31) - 1)
+    return false;
+  p.ldp = round_up(n, 64);
+  const int64_t pb = 2 * p.ldp, wb = 4 * h;
+  // the slice's tail: label coefficients (n floats) and the state; its head also takes the
+  // sorted labels of the one-hot pass (2 · kSortMax ints) once grad_weight is done
+  const int64_t tail = int64_t(align256(size_t(n) * 4)) + 256;
+  const int64_t head_min = 2 * kSortMax * 4;
+  const int64_t e_max = (slice_bytes - tail - 256) / pb;  // Pᵀ rows the slice can take
+  if (e_max < 1) return false;
+  const int64_t scratch = c * ldz * 2;                       // one chunk's 16-bit logits
+  if (v * wb - scratch < 0) return false;
+  const int64_t s_hi = std::min(v, (v * wb - scratch) / pb);  // T0 >= scratch
+  const int64_t s_lo = std::max<int64_t>(0, v - e_max);
+  // one 256 x 256 workgroup per CU: q m-tiles fill the 256 CUs once
+  const int64_t nt = (h + Wide::BN - 1) / Wide::BN;
+  const int64_t q = 256 % nt == 0 ? 256 / nt : 1;
+  int64_t S = round_up(s_lo, q * 256);
+  if (S > s_hi) S = round_up(s_lo, 256);
+  if (S > s_hi) S = round_up(s_lo, 64);
+  if (S > s_hi) return false;
+  if (S > v) S = v;
+  p.seg = S;
+  p.t0 = v * wb - S * pb;
+  p.yc_off = std::max<int64_t>(int64_t(align256(size_t((v - S) * pb))), head_min);
+  p.st_off = p.yc_off + int64_t(align256(size_t(n) * 4));
+  if (p.st_off + 256 > slice_bytes) return false;
+  // grad_weight ranges over the rows in grad_weight's bytes, then the slice's rows
+  p.nr = 0;
+  p.r[0] = 0;
+  int64_t r = 0;
+  while (r < S) {
+    const int64_t lim = std::min(S, (p.t0 + r * pb) / wb);  // rows writable from r on
+    int64_t nx = lim;
+    if (nx < S) {  // keep ranges whole waves of tiles, else whole tiles
+      if (nx - r >= q * 256)
+        nx = r + (nx - r) / (q * 256) * (q * 256);
+      else if (nx - r >= 256)
+        nx = r + (nx - r) / 256 * 256;
+    }
+    if (nx <= r || p.nr >= kMaxRanges) return false;
+    p.r[++p.nr] = nx;
+    r = nx;
+  }
+  if (S < v) {
+    if (p.nr >= kMaxRanges) return false;
+    p.r[++p.nr] = v;
+  }
+  return true;
+}
+
+hipError_t flce_transposed(const FlceArgs& a, const FlceWs& ws, int64_t chunk,
+                           const TransposedPlan& pl, hipStream_t s) {
+  const int64_t n = a.n, h = a.h, v = a.v, S = pl.seg;
+  const long long th = a.num_label_tokens >= 0 ? a.num_label_tokens : -1;
+  char* const sl = reinterpret_cast<char*>(ws.slice);
+  char* const gwb = reinterpret_cast<char*>(a.grad_weight);
+  uint16_t* const z16 = reinterpret_cast<uint16_t*>(gwb);         // one chunk's 16-bit logits
+  uint16_t* const pt1 = reinterpret_cast<uint16_t*>(gwb + pl.t0);  // Pᵀ rows [0, S)
+  uint16_t* const pt2 = reinterpret_cast<uint16_t*>(sl);           // Pᵀ rows [S, v)
+  float* const ycall = reinterpret_cast<float*>(sl + pl.yc_off);  // label coefficients [n]
+  FlceState* const st = reinterpret_cast<FlceState*>(sl + pl.st_off);
+  const long long* cnt = &st->count;
+  const RowVec none{nullptr, 0, 0};
+  hipError_t e;
+
+  if ((e = launch_label_prep(a.labels, n, v, a.ignore_index, &st->count, a.status_out, s)) !=
+      hipSuccess)
+    return e;
+  for (int64_t c0 = 0; c0 < n; c0 += chunk) {
+    const int64_t rows = n - c0 < chunk ? n - c0 : chunk;
+    const bool first = c0 == 0;
+    const int32_t* lab = a.labels + c0;
+    float* scr = reinterpret_cast<float*>(a.grad_hidden + c0 * h);
+    float2* part = reinterpret_cast<float2*>(scr);
+    float* lse_c = scr + 2 * rows * ws.tiles;
+    float* term = lse_c + rows;  // first the label logits, then the loss terms
+    View Ah{a.hidden + c0 * h, h, kGroup, rows, h};
+    View Bw{a.weight, h, kGroup, v, h};
+    EpiLogits16 el{z16, ws.ldz, a.bias, part, ws.tiles, lab, term};
+    {
+      TimedLaunch t(s, K_FLCE_GEMM_LOGITS);
+      if ((e = gemm::v2::launch<Wide, true, true>(Ah, Bw, rows, v, h, 1, true, el, s)) !=
+          hipSuccess)
+        return e;
+    }
+    {
+      TimedLaunch t(s, K_FLCE_ROW_LSE);
+      hipLaunchKernelGGL(lse_merge_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s,
+                         part, ws.tiles, nullptr, int64_t(0), term, rows, v, lab, a.ignore_index,
+                         lse_c, int64_t(-1), term, a.lse_out ? a.lse_out + c0 : nullptr,
+                         RowVec{ycall + c0, 0, 0}, none);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    {
+      TimedLaunch t(s, K_FLCE_LOSS_ACC);
+      hipLaunchKernelGGL(loss_accumulate_kernel, dim3(1), dim3(256), 0, s, term, rows, st,
+                         int(first));
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (a.grad_bias) {
+      TimedLaunch t(s, K_FLCE_BIAS_GRAD);
+      hipLaunchKernelGGL(shifted_bias_grad_kernel, dim3(unsigned((v + kBiasCols - 1) / kBiasCols)),
+                         dim3(64 * kBiasWaves), 0, s, z16, ws.ldz, rows, v, lab, a.ignore_index,
+                         lse_c, part, ws.tiles, a.grad_bias, int(first), cnt, th, a.grad_output);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    TimedLaunch t(s, K_FLCE_PROBS_TRANSPOSED);
+    hipLaunchKernelGGL(shifted_to_probs_t_kernel,
+                       dim3(unsigned((v + 255) / 256), unsigned((rows + 63) / 64)), dim3(256), 0,
+                       s, z16, ws.ldz, rows, v, lab, a.ignore_index, lse_c, part, ws.tiles, pt1,
+                       pt2, S, pl.ldp, c0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+
+  // grad_hidden = g·s·(P · W − c·W[y]) over all rows, K = v (Pᵀ read MN-major, its rows in
+  // two segments); split over K only when the row tiles alone do not fill the chip, the
+  // partials then in grad_weight's bytes below Pᵀ
+  {
+    View Ap{S > 0 ? pt1 : pt2, pl.ldp, kGroup, v, n};
+    if (S > 0 && S < v) {
+      Ap.p2 = pt2;
+      Ap.kseg = S;
+    }
+    View Bw2{a.weight, h, kGroup, v, h};
+    const int64_t tiles = row_tiles(n) * ((h + Wide::BN - 1) / Wide::BN);
+    int64_t splits = 256 / tiles;
+    if (splits > (v + 2047) / 2048) splits = (v + 2047) / 2048;
+    if (splits > pl.t0 / (8 * n * h)) splits = pl.t0 / (8 * n * h);
+    if (splits < 1) splits = 1;
+    float* part = reinterpret_cast<float*>(gwb);
+    const RowVec yc{ycall, 0, 0};
+    {
+      TimedLaunch t(s, K_FLCE_GEMM_GRAD_HIDDEN);
+      const bool two = S > 0 && S < v;
+      if (splits == 1) {
+        EpiGradHidden eh{a.grad_hidden, h, a.labels, a.weight, h, v, a.ignore_index, cnt, th,
+                         a.grad_output, 0.f, yc};
+        e = two ? gemm::v2::launch<Wide, false, false, EpiGradHidden, true>(Ap, Bw2, n, h, v, 1,
+                                                                             true, eh, s, true)
+                : gemm::v2::launch<Wide, false, false>(Ap, Bw2, n, h, v, 1, true, eh, s, true);
+      } else {
+        EpiPartial ep{part, n, h, 0};
+        e = two ? gemm::v2::launch<Wide, false, false, EpiPartial, true>(Ap, Bw2, n, h, v,
+                                                                          splits, true, ep, s)
+                : gemm::v2::launch<Wide, false, false>(Ap, Bw2, n, h, v, splits, true, ep, s);
+      }
+      if (e != hipSuccess) return e;
+    }
+    if (splits > 1) {
+      TimedLaunch t(s, K_FLCE_GRAD_HIDDEN_REDUCE);
+      hipLaunchKernelGGL(grad_hidden_reduce_kernel, dim3(unsigned((n * h / 4 + 255) / 256)),
+                         dim3(256), 0, s, part, n, h, splits, a.grad_hidden, a.labels, a.weight,
+                         v, a.ignore_index, cnt, th, a.grad_output, yc);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+
+  // grad_weight = g·s·Pᵀ · hidden over all rows (K = n), one launch per vocabulary range
+  View Bh{a.hidden, h, kGroup, n, h};
+  for (int i = 0; i < pl.nr; ++i) {
+    const int64_t r0 = pl.r[i], r1 = pl.r[i + 1];
+    const uint16_t* base = r0 < S ? pt1 + r0 * pl.ldp : pt2 + (r0 - S) * pl.ldp;
+    View Ap{base, pl.ldp, kGroup, r1 - r0, n};
+    EpiGradWeight ew{a.grad_weight + r0 * h, h, 1, cnt, th, a.grad_output, 0.f};
+    TimedLaunch t(s, K_FLCE_GEMM_GRAD_WEIGHT);
+    if ((e = gemm::v2::launch<Wide, true, false>(Ap, Bh, r1 - r0, h, n, 1, true, ew, s, true)) !=
+        hipSuccess)
+      return e;
+  }
+
+  // one-hot term of grad_weight, kSortMax rows at a time: labels sorted into runs at the
+  // slice's start (free once grad_weight is formed), one pass over the runs
+  int32_t* slab = reinterpret_cast<int32_t*>(sl);
+  int32_t* srow = slab + kSortMax;
+  for (int64_t g0 = 0; g0 < n; g0 += kSortMax) {
+    const int64_t rows = n - g0 < kSortMax ? n - g0 : kSortMax;
+    {
+      TimedLaunch t(s, K_FLCE_LABEL_SORT);
+      hipLaunchKernelGGL(label_rank_kernel, dim3(unsigned((rows + 63) / 64)), dim3(256), 0, s,
+                         a.labels + g0, rows, v, a.ignore_index, slab, srow);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    TimedLaunch t(s, K_FLCE_ONEHOT_FIX);
+    hipLaunchKernelGGL(onehot_segments_kernel, dim3(unsigned(rows)), dim3(256), 0, s,
+                       a.hidden + g0 * h, h, rows, slab, srow, v, a.grad_weight, cnt, th,
+                       a.grad_output, RowVec{ycall + g0, 0, 0});
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  TimedLaunch t(s, K_LOSS_REDUCE);
+  hipLaunchKernelGGL(loss_finish_kernel, dim3(1), dim3(64), 0, s, st, th, n, a.loss_out);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int flce_check_shape(int64_t n, int64_t h, int64_t v, int64_t chunk_size, uint32_t flags) {
@@ -1259,6 +1531,13 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
   // its recomputing schedule when grad_hidden rows can take the bookkeeping and no grad_bias
   // is asked for (its column sums need the room the second chunk takes)
   const bool paired = ws.compact && (!recompute || (gh_scratch && !fwd_only && !a.grad_bias));
+  // every row's probabilities kept transposed in grad_weight's bytes and the slice
+  // (flce_transposed): the stored-logits schedule, when grad_weight is overwritten and the
+  // batch fits
+  TransposedPlan tp;
+  if (paired && !recompute && !accumulate && a.grad_weight &&
+      plan_transposed(n, h, v, chunk, ws.ldz, chunk * ws.ldz * 4, tp))
+    return flce_transposed(a, ws, chunk, tp, s);
   FlceState* st = st_slice;  // where the state is now
   if (paired)
     st = reinterpret_cast<FlceState*>(reinterpret_cast<char*>(a.grad_hidden + n * h) - 16);

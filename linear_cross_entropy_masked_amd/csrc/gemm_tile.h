@@ -38,6 +38,10 @@ struct View {
   int64_t gs;    // elements between consecutive 64-column groups
   int64_t rows;  // valid rows
   int64_t cols;  // valid columns
+  // Two-segment MN-major operand (pipelined GEMM launched with SEGA): rows kseg .. rows − 1
+  // sit at p2 + (row − kseg) · ld instead of p + row · ld. kseg is a multiple of the K slice.
+  const uint16_t* p2 = nullptr;
+  int64_t kseg = 0;
 };
 
 // Buffer resource over [base, base + bytes): loads at offsets past the end return zero, which
@@ -361,12 +365,21 @@ struct Stream {
   int64_t step;   // advance after the next slice
   int64_t step2;  // advance after the one after (differs from step only for 32-deep slices
                   // of a grouped K-major operand: 32 elements, then the gap to the next group)
+  // two-segment operands only: slices left before the window moves to (base2, recs2); 0 never
+  int64_t left;
+  uint64_t base2;
+  int64_t recs2;
 };
 
 // Window of the K slice starting at k0 (a multiple of BK) for rows / columns r0 .. r0 + R − 1.
-template <bool KMAJOR, int BK>
+// SEG (MN-major only): the operand's k rows come in the two segments View::p / View::p2.
+template <bool KMAJOR, int BK, bool SEG = false>
 __device__ __forceinline__ Stream stream_at(const View& X, int64_t r0, int64_t k0, int64_t K) {
+  static_assert(!(SEG && KMAJOR), "two segments split the k rows of an MN-major operand");
   Stream st;
+  st.left = 0;
+  st.base2 = 0;
+  st.recs2 = 0;
   if constexpr (KMAJOR) {
     const int64_t g = (k0 >> 6) * X.gs + (k0 & 63);
     st.base = reinterpret_cast<uint64_t>(X.p + r0 * X.ld + g);
@@ -381,11 +394,27 @@ __device__ __forceinline__ Stream stream_at(const View& X, int64_t r0, int64_t k
   } else {
     // k rows past min(rows, K) read as zero; the window also stops at the end of the matrix
     // (the shifted base would otherwise let the last row's columns past `cols` run over it)
-    const int64_t kr = (X.rows < K ? X.rows : K) - k0;
+    const int64_t kall = X.rows < K ? X.rows : K;
     const int64_t shift = (r0 >> 6) * X.gs;
-    const int64_t avail = (X.rows - k0) * X.ld - shift;
-    st.base = reinterpret_cast<uint64_t>(X.p + k0 * X.ld + shift);
-    st.recs = (kr * X.ld < avail ? kr * X.ld : avail) * 2;
+    if (SEG && k0 >= X.kseg) {  // starts in the second segment
+      const int64_t kr = kall - k0;
+      const int64_t avail = (X.rows - k0) * X.ld - shift;
+      st.base = reinterpret_cast<uint64_t>(X.p2 + (k0 - X.kseg) * X.ld + shift);
+      st.recs = (kr * X.ld < avail ? kr * X.ld : avail) * 2;
+    } else {
+      const int64_t e1 = SEG ? X.kseg : X.rows;  // k rows of the first segment
+      const int64_t kr = (kall < e1 ? kall : e1) - k0;
+      const int64_t avail = (e1 - k0) * X.ld - shift;
+      st.base = reinterpret_cast<uint64_t>(X.p + k0 * X.ld + shift);
+      st.recs = (kr * X.ld < avail ? kr * X.ld : avail) * 2;
+      if (SEG) {
+        const int64_t kr2 = kall - X.kseg;
+        const int64_t avail2 = (X.rows - X.kseg) * X.ld - shift;
+        st.left = (X.kseg - k0) / BK;
+        st.base2 = reinterpret_cast<uint64_t>(X.p2 + shift);
+        st.recs2 = kr2 <= 0 ? 0 : (kr2 * X.ld < avail2 ? kr2 * X.ld : avail2) * 2;
+      }
+    }
     st.step = st.step2 = int64_t(BK) * X.ld * 2;
   }
   // every input is wave-uniform; saying so keeps the window in SGPRs for the whole K loop.
@@ -400,11 +429,17 @@ __device__ __forceinline__ Stream stream_at(const View& X, int64_t r0, int64_t k
   st.recs = int64_t(u64(uint64_t(st.recs)));
   st.step = int64_t(u64(uint64_t(st.step)));
   st.step2 = int64_t(u64(uint64_t(st.step2)));
+  if (SEG) {
+    st.left = int64_t(u64(uint64_t(st.left)));
+    st.base2 = u64(st.base2);
+    st.recs2 = int64_t(u64(uint64_t(st.recs2)));
+  }
   return st;
 }
 
-// Issue one operand's P loads of the current slice (LDS bytes m0 .. m0 + P KiB), then advance.
-template <int P>
+// Issue one operand's P loads of the current slice (LDS bytes m0 .. m0 + P KiB), then advance
+// (SEG: to the second segment after the first one's last slice).
+template <int P, bool SEG = false>
 __device__ __forceinline__ void dma_issue(Stream& st, const uint32_t (&off)[P], uint32_t m0) {
   const int64_t r = st.recs;
   const uint32_t n = r <= 0 ? 0u : (r >= 0xffffffffLL ? 0xffffffffu : uint32_t(r));
@@ -417,6 +452,10 @@ __device__ __forceinline__ void dma_issue(Stream& st, const uint32_t (&off)[P], 
   const int64_t t = st.step;
   st.step = st.step2;
   st.step2 = t;
+  if (SEG && --st.left == 0) {
+    st.base = st.base2;
+    st.recs = st.recs2;
+  }
 }
 
 // One 16 × 32 MFMA operand fragment for rows rbase .. rbase+15 and k = 32 kk .. 32 kk + 31 of
@@ -485,7 +524,7 @@ __device__ __forceinline__ bool tile_coord(const TileMap& tm, int64_t w, TileCoo
 }
 
 // One BM × BN output tile at tile coordinates `tc`.
-template <class C, bool AK, bool BKM, class Epi>
+template <class C, bool AK, bool BKM, class Epi, bool SEGA = false>
 __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M, int64_t N,
                                          int64_t K, int64_t ksplit, const TileCoord& tc,
                                          Epi& epi, char* lds) {
@@ -503,7 +542,7 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
   uint32_t offa[C::PA], offb[C::PB];
   dma_offsets<AK, C::BM, BK, C::PA>(A, offa);
   dma_offsets<BKM, C::BN, BK, C::PB>(B, offb);
-  Stream sa = stream_at<AK, BK>(A, m0, kbeg, K);
+  Stream sa = stream_at<AK, BK, SEGA>(A, m0, kbeg, K);
   Stream sb = stream_at<BKM, BK>(B, n0, kbeg, K);
   // LDS byte addresses of this wavefront's DMA destinations in slot 0
   const uint32_t wv = __builtin_amdgcn_readfirstlane(uint32_t(threadIdx.x >> 6));
@@ -542,7 +581,7 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
   int wslot = 0;   // ring slot the next issue fills
   auto issue = [&]() {
     const uint32_t o = uint32_t(wslot * C::StageBytes);
-    dma_issue<C::PA>(sa, offa, ma0 + o);
+    dma_issue<C::PA, SEGA>(sa, offa, ma0 + o);
     dma_issue<C::PB>(sb, offb, mb0 + o);
     wslot = wslot + 1 == STAGES ? 0 : wslot + 1;
     ++issued;
@@ -750,14 +789,14 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
   }
 }
 
-template <class C, bool AK, bool BKM, class Epi>
+template <class C, bool AK, bool BKM, class Epi, bool SEGA>
 __global__ void __launch_bounds__(C::THREADS, C::OCC)
     gemm_pipe_kernel(View A, View B, int64_t M, int64_t N, int64_t K, int64_t ksplit,
                      TileMap tm, Epi epi) {
   __shared__ __attribute__((aligned(1024))) char lds[C::LdsBytes];
   TileCoord tc;
   if (!tile_coord(tm, blockIdx.x, tc)) return;  // uniform over the workgroup
-  run_tile<C, AK, BKM>(A, B, M, N, K, ksplit, tc, epi, lds);
+  run_tile<C, AK, BKM, Epi, SEGA>(A, B, M, N, K, ksplit, tc, epi, lds);
 }
 
 // C[M, N] = A · B over K with configuration C; `splits` > 1 cuts K into that many ranges
@@ -766,11 +805,14 @@ __global__ void __launch_bounds__(C::THREADS, C::OCC)
 // grid instead of a run of consecutive tiles: with n split xn ways (xn = 4, 2 or 1, the
 // first that divides the n-tile count) an XCD reads 1 / xn of B and xn / 8 of A; worth it
 // when B is re-read by every m-tile and too large for one L2.
-template <class C, bool AK, bool BKM, class Epi>
+template <class C, bool AK, bool BKM, class Epi, bool SEGA = false>
 hipError_t launch(const View& A, const View& B, int64_t M, int64_t N, int64_t K, int64_t splits,
                   bool m_fast, const Epi& epi, hipStream_t s, bool xcd_blocks = false) {
   // grouped K-major operands keep whole groups of 64 (see stream_at)
   if ((AK && A.gs < 64) || (BKM && B.gs < 64)) return hipErrorInvalidValue;
+  // a two-segment A: MN-major, both segments given, split at a slice boundary
+  if (SEGA && (AK || A.p2 == nullptr || A.kseg <= 0 || A.kseg % C::BK != 0 || A.kseg >= A.rows))
+    return hipErrorInvalidValue;
   TileMap tm{(M + C::BM - 1) / C::BM, (N + C::BN - 1) / C::BN, splits < 1 ? 1 : splits, m_fast};
   int64_t ksplit = (K + tm.splits - 1) / tm.splits;
   ksplit = (ksplit + C::BK - 1) / C::BK * C::BK;
@@ -780,7 +822,7 @@ hipError_t launch(const View& A, const View& B, int64_t M, int64_t N, int64_t K,
     const int64_t gm = 8 / tm.xn;
     grid = 8 * ((tm.m_tiles + gm - 1) / gm) * (tm.n_tiles / tm.xn);
   }
-  hipLaunchKernelGGL((gemm_pipe_kernel<C, AK, BKM, Epi>), dim3(unsigned(grid)),
+  hipLaunchKernelGGL((gemm_pipe_kernel<C, AK, BKM, Epi, SEGA>), dim3(unsigned(grid)),
                      dim3(C::THREADS), 0, s, A, B, M, N, K, ksplit, tm, epi);
   return hipGetLastError();
 }

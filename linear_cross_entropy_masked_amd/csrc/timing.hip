@@ -40,7 +40,7 @@ const char* kNames[K_COUNT] = {
     "flce_bias_grad",     "flce_to_probs",         "flce_gemm_grad_hidden",
     "flce_gemm_grad_weight", "flce_onehot_fix",    "fill_zero",
     "flce_grad_hidden_reduce", "flce_gemm_probs", "flce_label_sort",
-    "ce_fused_rows",      "flce_loss_acc",
+    "ce_fused_rows",      "flce_loss_acc",         "flce_probs_transposed",
 };
 
 }  // namespace

@@ -3,7 +3,8 @@ guard bands, and after the call the bands must be intact, the inputs unchanged b
 and (for the CE layer's strided rows) the columns v .. ld − 1 of every row untouched.
 
 The fused linear CE keeps its bookkeeping in the workspace slice's free halves and in
-grad_hidden rows it has not written yet; these tests run both schedules, both workspace
+grad_hidden rows it has not written yet, and may keep its probabilities in grad_weight's bytes
+before writing grad_weight; these tests run every schedule, both workspace
 layouts (the compact one whose workspace is the slice alone, and the extended one), paired and
 unpaired chunks, and the split calls, and check that nothing lands outside the buffers. The
 outputs are also checked against the oracle where the case is a parity case.
@@ -144,10 +145,17 @@ def test_ce_calls_stay_inside_their_buffers(dev, n, v, ld_extra):
 # -------------------------------------------------------------------------- fused layer
 
 FLCE_CASES = [
-    # n, h, v, chunk, bias, grad_bias, recompute, accumulate: paired 16-bit logits (even and
-    # odd chunk counts), paired recompute, unpaired recompute with grad_bias, the extended
-    # layout (h not a multiple of 64; chunks under 64 rows), V not a multiple of 64
+    # n, h, v, chunk, bias, grad_bias, recompute, accumulate: every row's probabilities kept
+    # transposed in grad_weight's bytes and the slice (two segments; four grad_weight ranges
+    # and padding tokens; grad_hidden split partials below them; all of Pᵀ in the slice),
+    # paired 16-bit logits (a batch too long for that, even and odd chunk counts), paired
+    # recompute, unpaired recompute with grad_bias, the extended layout (h not a multiple of
+    # 64; chunks under 64 rows), V not a multiple of 64
     (200, 128, 1500, 64, True, True, False, False),
+    (600, 320, 3001, 128, False, False, False, False),
+    (300, 256, 9000, 64, False, False, False, False),
+    (64, 64, 300, 64, True, True, False, False),
+    (512, 128, 3000, 128, True, True, False, False),
     (192, 128, 1500, 64, False, False, True, False),
     (300, 128, 2001, 100, True, True, True, True),
     (130, 40, 1000, 32, True, True, False, False),
