@@ -310,16 +310,19 @@ struct EpiGradHidden {
     dh[m * ldh + n] = f32_to_bf16(r);
   }
   // aux: the 4 weights W[y_m, n .. n+3] as two bf16 pairs and the row's label coefficient;
-  // ok = 0 for a row without label
+  // ok = 0 for a row without label. The row's label comes in as its tag (loaded once per
+  // tile) and the weight load does not branch on it (row 0 stands in for a row without a
+  // label), so the gathers of a batch are in flight together.
+  static constexpr bool kRowTag = true;
+  __device__ __forceinline__ int row_tag(int64_t m) const { return labels[m]; }
   struct Aux {
     uint32_t a, b, ok;
     float c;
   };
-  __device__ __forceinline__ Aux load4(int64_t m, int64_t n) const {
-    const int32_t y = labels[m];
-    if (!has_label(y, v, ignore_index)) return Aux{0u, 0u, 0u, 0.f};
-    const uint2 wy = *reinterpret_cast<const uint2*>(w + int64_t(y) * ldw + n);
-    return Aux{wy.x, wy.y, 1u, ycoef[m]};
+  __device__ __forceinline__ Aux load4t(int64_t m, int64_t n, int y) const {
+    const bool ok = has_label(y, v, ignore_index);
+    const uint2 wy = *reinterpret_cast<const uint2*>(w + (ok ? int64_t(y) : 0) * ldw + n);
+    return Aux{wy.x, wy.y, ok ? 1u : 0u, ycoef[m]};
   }
   __device__ __forceinline__ void store4(int64_t m, int64_t n, gemm::f32x4_t a, Aux x) {
     uint2 o = {0u, 0u};
@@ -1409,7 +1412,8 @@ hipError_t flce_transposed(const FlceArgs& a, const FlceWs& ws, int64_t chunk,
 
   // grad_hidden = g·s·(P · W − c·W[y]) over all rows, K = v (Pᵀ read MN-major, its rows in
   // two segments); split over K only when the row tiles alone do not fill the chip, the
-  // partials then in grad_weight's bytes below Pᵀ
+  // partials then in grad_weight's bytes below Pᵀ. (Leaving fp32 P · W there and applying
+  // the one-hot term in the streaming reduce pass measured no faster than the epilogue.)
   {
     View Ap{S > 0 ? pt1 : pt2, pl.ldp, kGroup, v, n};
     if (S > 0 && S < v) {
@@ -1418,16 +1422,18 @@ hipError_t flce_transposed(const FlceArgs& a, const FlceWs& ws, int64_t chunk,
     }
     View Bw2{a.weight, h, kGroup, v, h};
     const int64_t tiles = row_tiles(n) * ((h + Wide::BN - 1) / Wide::BN);
+    const int64_t room = pl.t0 / (8 * n * h);  // partial sets that fit below Pᵀ
     int64_t splits = 256 / tiles;
     if (splits > (v + 2047) / 2048) splits = (v + 2047) / 2048;
-    if (splits > pl.t0 / (8 * n * h)) splits = pl.t0 / (8 * n * h);
+    if (splits > room) splits = room;
     if (splits < 1) splits = 1;
+    const bool partials = splits > 1;
     float* part = reinterpret_cast<float*>(gwb);
     const RowVec yc{ycall, 0, 0};
     {
       TimedLaunch t(s, K_FLCE_GEMM_GRAD_HIDDEN);
       const bool two = S > 0 && S < v;
-      if (splits == 1) {
+      if (!partials) {
         EpiGradHidden eh{a.grad_hidden, h, a.labels, a.weight, h, v, a.ignore_index, cnt, th,
                          a.grad_output, 0.f, yc};
         e = two ? gemm::v2::launch<Wide, false, false, EpiGradHidden, true>(Ap, Bw2, n, h, v, 1,
@@ -1441,7 +1447,7 @@ hipError_t flce_transposed(const FlceArgs& a, const FlceWs& ws, int64_t chunk,
       }
       if (e != hipSuccess) return e;
     }
-    if (splits > 1) {
+    if (partials) {
       TimedLaunch t(s, K_FLCE_GRAD_HIDDEN_REDUCE);
       hipLaunchKernelGGL(grad_hidden_reduce_kernel, dim3(unsigned((n * h / 4 + 255) / 256)),
                          dim3(256), 0, s, part, n, h, splits, a.grad_hidden, a.labels, a.weight,

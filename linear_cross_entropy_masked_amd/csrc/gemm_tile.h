@@ -18,6 +18,8 @@
 // LDS is double-buffered, so one barrier per K-tile suffices.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace lce {
@@ -498,6 +500,19 @@ __device__ __forceinline__ void wait_slices(int s) {
   }
 }
 
+// Epilogues that set kRowTag get each row's row_tag (e.g. its label) loaded once per tile,
+// ahead of the epilogue's other loads, and receive it in load4t(m, n, tag) in place of
+// load4(m, n): loads that depend on the tag then issue together instead of each waiting for
+// its own tag load.
+template <class E, class = void>
+struct RowTagged {
+  static constexpr bool value = false;
+};
+template <class E>
+struct RowTagged<E, std::void_t<decltype(E::kRowTag)>> {
+  static constexpr bool value = E::kRowTag;
+};
+
 // Tile coordinates (m-tile, n-tile, K split) of workgroup w; false for a workgroup with no
 // tile (the XCD-block mapping pads every XCD to the largest block).
 struct TileCoord {
@@ -616,6 +631,7 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
   // over the WN wavefronts through LDS) and handed to every store of the row.
   // They also get a per-row tag (row_tag, e.g. the row's label), loaded here ahead of the
   // stores that use it.
+  constexpr bool kTagged = RowTagged<Epi>::value;
   float tmax[TM];
   int rtag[TM];
 #pragma unroll
@@ -623,12 +639,14 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
     tmax[i] = -INFINITY;
     rtag[i] = -1;
   }
-  if constexpr (Epi::kTileMax) {
+  if constexpr (Epi::kTileMax || kTagged) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int64_t gm = m0 + wm * (C::BM / C::WM) + 16 * i + (lane & 15);
       if (gm < M) rtag[i] = epi.row_tag(gm);
     }
+  }
+  if constexpr (Epi::kTileMax) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int64_t gm = m0 + wm * (C::BM / C::WM) + 16 * i + (lane & 15);
@@ -686,7 +704,12 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int64_t gn = n0 + wn * (C::BN / C::WN) + 16 * j + 4 * (lane >> 4);
-        if (gm < M && gn + 4 <= N) aux[di][j] = epi.load4(gm, gn);
+        if (gm < M && gn + 4 <= N) {
+          if constexpr (kTagged)
+            aux[di][j] = epi.load4t(gm, gn, rtag[i0 + di]);
+          else
+            aux[di][j] = epi.load4(gm, gn);
+        }
       }
     }
 #pragma unroll
