@@ -80,6 +80,7 @@ KERNEL_NAMES = [
     ("EpiPartial", "flce_gemm_grad_hidden"), ("EpiGradWeight", "flce_gemm_grad_weight"),
     ("slice_row_lse_kernel", "flce_row_lse"), ("slice_bias_grad_kernel", "flce_bias_grad"),
     ("slice_to_probs_kernel", "flce_to_probs"), ("shifted_to_probs_kernel", "flce_to_probs"),
+    ("shifted_to_probs_t_kernel", "flce_probs_transposed"),
     ("shifted_bias_grad_kernel", "flce_bias_grad"), ("onehot_weight_fix_kernel", "flce_onehot_fix"),
     ("grad_hidden_reduce_kernel", "flce_grad_hidden_reduce"), ("fill_zero", "fill_zero"),
     ("label_rank_kernel", "flce_label_sort"), ("label_prep_kernel", "label_prep"),
@@ -152,6 +153,8 @@ def record_traffic(workload, fetch_dir, write_dir):
         with open(path) as f:
             table = json.load(f)
     digest = source_digest()
+    # a recording replaces the workload's earlier one (kernels a schedule no longer runs go)
+    table = {k: v for k, v in table.items() if not k.endswith("@" + workload)}
     for name, rec in out.items():
         rd, wr = rec.get("read_bytes", 0.0), rec.get("write_bytes", 0.0)
         table[f"{name}@{workload}"] = {
@@ -208,6 +211,7 @@ def record_mfma(workload, pmc_dir, trace_dir):
         with open(path) as f:
             table = json.load(f)
     digest = source_digest()
+    table = {k: v for k, v in table.items() if not k.endswith("@" + workload)}
     for k, d in sums.items():
         mops = d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
         name = next((n for sub, n in KERNEL_NAMES if sub in k), None)
@@ -291,33 +295,31 @@ def make_flush(torch, dev):
     return flush
 
 
-def gemm_bytes(kernel, w, stored_slice=True):
-    """Algorithmic HBM bytes of one launch of an FLCE product: each operand read once, each
-    result written once. The stored-logits schedule writes each chunk's logits as 16-bit
-    shifted values; the recomputing schedule stores none. At the benchmark's workloads both
-    run grad_weight once per two chunks (K = 2C). grad_weight adds its fp32 accumulator:
-    written by the first launch, read and written by the others (averaged over the
-    launches)."""
-    c, h, v = w.chunk_size, w.h, w.v
+def gemm_bytes(kernel, w, launches, stored_slice=True, transposed=False):
+    """Algorithmic HBM bytes of one launch of an FLCE product (averaged over its `launches`
+    per step): each operand read once, each result written once. The stored-logits schedules
+    write each chunk's logits as 16-bit shifted values; the recomputing schedule stores none.
+    Paired chunks: grad_hidden per chunk, grad_weight once per two chunks (K = 2C) adding
+    into its fp32 accumulator (written by the first launch, read and written by the others).
+    Transposed probabilities (every row's kept at once): grad_hidden is one product over all
+    rows, grad_weight one product per vocabulary range over all rows (K = n), each reading
+    the hidden rows and writing its range of grad_weight once."""
+    c, h, v, n = w.chunk_size, w.h, w.v, w.n
     if kernel == "flce_gemm_logits":  # W and the hidden chunk in; 16-bit logits out (stored)
         return 2 * v * h + 2 * c * h + (2 * c * v if stored_slice else 0)
     if kernel == "flce_gemm_probs":  # W and the hidden chunk in; bf16 probabilities out
         return 2 * v * h + 2 * c * h + 2 * c * v
     if kernel == "flce_gemm_grad_hidden":  # probabilities and W in; grad_hidden rows out
+        if transposed:
+            return (2 * n * v + 2 * v * h + 2 * n * h) / launches
         return 2 * c * v + 2 * v * h + 2 * c * h
-    if kernel == "flce_gemm_grad_weight":  # probabilities and hidden in; fp32 accumulator
-        launches = grad_weight_launches(w)
-        k = w.n / launches
+    if kernel == "flce_gemm_grad_weight":  # probabilities and hidden in; fp32 grad_weight
+        if transposed:
+            return (2 * n * v + 2 * n * h * launches + 4 * v * h) / launches
+        k = n / launches
         acc = (4 + 8 * (launches - 1)) * v * h / launches
         return 2 * k * v + 2 * k * h + acc
     raise KeyError(kernel)
-
-
-def grad_weight_launches(w):
-    """Both schedules keep two chunks per slice here (h a multiple of 64, chunk >= 64,
-    grad_hidden asked for, no grad_bias): one grad_weight launch per two chunks."""
-    chunks = -(-w.n // w.chunk_size)
-    return -(-chunks // 2)
 
 
 def gemm_roofline(kernel, flops, nbytes, avg_ms):
@@ -399,19 +401,21 @@ def run_flce(args, torch, lce, workloads, name=None, recompute=False, steps=None
 
     flops = 6.0 * w.n * w.h * w.v
     chunks = -(-w.n // w.chunk_size)
-    one = 2.0 * w.chunk_size * w.h * w.v  # one chunk's product (every chunk is full here)
-    # algorithmic flops per launch of each MFMA kernel: one chunk's product, grad_weight's
-    # over the rows of its launch (two chunks)
-    per_launch = {"flce_gemm_logits": one, "flce_gemm_probs": one,
-                  "flce_gemm_grad_hidden": one,
-                  "flce_gemm_grad_weight": 2.0 * w.n * w.h * w.v / grad_weight_launches(w)}
-    gemms = [k for k in kernels if k[0] in per_launch]
+    # each MFMA kernel does one 2·n·h·v product per step (the logits twice when recomputing:
+    # two kernels), over however many launches the schedule splits it into; per launch the
+    # algorithmic flops and bytes are averaged over those launches
+    gemm_names = ("flce_gemm_logits", "flce_gemm_probs", "flce_gemm_grad_hidden",
+                  "flce_gemm_grad_weight")
+    transposed = any(k[0] == "flce_probs_transposed" for k in kernels)
+    gemms = [k for k in kernels if k[0] in gemm_names]
     dom = max(gemms, key=lambda k: k[1]) if gemms else None
     roof = None
     if dom:
         avg_ms = dom[1] / dom[2]
-        roof = gemm_roofline(dom[0], per_launch[dom[0]],
-                             gemm_bytes(dom[0], w, stored_slice=not recompute), avg_ms)
+        launches = dom[2] // kreps
+        roof = gemm_roofline(dom[0], 2.0 * w.n * w.h * w.v / launches,
+                             gemm_bytes(dom[0], w, launches, stored_slice=not recompute,
+                                        transposed=transposed), avg_ms)
         roof["traffic"] = stored_traffic(dom[0], w.name)
         roof["mfma_counters"] = stored_mfma(dom[0], w.name)
     executed = (8.0 if recompute else 6.0) * w.n * w.h * w.v

@@ -34,15 +34,23 @@ def test_ce_algorithmic_bytes_at_the_large_vocabulary_workload():
 def test_flce_launch_pricing_at_the_llama3_head():
     w = workloads.WORKLOADS["flce_8192x4096x128256"]
     n, h, v = w.n, w.h, w.v
-    assert bench.grad_weight_launches(w) == 4  # 8 chunks of 1024, two per launch
+    # paired chunks: four grad_weight launches of K = 2048; probabilities and hidden rows
+    # once, the accumulator written by the first launch and read and written by the other
+    # three: (4 + 3 * 8) / 4 = 7 bytes per element
     k = 2048
-    # probabilities and hidden rows once; accumulator written by the first of the four
-    # launches, read and written by the other three: (4 + 3 * 8) / 4 = 7 bytes per element
-    assert bench.gemm_bytes("flce_gemm_grad_weight", w) == 2 * k * v + 2 * k * h + 7 * v * h
-    assert bench.gemm_bytes("flce_gemm_logits", w) == 2 * v * h + 2 * 1024 * h + 2 * 1024 * v
-    assert bench.gemm_bytes("flce_gemm_logits", w, stored_slice=False) == 2 * v * h + 2 * 1024 * h
-    lc = workloads.WORKLOADS["flce_32768x8192x128256_packed"]
-    assert bench.grad_weight_launches(lc) == 8
+    assert bench.gemm_bytes("flce_gemm_grad_weight", w, 4) == 2 * k * v + 2 * k * h + 7 * v * h
+    assert bench.gemm_bytes("flce_gemm_grad_hidden", w, 8) == 2 * 1024 * v + 2 * v * h + 2 * 1024 * h
+    # transposed probabilities: five grad_weight launches over vocabulary ranges, K = n; all
+    # of Pᵀ once, the hidden rows once per launch, grad_weight written once
+    assert bench.gemm_bytes("flce_gemm_grad_weight", w, 5, transposed=True) == \
+        (2 * n * v + 5 * 2 * n * h + 4 * v * h) / 5
+    assert bench.gemm_bytes("flce_gemm_grad_hidden", w, 1, transposed=True) == \
+        2 * n * v + 2 * v * h + 2 * n * h
+    # the logits product is the same in both
+    for t in (False, True):
+        assert bench.gemm_bytes("flce_gemm_logits", w, 8, transposed=t) == \
+            2 * v * h + 2 * 1024 * h + 2 * 1024 * v
+    assert bench.gemm_bytes("flce_gemm_logits", w, 8, stored_slice=False) == 2 * v * h + 2 * 1024 * h
 
 
 def test_roofline_takes_the_higher_floor():
@@ -50,7 +58,7 @@ def test_roofline_takes_the_higher_floor():
     # above the 312.5 flop/B ridge: MFMA-bound
     w = workloads.WORKLOADS["flce_8192x4096x128256"]
     flops = 2.0 * 2048 * w.h * w.v
-    nbytes = bench.gemm_bytes("flce_gemm_grad_weight", w)
+    nbytes = bench.gemm_bytes("flce_gemm_grad_weight", w, 4)
     r = bench.gemm_roofline("flce_gemm_grad_weight", flops, nbytes, 2.0)
     assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s"
     assert r["achieved"] == pytest.approx(flops / 2e-3 / 1e12, rel=1e-3)
