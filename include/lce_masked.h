@@ -220,10 +220,14 @@ int ce_rows_bwd(const uint16_t* logits, int64_t n, int64_t v, int64_t ld, uint16
  * layout two chunks share the slice and grad_weight is formed once per two chunks: the
  * stored-logits schedule keeps each chunk's logits as 16-bit values (fp16 of z minus the
  * row's maximum over a 256-column tile); the recomputing schedule (and flce_bwd) keeps each
- * chunk's bf16 probabilities, when grad_hidden is asked for and grad_bias is not. Otherwise
- * a few words per chunk row sit beside the slice (lse, label logit, loss term and one
- * (max, sum) pair per 256-column tile); nothing grows with n. Host-only; safe without a
- * GPU. */
+ * chunk's bf16 probabilities, when grad_hidden is asked for and grad_bias is not. When the
+ * stored-logits schedule overwrites grad_weight (no FLCE_ACCUMULATE), chunk_size is a
+ * multiple of 64 and the batch is short enough (about n <= 2h), every row's bf16
+ * probabilities are kept at once, transposed, in the slice and in grad_weight's own bytes,
+ * and grad_hidden and grad_weight are each formed by products over the whole batch (the
+ * fp32 working set is still the one slice). Otherwise a few words per chunk row sit beside
+ * the slice (lse, label logit, loss term and one (max, sum) pair per 256-column tile);
+ * nothing grows with n. Host-only; safe without a GPU. */
 int flce_workspace_size(int64_t n, int64_t h, int64_t v, int64_t chunk_size, uint32_t flags,
                         size_t* bytes);
 
@@ -248,10 +252,10 @@ int flce_workspace_size(int64_t n, int64_t h, int64_t v, int64_t chunk_size, uin
  * a relative error of at most exp(2^-11 · (max_v z − z)) − 1; lse and loss always come from
  * the fp32 logits. The loss adds the rows' terms in row order in fp64, so it does not
  * depend on chunk_size.
- * grad_hidden also serves as scratch before its rows are written (see flce_workspace_size):
- * its contents are defined only once the call has run, and a grad_hidden that overlaps any
- * other buffer of the call (hidden included: there is no in-place form) is refused with
- * LCE_ERR_OVERLAP. */
+ * grad_hidden also serves as scratch before its rows are written, and so does grad_weight
+ * when it is overwritten (see flce_workspace_size): their contents are defined only once
+ * the call has run, and a grad_hidden that overlaps any other buffer of the call (hidden
+ * included: there is no in-place form) is refused with LCE_ERR_OVERLAP. */
 int flce_fwd_bwd(const uint16_t* hidden, const uint16_t* weight, const float* bias,
                  const int32_t* labels, int64_t n, int64_t h, int64_t v, int32_t ignore_index,
                  int64_t chunk_size, int64_t num_label_tokens, uint32_t flags,
