@@ -618,12 +618,15 @@ __global__ void __launch_bounds__(256) lse_merge_rows_kernel(
   }
 }
 
-// grad_bias[v] (=|+=) coef · (Σ_{labelled i} p_iv − #{i: y_i = v}). One workgroup per 64
-// columns: each of its 16 wavefronts takes every 16th row of the chunk (lane = column, so a
-// row's 64 columns are one coalesced access and the row's label and shift are wavefront
-// uniform), then the 16 partial sums of a column are added in wavefront order through LDS:
-// the same order on every run. `prob(i, col)` is p_iv in fp32, before any bf16 rounding.
-constexpr int kBiasCols = 64, kBiasWaves = 16;
+// grad_bias[v] (=|+=) coef · (Σ_{labelled i} p_iv − #{i: y_i = v}). One 1024-thread
+// workgroup per 128 columns: lane l of wavefront w takes the 8 columns 8 (l % 16) .. + 7 of
+// the block (one 16-byte load per row) over the rows i ≡ 4 w + l / 16 (mod 64), in
+// increasing order, four rows' loads in flight; the 64 partial sums of a column are then
+// added in residue order through LDS, the same order on every run.
+// prob.load8(i, c0, p) gives p_iv in fp32 (before any bf16 rounding) for the 8 columns
+// c0 .. c0 + 7, c0 < v and c0 + 8 <= ldz.
+constexpr int kBiasCols = 64, kBiasWaves = 16;  // bias_from_colsums_kernel
+constexpr int kBiasBlockCols = 128, kBiasThreads = 1024, kBiasParts = 64;
 
 template <class Prob>
 __device__ __forceinline__ void bias_grad_columns(const Prob& prob, int64_t rows, int64_t v,
@@ -631,49 +634,78 @@ __device__ __forceinline__ void bias_grad_columns(const Prob& prob, int64_t rows
                                                   int32_t ignore_index, float* grad_bias,
                                                   int overwrite, const long long* count_dev,
                                                   long long count_host, const float* gout) {
-  __shared__ float ps[kBiasWaves][kBiasCols];
-  __shared__ int pc[kBiasWaves][kBiasCols];
+  __shared__ float ps[kBiasParts][kBiasBlockCols];
+  __shared__ int pc[kBiasParts][kBiasBlockCols];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int64_t col = int64_t(blockIdx.x) * kBiasCols + lane;
-  float sp = 0.f;
-  int cnt = 0;
-  if (col < v) {
-#pragma unroll 4
-    for (int64_t i = wv; i < rows; i += kBiasWaves) {
-      const int32_t y = labels[i];
-      if (has_label(y, v, ignore_index)) {
-        sp += prob(i, col);
-        cnt += (int64_t(y) == col);
+  const int cg = lane & 15, part = 4 * wv + (lane >> 4);
+  const int64_t c0 = int64_t(blockIdx.x) * kBiasBlockCols + 8 * cg;
+  float sp[8];
+  int cnt[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    sp[q] = 0.f;
+    cnt[q] = 0;
+  }
+  if (c0 < v) {
+    for (int64_t i0 = part; i0 < rows; i0 += 4 * kBiasParts) {
+      int32_t y[4];
+      float p[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t i = i0 + u * kBiasParts;
+        y[u] = i < rows ? labels[i] : -1;
+        if (i < rows) prob.load8(i, c0, p[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (!has_label(y[u], v, ignore_index)) continue;
+        const int64_t d = int64_t(y[u]) - c0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          if (c0 + q < v) sp[q] += p[u][q];
+          cnt[q] += d == q;
+        }
       }
     }
   }
-  ps[wv][lane] = sp;
-  pc[wv][lane] = cnt;
-  __syncthreads();
-  if (wv == 0 && col < v) {
-    float s = 0.f;
-    int c = 0;
 #pragma unroll
-    for (int w = 0; w < kBiasWaves; ++w) {
-      s += ps[w][lane];
-      c += pc[w][lane];
+  for (int q = 0; q < 8; ++q) {
+    ps[part][8 * cg + q] = sp[q];
+    pc[part][8 * cg + q] = cnt[q];
+  }
+  __syncthreads();
+  if (threadIdx.x < kBiasBlockCols) {
+    const int64_t col = int64_t(blockIdx.x) * kBiasBlockCols + threadIdx.x;
+    if (col < v) {
+      float s = 0.f;
+      int c = 0;
+#pragma unroll 8
+      for (int r = 0; r < kBiasParts; ++r) {
+        s += ps[r][threadIdx.x];
+        c += pc[r][threadIdx.x];
+      }
+      const float d = flce_coef(count_dev, count_host, gout) * (s - float(c));
+      grad_bias[col] = overwrite ? d : grad_bias[col] + d;
     }
-    const float d = flce_coef(count_dev, count_host, gout) * (s - float(c));
-    grad_bias[col] = overwrite ? d : grad_bias[col] + d;
   }
 }
 
-// p from the fp32 slice: exp(z − lse).
+// p from the fp32 slice: exp(z − lse) (rows of 64-column groups, so c0 is 32-byte aligned).
 struct SliceProb {
   const float* z;
   int64_t ldz;
   const float* lse_c;
-  __device__ __forceinline__ float operator()(int64_t i, int64_t col) const {
-    return fast_exp2((z[i * ldz + col] - lse_c[i]) * kLog2e);
+  __device__ __forceinline__ void load8(int64_t i, int64_t c0, float (&p)[8]) const {
+    const float4 a = *reinterpret_cast<const float4*>(z + i * ldz + c0);
+    const float4 b = *reinterpret_cast<const float4*>(z + i * ldz + c0 + 4);
+    const float c = lse_c[i];
+    const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) p[q] = fast_exp2((x[q] - c) * kLog2e);
   }
 };
 
-__global__ void __launch_bounds__(64 * kBiasWaves) slice_bias_grad_kernel(
+__global__ void __launch_bounds__(kBiasThreads) slice_bias_grad_kernel(
     const float* __restrict__ z, int64_t ldz, int64_t rows, int64_t v,
     const int32_t* __restrict__ labels, int32_t ignore_index, const float* __restrict__ lse_c,
     float* __restrict__ grad_bias, int overwrite, const long long* count_dev,
@@ -827,20 +859,24 @@ __global__ void __launch_bounds__(256) shifted_to_probs_t_kernel(
 
 // p from the shifted 16-bit logits d = fp16(z − m_t): exp(d + m_t − lse) in fp32 (the
 // probability before its bf16 rounding); m_t is the row's maximum over the column's 256-wide
-// tile t, uniform over a wavefront's 64 columns.
+// tile t, the same for the 8 columns of one load.
 struct ShiftedProb {
   const uint16_t* z;
   int64_t ldz;
   const float* lse_c;
   const float2* part;
   int64_t tiles;
-  __device__ __forceinline__ float operator()(int64_t i, int64_t col) const {
-    const float d = f16_to_f32(z[i * ldz + col]);
-    return fast_exp2((d + (part[i * tiles + (col >> 8)].x - lse_c[i])) * kLog2e);
+  __device__ __forceinline__ void load8(int64_t i, int64_t c0, float (&p)[8]) const {
+    const uint4 x = *reinterpret_cast<const uint4*>(z + i * ldz + c0);
+    const float sh = part[i * tiles + (c0 >> 8)].x - lse_c[i];
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      p[q] = fast_exp2((f16_to_f32(w[q >> 1] >> (16 * (q & 1))) + sh) * kLog2e);
   }
 };
 
-__global__ void __launch_bounds__(64 * kBiasWaves) shifted_bias_grad_kernel(
+__global__ void __launch_bounds__(kBiasThreads) shifted_bias_grad_kernel(
     const uint16_t* __restrict__ z, int64_t ldz, int64_t rows, int64_t v,
     const int32_t* __restrict__ labels, int32_t ignore_index, const float* __restrict__ lse_c,
     const float2* __restrict__ part, int64_t tiles, float* __restrict__ grad_bias, int overwrite,
@@ -1125,8 +1161,9 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
     }
     if (a.grad_bias) {
       TimedLaunch t(s, K_FLCE_BIAS_GRAD);
-      hipLaunchKernelGGL(shifted_bias_grad_kernel, dim3(unsigned((v + kBiasCols - 1) / kBiasCols)),
-                         dim3(64 * kBiasWaves), 0,
+      hipLaunchKernelGGL(shifted_bias_grad_kernel,
+                         dim3(unsigned((v + kBiasBlockCols - 1) / kBiasBlockCols)),
+                         dim3(kBiasThreads), 0,
                          s, half[hf], ws.ldz, rows, v, lab, a.ignore_index, lse_c, part,
                          ws.tiles, a.grad_bias, int(first && !accumulate), &st->count, th,
                          a.grad_output);
@@ -1397,8 +1434,9 @@ hipError_t flce_transposed(const FlceArgs& a, const FlceWs& ws, int64_t chunk,
     }
     if (a.grad_bias) {
       TimedLaunch t(s, K_FLCE_BIAS_GRAD);
-      hipLaunchKernelGGL(shifted_bias_grad_kernel, dim3(unsigned((v + kBiasCols - 1) / kBiasCols)),
-                         dim3(64 * kBiasWaves), 0, s, z16, ws.ldz, rows, v, lab, a.ignore_index,
+      hipLaunchKernelGGL(shifted_bias_grad_kernel,
+                         dim3(unsigned((v + kBiasBlockCols - 1) / kBiasBlockCols)),
+                         dim3(kBiasThreads), 0, s, z16, ws.ldz, rows, v, lab, a.ignore_index,
                          lse_c, part, ws.tiles, a.grad_bias, int(first), cnt, th, a.grad_output);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -1642,8 +1680,9 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
       // 3. bias gradient from the fp32 logits
       if (a.grad_bias) {
         TimedLaunch t(s, K_FLCE_BIAS_GRAD);
-        hipLaunchKernelGGL(slice_bias_grad_kernel, dim3(unsigned((v + kBiasCols - 1) / kBiasCols)),
-                           dim3(64 * kBiasWaves), 0,
+        hipLaunchKernelGGL(slice_bias_grad_kernel,
+                           dim3(unsigned((v + kBiasBlockCols - 1) / kBiasBlockCols)),
+                           dim3(kBiasThreads), 0,
                            s, ws.slice, ws.ldz, rows, v, lab, a.ignore_index, lse_c,
                            a.grad_bias, int(first && !accumulate), &st->count, th, a.grad_output);
         if ((e = hipGetLastError()) != hipSuccess) return e;
