@@ -447,6 +447,9 @@ __global__ void __launch_bounds__(256) onehot_segments_kernel(
 }
 
 
+// grad_hidden's fp32 split-K partial sums: element e of split z at float dense ? z·M·N + e :
+// gap_index(z·M·N + e) of `slice` (the free halves of the slice's 64-column groups, or a
+// region of its own).
 struct EpiPartial {
   static constexpr bool kColSums = false;
   static constexpr bool kTileMax = false;
@@ -454,15 +457,17 @@ struct EpiPartial {
   float* slice;
   int64_t M, N;
   int64_t kz;
+  int dense;
   __device__ void begin(int64_t z) { kz = z; }
+  __device__ __forceinline__ int64_t at(int64_t e) const { return dense ? e : gap_index(e); }
   __device__ __forceinline__ void operator()(int64_t m, int64_t n, float a) {
-    slice[gap_index((kz * M + m) * N + n)] = a;
+    slice[at((kz * M + m) * N + n)] = a;
   }
   struct Aux {};
   __device__ __forceinline__ Aux load4(int64_t, int64_t) const { return Aux{}; }
   // N % 4 == 0 and n % 4 == 0 keep the 4 values inside one 32-float gap
   __device__ __forceinline__ void store4(int64_t m, int64_t n, gemm::f32x4_t a, Aux) {
-    *reinterpret_cast<gemm::f32x4_t*>(slice + gap_index((kz * M + m) * N + n)) = a;
+    *reinterpret_cast<gemm::f32x4_t*>(slice + at((kz * M + m) * N + n)) = a;
   }
 };
 
@@ -470,7 +475,7 @@ struct EpiPartial {
 // lane takes 4 consecutive elements (N % 4 == 0: a 16-byte read of each split's partials,
 // which stay inside one 32-float gap, 8-byte accesses to W and dH).
 __global__ void __launch_bounds__(256) grad_hidden_reduce_kernel(
-    const float* __restrict__ slice, int64_t M, int64_t N, int64_t splits,
+    const float* __restrict__ slice, int dense, int64_t M, int64_t N, int64_t splits,
     uint16_t* __restrict__ dh, const int32_t* __restrict__ labels, const uint16_t* __restrict__ w,
     int64_t v, int32_t ignore_index, const long long* count_dev, long long count_host,
     const float* gout, RowVec ycoef) {
@@ -482,7 +487,8 @@ __global__ void __launch_bounds__(256) grad_hidden_reduce_kernel(
   if (has_label(y, v, ignore_index)) {
     float4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int64_t z = 0; z < splits; ++z) {
-      const float4 p = *reinterpret_cast<const float4*>(slice + gap_index(z * M * N + e));
+      const int64_t f = z * M * N + e;
+      const float4 p = *reinterpret_cast<const float4*>(slice + (dense ? f : gap_index(f)));
       acc.x += p.x;
       acc.y += p.y;
       acc.z += p.z;
@@ -1096,6 +1102,8 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
                              reinterpret_cast<uint16_t*>(ws.slice) + chunk * ws.ldz};
   const int64_t half_bytes = chunk * ws.ldz * 2;
   constexpr int64_t kStateReserve = 256;  // end of a half kept for the moved call state
+  // before it, the label coefficients of the chunk whose grad_hidden runs from that half
+  const int64_t coef_off = half_bytes / 4 - kStateReserve / 4 - round_up(chunk, 64);
   hipError_t e;
 
   const RowVec none{nullptr, 0, 0};
@@ -1191,11 +1199,12 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
     View Ap{half[hf], ws.ldz, kGroup, rows, v};  // P: rows = chunk rows, cols = vocab (K-major)
     View Bw2{a.weight, h, kGroup, v, h};         // W: rows = k (vocab), cols = n (hidden)
     const int64_t tiles = row_tiles(rows) * ((h + Wide::BN - 1) / Wide::BN);
-    // partial element e of split z sits at float gap_index(z · rows · h + e) of `other`
-    const int64_t gap_cap = (half_bytes - kStateReserve) / (8 * rows * h);
+    // partial element e of split z sits at float z · rows · h + e of `other`, short of the
+    // label coefficients and the state reserve at its end
+    const int64_t cap = coef_off / (rows * h);
     int64_t splits = 256 / tiles;
-    if (splits > gap_cap) splits = gap_cap;
-    if (splits > (v + 2047) / 2048) splits = (v + 2047) / 2048;  // keep >= 2048 of K per split
+    if (splits > cap) splits = cap;
+    if (splits > (v + 1023) / 1024) splits = (v + 1023) / 1024;  // keep >= 1024 of K per split
     if (splits < 1) splits = 1;
     const long long* cnt = &st->count;
     uint16_t* dh = a.grad_hidden + c0 * h;
@@ -1207,7 +1216,7 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
                          yc};
         r = gemm::v2::launch<Wide, true, false>(Ap, Bw2, rows, h, v, 1, true, eh, s);
       } else {
-        EpiPartial ep{other, rows, h, 0};
+        EpiPartial ep{other, rows, h, 0, 1};
         r = gemm::v2::launch<Wide, true, false>(Ap, Bw2, rows, h, v, splits, true, ep, s);
       }
       if (r != hipSuccess) return r;
@@ -1215,7 +1224,7 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
     if (splits == 1) return hipSuccess;
     TimedLaunch t(s, K_FLCE_GRAD_HIDDEN_REDUCE);
     hipLaunchKernelGGL(grad_hidden_reduce_kernel, dim3(unsigned((rows * h / 4 + 255) / 256)),
-                       dim3(256), 0, s, other, rows, h, splits, dh, lab, a.weight, v,
+                       dim3(256), 0, s, other, 1, rows, h, splits, dh, lab, a.weight, v,
                        a.ignore_index, cnt, th, a.grad_output, yc);
     return hipGetLastError();
   };
@@ -1254,13 +1263,13 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
     return hipGetLastError();
   };
 
-  // Label coefficients (label_coef) of a pair's rows: A's go to the first halves of half 1's
-  // groups (clear of the partials of A's grad_hidden, which take the second halves) and, when
-  // the pair has a B, beside B's bookkeeping in B's grad_hidden rows, where B's follow; the
-  // one-hot term of grad_weight reads them there. B's are then copied into the first halves
-  // of half 0's groups (free once grad_weight is done) for B's grad_hidden, which overwrites
-  // B's rows. A B whose rows cannot hold the pair's coefficients beside its bookkeeping (a
-  // short last chunk) starts a pair of its own.
+  // Label coefficients (label_coef) of a pair's rows: A's go to the end of half 1 (before its
+  // state reserve; A's grad_hidden partials stop short of them) and, when the pair has a B,
+  // beside B's bookkeeping in B's grad_hidden rows, where B's follow; the one-hot term of
+  // grad_weight reads them there. B's are then copied to the end of half 0 (free once
+  // grad_weight is done) for B's grad_hidden, which overwrites B's rows. A B whose rows
+  // cannot hold the pair's coefficients beside its bookkeeping (a short last chunk) starts a
+  // pair of its own.
   for (int64_t c0 = 0, ra = 0, rb = 0; c0 < n; c0 += ra + rb) {
     ra = n - c0 < chunk ? n - c0 : chunk;
     const int64_t rest = n - c0 - ra;
@@ -1275,8 +1284,8 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
         rb = 0;
     }
     const bool first = c0 == 0;
-    const RowVec in_half1{reinterpret_cast<float*>(half[1]), 0, 1};
-    const RowVec in_half0{reinterpret_cast<float*>(half[0]), 0, 1};
+    const RowVec in_half1{reinterpret_cast<float*>(half[1]) + coef_off, 0, 0};
+    const RowVec in_half0{reinterpret_cast<float*>(half[0]) + coef_off, 0, 0};
     const RowVec pair_a{pair_coef, 0, 0};
     if ((e = front(c0, ra, 0, first, in_half1, pair_coef ? pair_a : none)) != hipSuccess)
       return e;
@@ -1478,7 +1487,7 @@ hipError_t flce_transposed(const FlceArgs& a, const FlceWs& ws, int64_t chunk,
                                                                              true, eh, s, true)
                 : gemm::v2::launch<Wide, false, false>(Ap, Bw2, n, h, v, 1, true, eh, s, true);
       } else {
-        EpiPartial ep{part, n, h, 0};
+        EpiPartial ep{part, n, h, 0, 0};
         e = two ? gemm::v2::launch<Wide, false, false, EpiPartial, true>(Ap, Bw2, n, h, v,
                                                                           splits, true, ep, s)
                 : gemm::v2::launch<Wide, false, false>(Ap, Bw2, n, h, v, splits, true, ep, s);
@@ -1488,7 +1497,7 @@ hipError_t flce_transposed(const FlceArgs& a, const FlceWs& ws, int64_t chunk,
     if (partials) {
       TimedLaunch t(s, K_FLCE_GRAD_HIDDEN_REDUCE);
       hipLaunchKernelGGL(grad_hidden_reduce_kernel, dim3(unsigned((n * h / 4 + 255) / 256)),
-                         dim3(256), 0, s, part, n, h, splits, a.grad_hidden, a.labels, a.weight,
+                         dim3(256), 0, s, part, 0, n, h, splits, a.grad_hidden, a.labels, a.weight,
                          v, a.ignore_index, cnt, th, a.grad_output, yc);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -1762,7 +1771,7 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     const long long* cnt = &st->count;
     EpiGradHidden eh{a.grad_hidden + c0 * h, h, lab, a.weight, h, v, a.ignore_index,
                      cnt, th, a.grad_output, 0.f, yc};
-    EpiPartial ep{ws.slice, rows, h, 0};
+    EpiPartial ep{ws.slice, rows, h, 0, 0};
     EpiGradWeight ew{a.grad_weight, h, int(first && !accumulate), cnt, th, a.grad_output, 0.f};
     if (a.grad_hidden) {
       TimedLaunch t(s, K_FLCE_GEMM_GRAD_HIDDEN);
@@ -1779,7 +1788,7 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     if (a.grad_hidden && splits > 1) {
       TimedLaunch t(s, K_FLCE_GRAD_HIDDEN_REDUCE);
       hipLaunchKernelGGL(grad_hidden_reduce_kernel, dim3(unsigned((rows * h / 4 + 255) / 256)),
-                         dim3(256), 0, s, ws.slice, rows, h, splits, a.grad_hidden + c0 * h, lab,
+                         dim3(256), 0, s, ws.slice, 0, rows, h, splits, a.grad_hidden + c0 * h, lab,
                          a.weight, v, a.ignore_index, cnt, th, a.grad_output, yc);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
