@@ -1333,7 +1333,7 @@ struct TransposedPlan {
   int64_t ldp;             // Pᵀ row length: n rounded up to 64 tokens
   int64_t seg;             // S: Pᵀ rows [0, S) in grad_weight's bytes, [S, v) in the slice
   int64_t t0;              // byte offset of Pᵀ row 0 in grad_weight
-  int64_t yc_off, st_off;  // slice byte offsets of the label coefficients and the call state
+  int64_t yc_off, lt_off, st_off;  // slice byte offsets: label coefficients, loss terms, state
   int nr;                  // grad_weight launches
   int64_t r[kMaxRanges + 1];
 };
@@ -1345,9 +1345,10 @@ bool plan_transposed(int64_t n, int64_t h, int64_t v, int64_t c, int64_t ldz, in
     return false;
   p.ldp = round_up(n, 64);
   const int64_t pb = 2 * p.ldp, wb = 4 * h;
-  // the slice's tail: label coefficients (n floats) and the state; its head also takes the
-  // sorted labels of the one-hot pass (2 · kSortMax ints) once grad_weight is done
-  const int64_t tail = int64_t(align256(size_t(n) * 4)) + 256;
+  // the slice's tail: label coefficients and loss terms (n floats each) and the state; its
+  // head also takes the sorted labels of the one-hot pass (2 · kSortMax ints) once
+  // grad_weight is done
+  const int64_t tail = 2 * int64_t(align256(size_t(n) * 4)) + 256;
   const int64_t head_min = 2 * kSortMax * 4;
   const int64_t e_max = (slice_bytes - tail - 256) / pb;  // Pᵀ rows the slice can take
   if (e_max < 1) return false;
@@ -1366,7 +1367,8 @@ bool plan_transposed(int64_t n, int64_t h, int64_t v, int64_t c, int64_t ldz, in
   p.seg = S;
   p.t0 = v * wb - S * pb;
   p.yc_off = std::max<int64_t>(int64_t(align256(size_t((v - S) * pb))), head_min);
-  p.st_off = p.yc_off + int64_t(align256(size_t(n) * 4));
+  p.lt_off = p.yc_off + int64_t(align256(size_t(n) * 4));
+  p.st_off = p.lt_off + int64_t(align256(size_t(n) * 4));
   if (p.st_off + 256 > slice_bytes) return false;
   // grad_weight ranges over the rows in grad_weight's bytes, then the slice's rows
   p.nr = 0;
@@ -1402,6 +1404,7 @@ hipError_t flce_transposed(const FlceArgs& a, const FlceWs& ws, int64_t chunk,
   uint16_t* const pt1 = reinterpret_cast<uint16_t*>(gwb + pl.t0);  // Pᵀ rows [0, S)
   uint16_t* const pt2 = reinterpret_cast<uint16_t*>(sl);           // Pᵀ rows [S, v)
   float* const ycall = reinterpret_cast<float*>(sl + pl.yc_off);  // label coefficients [n]
+  float* const lterm = reinterpret_cast<float*>(sl + pl.lt_off);  // loss terms [n]
   FlceState* const st = reinterpret_cast<FlceState*>(sl + pl.st_off);
   const long long* cnt = &st->count;
   const RowVec none{nullptr, 0, 0};
@@ -1417,10 +1420,10 @@ hipError_t flce_transposed(const FlceArgs& a, const FlceWs& ws, int64_t chunk,
     float* scr = reinterpret_cast<float*>(a.grad_hidden + c0 * h);
     float2* part = reinterpret_cast<float2*>(scr);
     float* lse_c = scr + 2 * rows * ws.tiles;
-    float* term = lse_c + rows;  // first the label logits, then the loss terms
+    float* zy = lse_c + rows;  // the label logits
     View Ah{a.hidden + c0 * h, h, kGroup, rows, h};
     View Bw{a.weight, h, kGroup, v, h};
-    EpiLogits16 el{z16, ws.ldz, a.bias, part, ws.tiles, lab, term};
+    EpiLogits16 el{z16, ws.ldz, a.bias, part, ws.tiles, lab, zy};
     {
       TimedLaunch t(s, K_FLCE_GEMM_LOGITS);
       if ((e = gemm::v2::launch<Wide, true, true>(Ah, Bw, rows, v, h, 1, true, el, s)) !=
@@ -1430,15 +1433,9 @@ hipError_t flce_transposed(const FlceArgs& a, const FlceWs& ws, int64_t chunk,
     {
       TimedLaunch t(s, K_FLCE_ROW_LSE);
       hipLaunchKernelGGL(lse_merge_rows_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s,
-                         part, ws.tiles, nullptr, int64_t(0), term, rows, v, lab, a.ignore_index,
-                         lse_c, int64_t(-1), term, a.lse_out ? a.lse_out + c0 : nullptr,
+                         part, ws.tiles, nullptr, int64_t(0), zy, rows, v, lab, a.ignore_index,
+                         lse_c, int64_t(-1), lterm + c0, a.lse_out ? a.lse_out + c0 : nullptr,
                          RowVec{ycall + c0, 0, 0}, none);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    {
-      TimedLaunch t(s, K_FLCE_LOSS_ACC);
-      hipLaunchKernelGGL(loss_accumulate_kernel, dim3(1), dim3(256), 0, s, term, rows, st,
-                         int(first));
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (a.grad_bias) {
@@ -1454,6 +1451,13 @@ hipError_t flce_transposed(const FlceArgs& a, const FlceWs& ws, int64_t chunk,
                        dim3(unsigned((v + 255) / 256), unsigned((rows + 63) / 64)), dim3(256), 0,
                        s, z16, ws.ldz, rows, v, lab, a.ignore_index, lse_c, part, ws.tiles, pt1,
                        pt2, S, pl.ldp, c0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+
+  // the loss terms of all rows added in row order, in one pass
+  {
+    TimedLaunch t(s, K_FLCE_LOSS_ACC);
+    hipLaunchKernelGGL(loss_accumulate_kernel, dim3(1), dim3(256), 0, s, lterm, n, st, 1);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
 
