@@ -82,28 +82,42 @@ def test_single_pass_ce_graph_replays_match_eager(dev):
         assert torch.equal(logits.view(torch.int16), ref_grad.view(torch.int16)), f"replay {k}"
 
 
-@pytest.mark.parametrize("recompute,bias_grad", [(False, True), (True, True), (True, False)])
-def test_flce_graph_replays_match_eager(dev, recompute, bias_grad):
-    """Both schedules with two chunks per slice (stored logits; recomputing without grad_bias)
-    and the recomputing schedule one chunk at a time (with grad_bias)."""
-    inp = random_flce(333, 128, 3001, bias=True, seed=53)
+@pytest.mark.parametrize("n,h,chunk,recompute,bias_grad,transposed", [
+    (333, 128, 100, False, True, False), (333, 128, 100, True, True, False),
+    (333, 128, 100, True, False, False), (600, 320, 128, False, True, True)])
+def test_flce_graph_replays_match_eager(dev, n, h, chunk, recompute, bias_grad, transposed):
+    """Both schedules with two chunks per slice (stored logits; recomputing without grad_bias),
+    the recomputing schedule one chunk at a time (with grad_bias), and every row's
+    probabilities kept transposed in grad_weight's bytes and the slice."""
+    v = 3001
+    inp = random_flce(n, h, v, bias=True, seed=53)
     hid = bits_to_device(inp.hidden, dev)
     w = bits_to_device(inp.weight, dev)
     b = torch.from_numpy(inp.bias).to(dev)
     lab = torch.from_numpy(inp.labels).to(dev)
-    gh = torch.empty((333, 128), dtype=torch.bfloat16, device=dev)
-    gw = torch.empty((3001, 128), dtype=torch.float32, device=dev)
-    gb = torch.empty(3001, dtype=torch.float32, device=dev) if bias_grad else False
+    gh = torch.empty((n, h), dtype=torch.bfloat16, device=dev)
+    gw = torch.empty((v, h), dtype=torch.float32, device=dev)
+    gb = torch.empty(v, dtype=torch.float32, device=dev) if bias_grad else False
     flags = lce.FLCE_RECOMPUTE if recompute else 0
-    ws = torch.empty(lce.flce_workspace_size(333, 128, 3001, 100, flags), dtype=torch.uint8,
+    ws = torch.empty(lce.flce_workspace_size(n, h, v, chunk, flags), dtype=torch.uint8,
                      device=dev)
     out = {}
 
     def step():
-        out["loss"], _, _, _, _ = lce.flce_fwd_bwd(hid, w, lab, b, chunk_size=100,
+        out["loss"], _, _, _, _ = lce.flce_fwd_bwd(hid, w, lab, b, chunk_size=chunk,
                                                    recompute=recompute, grad_hidden=gh,
                                                    grad_weight=gw, grad_bias=gb, workspace=ws)
 
+    torch.cuda.synchronize()
+    lce.lce_timing_read()
+    lce.lce_timing_enable(True)
+    try:
+        step()
+        torch.cuda.synchronize()
+        names = {name for name, _, _ in lce.lce_timing_read()}
+    finally:
+        lce.lce_timing_enable(False)
+    assert ("flce_probs_transposed" in names) == transposed, names
     step()
     torch.cuda.synchronize()
     outs = [gh, gw] + ([gb] if bias_grad else [])

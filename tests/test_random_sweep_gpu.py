@@ -8,7 +8,9 @@ elements within one bf16 ulp of the exact value; FLCE gradients within the eleme
 budget of the bf16 probability operand; rows without a label exactly zero."""
 import numpy as np
 import pytest
+import torch
 
+import linear_cross_entropy_masked_amd as lce
 import oracle
 from workloads import random_ce, random_flce
 
@@ -104,6 +106,30 @@ def _flce_paired_cases(k=10, seed=2026):
     return out
 
 
+def _flce_transposed_cases(k=8, seed=2027):
+    """Shapes where the stored-logits schedule keeps every row's probabilities transposed in
+    grad_weight's bytes and the slice: chunks a multiple of 64, batches shorter than about
+    2h, hidden widths whose grad_hidden rows hold a chunk's bookkeeping (2h >= 8 * ceil(v /
+    256) + 24 with v < 9000). Each case checks that the schedule ran."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < k:
+        h = 64 * int(rng.integers(3, 13))
+        chunk = 64 * int(rng.integers(1, 4))
+        n = int(rng.integers(chunk, int(1.8 * h) + 1))
+        v = int(np.exp(rng.uniform(np.log(300), np.log(9000))))
+        if n * h * v > 300_000_000:
+            continue
+        bias = bool(rng.random() < 0.5)
+        out.append(dict(
+            n=n, h=h, v=v, chunk=chunk, bias=bias, bias_grad=bias and bool(rng.random() < 0.5),
+            recompute=False, ignore=float(rng.uniform(0, 0.4)),
+            count=None if rng.random() < 0.6 else int(rng.integers(1, 2 * n + 2)),
+            g=None if rng.random() < 0.6 else float(rng.normal(0, 2)),
+            wsig=float(rng.uniform(0.01, 0.2)), seed=int(rng.integers(1 << 30))))
+    return out
+
+
 @pytest.mark.parametrize("c", _flce_cases(),
                          ids=lambda c: f"n{c['n']}_h{c['h']}_v{c['v']}_c{c['chunk']}")
 def test_flce_random_case(dev, c):
@@ -116,6 +142,21 @@ def test_flce_random_case(dev, c):
                                        f"{'_bias' if c['bias'] else ''}{'_gb' if c['bias_grad'] else ''}")
 def test_flce_random_paired_case(dev, c):
     _check_flce_case(dev, c)
+
+
+@pytest.mark.parametrize("c", _flce_transposed_cases(),
+                         ids=lambda c: f"n{c['n']}_h{c['h']}_v{c['v']}_c{c['chunk']}"
+                                       f"{'_bias' if c['bias'] else ''}{'_gb' if c['bias_grad'] else ''}")
+def test_flce_random_transposed_case(dev, c):
+    torch.cuda.synchronize()
+    lce.lce_timing_read()
+    lce.lce_timing_enable(True)
+    try:
+        _check_flce_case(dev, c)
+        names = {name for name, _, _ in lce.lce_timing_read()}
+    finally:
+        lce.lce_timing_enable(False)
+    assert "flce_probs_transposed" in names, names
 
 
 def _check_flce_case(dev, c):
