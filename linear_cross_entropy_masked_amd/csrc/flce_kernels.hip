@@ -27,8 +27,12 @@
 // Where h is a multiple of 64 and C >= 64 (the compact workspace: the slice and nothing
 // else), the stored-logits schedule keeps each chunk's logits as fp16(z − tile max), two
 // chunks per slice, and runs step 6 once per two chunks (flce_paired): the fp32 accumulator
-// is then read and written half as often. The lse and the loss come from the fp32 logits in
-// either form.
+// is then read and written half as often. When, in addition, grad_weight is overwritten, C is
+// a multiple of 64 and the batch is no longer than about 2h (flce_transposed), steps 4-7 run
+// over the whole batch instead: every row's probabilities are kept, transposed, in the slice
+// and in grad_weight's own bytes, then grad_hidden is one product over all rows and
+// grad_weight one plain product per vocabulary range, with no fp32 read-modify-write. The
+// lse and the loss come from the fp32 logits in every form.
 #include <algorithm>
 
 #include "common.h"
@@ -156,16 +160,13 @@ __device__ __forceinline__ int64_t lse_off(int64_t gap, int64_t i) {
   return gap < 0 ? i : gap_index(gap + i);
 }
 
-// One fp32 value per chunk row kept in memory the call owns anyway: p[i] (layout 0), the
-// first half of a 64-float slice group, p[(i / 32) · 64 + i % 32] (layout 1: clear of the
-// split-K partials, which take the second halves), or the slice's free halves from element
-// `base` on (layout 2). p == nullptr: none.
+// One fp32 value per chunk row kept in memory the call owns anyway: p[i] (layout 0), or the
+// slice's free halves from element `base` on (layout 2). p == nullptr: none.
 struct RowVec {
   float* p;
   int64_t base;
   int layout;
   __device__ __forceinline__ float& operator[](int64_t i) const {
-    if (layout == 1) return p[(i >> 5) * 64 + (i & 31)];
     if (layout == 2) return p[gap_index(base + i)];
     return p[i];
   }
@@ -1317,8 +1318,8 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
 // grad_weight's 4 · h, so when the batch is no longer than about 2h it fits the bytes of the
 // fp32 grad_weight the call is about to overwrite, plus the slice:
 //   - grad_weight's bytes [T0, v · 4h) hold Pᵀ rows 0 .. S − 1 (T0 = v · 4h − S · 2 ldp);
-//     the slice's start holds rows S .. v − 1, followed by every row's label coefficient
-//     and the call state;
+//     the slice's start holds rows S .. v − 1, followed by every row's label coefficient and
+//     loss term and the call state;
 //   - grad_weight's bytes [0, T0) hold one chunk's 16-bit shifted logits while the chunks are
 //     formed, then grad_hidden's split partials (if any);
 //   - grad_hidden is then one product over all n rows (K = v) and grad_weight one product
