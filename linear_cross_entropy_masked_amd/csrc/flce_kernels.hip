@@ -817,50 +817,49 @@ __global__ void __launch_bounds__(256) shifted_to_probs_kernel(
   *reinterpret_cast<uint4*>(p) = o;
 }
 
-// The same conversion with the result stored transposed, for the schedule that keeps every
-// row's probabilities (flce_transposed): chunk rows c0 .. c0 + rows − 1 become columns of
-// Pᵀ [v, ldp], whose rows v < seg_rows sit at pt1 + v · ldp and the others at
-// pt2 + (v − seg_rows) · ldp. Values are shifted_to_probs_kernel's bit for bit; tokens past
-// the chunk's rows (the last chunk's, up to ldp) get zeros. A workgroup converts 64 tokens ×
-// 256 columns (one logits tile, so one m_t per token): lane i takes tokens 8 (i % 8) .. + 7
-// and columns 8 (i / 8) .. + 7, with eight 16-byte loads (a wavefront reads 128 contiguous
-// bytes of each of 8 token rows) and eight 16-byte stores (128 contiguous bytes of each of
-// 8 Pᵀ rows); the 8 × 8 transpose is a renaming of registers.
-__global__ void __launch_bounds__(256) shifted_to_probs_t_kernel(
+// The same conversion with the result stored in vocabulary panels, for the schedule that keeps
+// every row's probabilities (flce_transposed): the probabilities of columns 64 b .. 64 b + 63
+// form panel b, a token-major [ldp][64] block (Pᵀ's rows 64 b .. in 64-row blocks, each stored
+// transposed); panels b < seg_panels sit at pt1 + b · ldp · 64, the others at
+// pt2 + (b − seg_panels) · ldp · 64. Chunk rows c0 .. c0 + rows − 1 are tokens c0 ...; values
+// are shifted_to_probs_kernel's bit for bit; tokens past the chunk's rows (the last chunk's, up
+// to ldp) and the last panel's columns past v get zeros. A workgroup converts 256 columns (one
+// logits tile: one m_t per token, four panels) × 64 tokens: lane i takes columns
+// 8 (i % 32) .. + 7 of token 8 it + i / 32 over eight passes, so a wavefront reads 512
+// contiguous bytes of each of two token rows per pass and the workgroup writes 8 KB of each
+// of its panels.
+__global__ void __launch_bounds__(256) shifted_to_probs_p_kernel(
     const uint16_t* __restrict__ z, int64_t ldz, int64_t rows, int64_t v,
     const int32_t* __restrict__ labels, int32_t ignore_index, const float* __restrict__ lse_c,
     const float2* __restrict__ part, int64_t tiles, uint16_t* pt1, uint16_t* pt2,
-    int64_t seg_rows, int64_t ldp, int64_t c0) {
-  const int tg = threadIdx.x & 7, g = threadIdx.x >> 3;
+    int64_t seg_panels, int64_t ldp, int64_t c0) {
   const int64_t vt = blockIdx.x;
-  const int64_t v0 = vt * 256 + 8 * g;
-  if (v0 >= v) return;  // none of the lane's columns exists; else v0 + 8 <= ldz (64 | ldz)
-  const int64_t t0 = int64_t(blockIdx.y) * 64 + 8 * tg;
-  float p[8][8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int64_t t = t0 + r;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) p[r][q] = 0.f;
-    if (t < rows && has_label(labels[t], v, ignore_index)) {
+  const int q = threadIdx.x & 31;
+  const int64_t v0 = vt * 256 + 8 * q;
+  if (v0 >= round_up(v, 64)) return;  // past the last panel
+  const int64_t b = v0 >> 6;
+  uint16_t* panel = (b < seg_panels ? pt1 + b * ldp * 64 : pt2 + (b - seg_panels) * ldp * 64) +
+                    (v0 & 63);
+  const int64_t tend = round_up(rows, 64);
+#pragma unroll 4
+  for (int it = 0; it < 8; ++it) {
+    const int64_t t = int64_t(blockIdx.y) * 64 + it * 8 + (threadIdx.x >> 5);
+    if (t >= tend) break;
+    uint4 o = {0u, 0u, 0u, 0u};
+    if (t < rows && v0 < v && has_label(labels[t], v, ignore_index)) {
       const uint4 x = *reinterpret_cast<const uint4*>(z + t * ldz + v0);
       const float sh = part[t * tiles + vt].x - lse_c[t];
       const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+      float r[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float d = f16_to_f32(w[q >> 1] >> (16 * (q & 1)));
-        p[r][q] = v0 + q < v ? fast_exp2((d + sh) * kLog2e) : 0.f;
+      for (int k = 0; k < 8; ++k) {
+        const float d = f16_to_f32(w[k >> 1] >> (16 * (k & 1)));
+        r[k] = v0 + k < v ? fast_exp2((d + sh) * kLog2e) : 0.f;
       }
+      o = uint4{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]), pack_bf16x2(r[4], r[5]),
+                pack_bf16x2(r[6], r[7])};
     }
-  }
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int64_t row = v0 + q;
-    if (row >= v) break;
-    uint16_t* dst = (row < seg_rows ? pt1 + row * ldp : pt2 + (row - seg_rows) * ldp) + c0 + t0;
-    *reinterpret_cast<uint4*>(dst) =
-        uint4{pack_bf16x2(p[0][q], p[1][q]), pack_bf16x2(p[2][q], p[3][q]),
-              pack_bf16x2(p[4][q], p[5][q]), pack_bf16x2(p[6][q], p[7][q])};
+    *reinterpret_cast<uint4*>(panel + (c0 + t) * 64) = o;
   }
 }
 
@@ -1316,23 +1315,26 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
 // Every row's probabilities kept at once, transposed (stored-logits schedule, no
 // FLCE_ACCUMULATE). Pᵀ [v, ldp] in bf16 takes 2 · ldp bytes per vocabulary row against
 // grad_weight's 4 · h, so when the batch is no longer than about 2h it fits the bytes of the
-// fp32 grad_weight the call is about to overwrite, plus the slice:
-//   - grad_weight's bytes [T0, v · 4h) hold Pᵀ rows 0 .. S − 1 (T0 = v · 4h − S · 2 ldp);
-//     the slice's start holds rows S .. v − 1, followed by every row's label coefficient and
-//     loss term and the call state;
+// fp32 grad_weight the call is about to overwrite, plus the slice. Pᵀ is kept in 64-row
+// panels, each a token-major [ldp][64] block (shifted_to_probs_p_kernel):
+//   - grad_weight's bytes [T0, v · 4h) hold Pᵀ rows 0 .. S − 1 (T0 = v · 4h − S · 2 ldp, S a
+//     multiple of 64); the slice's start holds rows S .. round_up(v, 64) − 1, followed by
+//     every row's label coefficient and loss term and the call state;
 //   - grad_weight's bytes [0, T0) hold one chunk's 16-bit shifted logits while the chunks are
 //     formed, then grad_hidden's split partials (if any);
-//   - grad_hidden is then one product over all n rows (K = v) and grad_weight one product
-//     over all n rows (K = n) per vocabulary range: a plain store, no fp32 read-modify-write.
-//     The launch for rows [r_i, r_{i+1}) writes grad_weight bytes [r_i · 4h, r_{i+1} · 4h),
-//     which must hold no Pᵀ row >= r_i: r_{i+1} · 4h <= T0 + r_i · 2 ldp. The rows in the
-//     slice form the last range, free of that condition.
+//   - grad_hidden is then one product over all n rows (K = v, the panels read K-major) and
+//     grad_weight one product over all n rows (K = n, the panels read MN-major) per
+//     vocabulary range of whole panels: a plain store, no fp32 read-modify-write. The launch
+//     for rows [r_i, r_{i+1}) writes grad_weight bytes [r_i · 4h, r_{i+1} · 4h), which must
+//     hold no Pᵀ row >= r_i: r_{i+1} · 4h <= T0 + r_i · 2 ldp. The rows in the slice form the
+//     last range, free of that condition.
 // Each chunk's tile pairs, lse and loss terms sit in its own grad_hidden rows (flce_paired's
 // layout) until the single grad_hidden product writes them.
 constexpr int kMaxRanges = 64;
 struct TransposedPlan {
   int64_t ldp;             // Pᵀ row length: n rounded up to 64 tokens
   int64_t seg;             // S: Pᵀ rows [0, S) in grad_weight's bytes, [S, v) in the slice
+  int64_t vp;              // v rounded up to whole 64-row panels
   int64_t t0;              // byte offset of Pᵀ row 0 in grad_weight
   int64_t yc_off, lt_off, st_off;  // slice byte offsets: label coefficients, loss terms, state
   int nr;                  // grad_weight launches
@@ -1345,6 +1347,7 @@ bool plan_transposed(int64_t n, int64_t h, int64_t v, int64_t c, int64_t ldz, in
       (v + 255) / 256 > (int64_t(1) << 31) - 1)
     return false;
   p.ldp = round_up(n, 64);
+  p.vp = round_up(v, 64);
   const int64_t pb = 2 * p.ldp, wb = 4 * h;
   // the slice's tail: label coefficients and loss terms (n floats each) and the state; its
   // head also takes the sorted labels of the one-hot pass (2 · kSortMax ints) once
@@ -1356,18 +1359,17 @@ bool plan_transposed(int64_t n, int64_t h, int64_t v, int64_t c, int64_t ldz, in
   const int64_t scratch = c * ldz * 2;                       // one chunk's 16-bit logits
   if (v * wb - scratch < 0) return false;
   const int64_t s_hi = std::min(v, (v * wb - scratch) / pb);  // T0 >= scratch
-  const int64_t s_lo = std::max<int64_t>(0, v - e_max);
+  const int64_t s_lo = std::max<int64_t>(0, p.vp - e_max);
   // one 256 x 256 workgroup per CU: q m-tiles fill the 256 CUs once
   const int64_t nt = (h + Wide::BN - 1) / Wide::BN;
   const int64_t q = 256 % nt == 0 ? 256 / nt : 1;
   int64_t S = round_up(s_lo, q * 256);
   if (S > s_hi) S = round_up(s_lo, 256);
   if (S > s_hi) S = round_up(s_lo, 64);
-  if (S > s_hi) return false;
-  if (S > v) S = v;
+  if (S > s_hi) return false;  // (s_hi <= v, so S <= v and S is a multiple of 64)
   p.seg = S;
   p.t0 = v * wb - S * pb;
-  p.yc_off = std::max<int64_t>(int64_t(align256(size_t((v - S) * pb))), head_min);
+  p.yc_off = std::max<int64_t>(int64_t(align256(size_t((p.vp - S) * pb))), head_min);
   p.lt_off = p.yc_off + int64_t(align256(size_t(n) * 4));
   p.st_off = p.lt_off + int64_t(align256(size_t(n) * 4));
   if (p.st_off + 256 > slice_bytes) return false;
@@ -1378,11 +1380,13 @@ bool plan_transposed(int64_t n, int64_t h, int64_t v, int64_t c, int64_t ldz, in
   while (r < S) {
     const int64_t lim = std::min(S, (p.t0 + r * pb) / wb);  // rows writable from r on
     int64_t nx = lim;
-    if (nx < S) {  // keep ranges whole waves of tiles, else whole tiles
+    if (nx < S) {  // keep ranges whole waves of tiles, else whole tiles, else whole panels
       if (nx - r >= q * 256)
         nx = r + (nx - r) / (q * 256) * (q * 256);
       else if (nx - r >= 256)
         nx = r + (nx - r) / 256 * 256;
+      else
+        nx = r + (nx - r) / 64 * 64;
     }
     if (nx <= r || p.nr >= kMaxRanges) return false;
     p.r[++p.nr] = nx;
@@ -1402,8 +1406,9 @@ hipError_t flce_transposed(const FlceArgs& a, const FlceWs& ws, int64_t chunk,
   char* const sl = reinterpret_cast<char*>(ws.slice);
   char* const gwb = reinterpret_cast<char*>(a.grad_weight);
   uint16_t* const z16 = reinterpret_cast<uint16_t*>(gwb);         // one chunk's 16-bit logits
-  uint16_t* const pt1 = reinterpret_cast<uint16_t*>(gwb + pl.t0);  // Pᵀ rows [0, S)
-  uint16_t* const pt2 = reinterpret_cast<uint16_t*>(sl);           // Pᵀ rows [S, v)
+  uint16_t* const pt1 = reinterpret_cast<uint16_t*>(gwb + pl.t0);  // Pᵀ panels of rows [0, S)
+  uint16_t* const pt2 = reinterpret_cast<uint16_t*>(sl);           // ... of rows [S, v)
+  const int64_t pg = pl.ldp * 64;                                   // elements per panel
   float* const ycall = reinterpret_cast<float*>(sl + pl.yc_off);  // label coefficients [n]
   float* const lterm = reinterpret_cast<float*>(sl + pl.lt_off);  // loss terms [n]
   FlceState* const st = reinterpret_cast<FlceState*>(sl + pl.st_off);
@@ -1448,10 +1453,10 @@ hipError_t flce_transposed(const FlceArgs& a, const FlceWs& ws, int64_t chunk,
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     TimedLaunch t(s, K_FLCE_PROBS_TRANSPOSED);
-    hipLaunchKernelGGL(shifted_to_probs_t_kernel,
+    hipLaunchKernelGGL(shifted_to_probs_p_kernel,
                        dim3(unsigned((v + 255) / 256), unsigned((rows + 63) / 64)), dim3(256), 0,
                        s, z16, ws.ldz, rows, v, lab, a.ignore_index, lse_c, part, ws.tiles, pt1,
-                       pt2, S, pl.ldp, c0);
+                       pt2, S / 64, pl.ldp, c0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
 
@@ -1462,15 +1467,19 @@ hipError_t flce_transposed(const FlceArgs& a, const FlceWs& ws, int64_t chunk,
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
 
-  // grad_hidden = g·s·(P · W − c·W[y]) over all rows, K = v (Pᵀ read MN-major, its rows in
-  // two segments); split over K only when the row tiles alone do not fill the chip, the
-  // partials then in grad_weight's bytes below Pᵀ. (Leaving fp32 P · W there and applying
-  // the one-hot term in the streaming reduce pass measured no faster than the epilogue.)
+  // grad_hidden = g·s·(P · W − c·W[y]) over all rows, K = v (the panels read K-major: rows
+  // = tokens, 64 columns per panel, the panels in two segments); split over K only when the
+  // row tiles alone do not fill the chip, the partials then in grad_weight's bytes below Pᵀ.
+  // (Leaving fp32 P · W there and applying the one-hot term in the streaming reduce pass
+  // measured no faster than the epilogue.)
   {
-    View Ap{S > 0 ? pt1 : pt2, pl.ldp, kGroup, v, n};
-    if (S > 0 && S < v) {
+    const bool two = S > 0 && S < v;
+    View Ap{S > 0 ? pt1 : pt2, 64, pg, n, v};
+    Ap.ext = (S > 0 ? S : pl.vp) * pl.ldp;
+    if (two) {
       Ap.p2 = pt2;
       Ap.kseg = S;
+      Ap.ext2 = (pl.vp - S) * pl.ldp;
     }
     View Bw2{a.weight, h, kGroup, v, h};
     const int64_t tiles = row_tiles(n) * ((h + Wide::BN - 1) / Wide::BN);
@@ -1484,18 +1493,17 @@ hipError_t flce_transposed(const FlceArgs& a, const FlceWs& ws, int64_t chunk,
     const RowVec yc{ycall, 0, 0};
     {
       TimedLaunch t(s, K_FLCE_GEMM_GRAD_HIDDEN);
-      const bool two = S > 0 && S < v;
       if (!partials) {
         EpiGradHidden eh{a.grad_hidden, h, a.labels, a.weight, h, v, a.ignore_index, cnt, th,
                          a.grad_output, 0.f, yc};
-        e = two ? gemm::v2::launch<Wide, false, false, EpiGradHidden, true>(Ap, Bw2, n, h, v, 1,
-                                                                             true, eh, s, true)
-                : gemm::v2::launch<Wide, false, false>(Ap, Bw2, n, h, v, 1, true, eh, s, true);
+        e = two ? gemm::v2::launch<Wide, true, false, EpiGradHidden, true>(Ap, Bw2, n, h, v, 1,
+                                                                            true, eh, s, true)
+                : gemm::v2::launch<Wide, true, false>(Ap, Bw2, n, h, v, 1, true, eh, s, true);
       } else {
         EpiPartial ep{part, n, h, 0, 0};
-        e = two ? gemm::v2::launch<Wide, false, false, EpiPartial, true>(Ap, Bw2, n, h, v,
-                                                                          splits, true, ep, s)
-                : gemm::v2::launch<Wide, false, false>(Ap, Bw2, n, h, v, splits, true, ep, s);
+        e = two ? gemm::v2::launch<Wide, true, false, EpiPartial, true>(Ap, Bw2, n, h, v,
+                                                                         splits, true, ep, s)
+                : gemm::v2::launch<Wide, true, false>(Ap, Bw2, n, h, v, splits, true, ep, s);
       }
       if (e != hipSuccess) return e;
     }
@@ -1508,15 +1516,17 @@ hipError_t flce_transposed(const FlceArgs& a, const FlceWs& ws, int64_t chunk,
     }
   }
 
-  // grad_weight = g·s·Pᵀ · hidden over all rows (K = n), one launch per vocabulary range
+  // grad_weight = g·s·Pᵀ · hidden over all rows (K = n), one launch per vocabulary range of
+  // whole panels (read MN-major: k rows = tokens, 64 vocabulary columns per panel)
   View Bh{a.hidden, h, kGroup, n, h};
   for (int i = 0; i < pl.nr; ++i) {
     const int64_t r0 = pl.r[i], r1 = pl.r[i + 1];
     const uint16_t* base = r0 < S ? pt1 + r0 * pl.ldp : pt2 + (r0 - S) * pl.ldp;
-    View Ap{base, pl.ldp, kGroup, r1 - r0, n};
+    View Ap{base, 64, pg, n, r1 - r0};
+    Ap.ext = ((r0 < S ? S : pl.vp) - r0) * pl.ldp;
     EpiGradWeight ew{a.grad_weight + r0 * h, h, 1, cnt, th, a.grad_output, 0.f};
     TimedLaunch t(s, K_FLCE_GEMM_GRAD_WEIGHT);
-    if ((e = gemm::v2::launch<Wide, true, false>(Ap, Bh, r1 - r0, h, n, 1, true, ew, s, true)) !=
+    if ((e = gemm::v2::launch<Wide, false, false>(Ap, Bh, r1 - r0, h, n, 1, true, ew, s, true)) !=
         hipSuccess)
       return e;
   }

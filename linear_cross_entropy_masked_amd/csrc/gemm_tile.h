@@ -40,10 +40,19 @@ struct View {
   int64_t gs;    // elements between consecutive 64-column groups
   int64_t rows;  // valid rows
   int64_t cols;  // valid columns
-  // Two-segment MN-major operand (pipelined GEMM launched with SEGA): rows kseg .. rows − 1
-  // sit at p2 + (row − kseg) · ld instead of p + row · ld. kseg is a multiple of the K slice.
+  // Two-segment operand (pipelined GEMM launched with SEGA): k rows kseg .. of an MN-major
+  // operand sit at p2 + (row − kseg) · ld instead of p + row · ld; k columns kseg .. of a
+  // K-major panel operand (below) at p2 with column col − kseg. kseg is a multiple of the K
+  // slice (and of 64 for panels).
   const uint16_t* p2 = nullptr;
   int64_t kseg = 0;
+  // Panels (ext > 0): the 64-column groups lie gs apart as whole [rows][64] blocks (gs >=
+  // rows · ld), and ext / ext2 are the elements stored from p / p2 on. The DMA window then
+  // runs to the end of that storage instead of masking rows or k past the valid range: the
+  // caller zero-fills what a product may read there (padding rows and columns of the last
+  // panel); rows past the last panel of a K-major operand only reach output rows past M.
+  int64_t ext = 0;
+  int64_t ext2 = 0;
 };
 
 // Buffer resource over [base, base + bytes): loads at offsets past the end return zero, which
@@ -374,18 +383,34 @@ struct Stream {
 };
 
 // Window of the K slice starting at k0 (a multiple of BK) for rows / columns r0 .. r0 + R − 1.
-// SEG (MN-major only): the operand's k rows come in the two segments View::p / View::p2.
+// SEG: the operand's k rows (MN-major) or k columns (K-major panels) come in the two segments
+// View::p / View::p2.
 template <bool KMAJOR, int BK, bool SEG = false>
 __device__ __forceinline__ Stream stream_at(const View& X, int64_t r0, int64_t k0, int64_t K) {
-  static_assert(!(SEG && KMAJOR), "two segments split the k rows of an MN-major operand");
   Stream st;
   st.left = 0;
   st.base2 = 0;
   st.recs2 = 0;
   if constexpr (KMAJOR) {
-    const int64_t g = (k0 >> 6) * X.gs + (k0 & 63);
-    st.base = reinterpret_cast<uint64_t>(X.p + r0 * X.ld + g);
-    st.recs = ((X.rows - r0) * X.ld - g) * 2;
+    if (X.ext > 0) {  // panels: the window runs to the end of the segment's storage
+      auto at = [&](int64_t kk) { return (kk >> 6) * X.gs + (kk & 63) + r0 * X.ld; };
+      if (SEG && k0 >= X.kseg) {
+        st.base = reinterpret_cast<uint64_t>(X.p2 + at(k0 - X.kseg));
+        st.recs = (X.ext2 - at(k0 - X.kseg)) * 2;
+      } else {
+        st.base = reinterpret_cast<uint64_t>(X.p + at(k0));
+        st.recs = (X.ext - at(k0)) * 2;
+        if (SEG) {
+          st.left = (X.kseg - k0) / BK;
+          st.base2 = reinterpret_cast<uint64_t>(X.p2 + at(0));
+          st.recs2 = (X.ext2 - at(0)) * 2;
+        }
+      }
+    } else {
+      const int64_t g = (k0 >> 6) * X.gs + (k0 & 63);
+      st.base = reinterpret_cast<uint64_t>(X.p + r0 * X.ld + g);
+      st.recs = ((X.rows - r0) * X.ld - g) * 2;
+    }
     if (BK == 64) {
       st.step = st.step2 = X.gs * 2;
     } else {  // 32 within a group, then on to the next group's start
@@ -398,7 +423,10 @@ __device__ __forceinline__ Stream stream_at(const View& X, int64_t r0, int64_t k
     // (the shifted base would otherwise let the last row's columns past `cols` run over it)
     const int64_t kall = X.rows < K ? X.rows : K;
     const int64_t shift = (r0 >> 6) * X.gs;
-    if (SEG && k0 >= X.kseg) {  // starts in the second segment
+    if (X.ext > 0) {  // panels (one segment): the window runs to the end of the storage
+      st.base = reinterpret_cast<uint64_t>(X.p + k0 * X.ld + shift);
+      st.recs = (X.ext - (k0 * X.ld + shift)) * 2;
+    } else if (SEG && k0 >= X.kseg) {  // starts in the second segment
       const int64_t kr = kall - k0;
       const int64_t avail = (X.rows - k0) * X.ld - shift;
       st.base = reinterpret_cast<uint64_t>(X.p2 + (k0 - X.kseg) * X.ld + shift);
@@ -833,8 +861,11 @@ hipError_t launch(const View& A, const View& B, int64_t M, int64_t N, int64_t K,
                   bool m_fast, const Epi& epi, hipStream_t s, bool xcd_blocks = false) {
   // grouped K-major operands keep whole groups of 64 (see stream_at)
   if ((AK && A.gs < 64) || (BKM && B.gs < 64)) return hipErrorInvalidValue;
-  // a two-segment A: MN-major, both segments given, split at a slice boundary
-  if (SEGA && (AK || A.p2 == nullptr || A.kseg <= 0 || A.kseg % C::BK != 0 || A.kseg >= A.rows))
+  // a two-segment A: MN-major rows or K-major panel columns, both segments given, split at a
+  // slice boundary (a panel boundary for panels); MN-major panels come in one segment
+  if (SEGA && (A.p2 == nullptr || A.kseg <= 0 || A.kseg % C::BK != 0 ||
+               (AK ? (A.ext <= 0 || A.ext2 <= 0 || A.kseg % 64 != 0 || A.kseg >= A.cols)
+                   : (A.ext > 0 || A.kseg >= A.rows))))
     return hipErrorInvalidValue;
   TileMap tm{(M + C::BM - 1) / C::BM, (N + C::BN - 1) / C::BN, splits < 1 ? 1 : splits, m_fast};
   int64_t ksplit = (K + tm.splits - 1) / tm.splits;

@@ -5,8 +5,9 @@ batch no longer than about twice the hidden width, the call keeps every row's bf
 probabilities at once, transposed: the vocabulary rows that fit in the slice at its start, the
 others in the bytes of the fp32 grad_weight it is about to overwrite. grad_hidden is then one
 product over all rows and grad_weight one product per vocabulary range, each a plain store.
-The cases below reach each part of that layout: two segments of Pᵀ, several grad_weight
-ranges (whole tiles and ranges of a few rows), padding tokens, grad_hidden split over K with
+Pᵀ is kept in 64-row panels, each token-major. The cases below reach each part of that
+layout: two segments of Pᵀ, several grad_weight ranges (whole tiles and single panels), a
+vocabulary that ends inside a panel, padding tokens, grad_hidden split over K with
 its partials in grad_weight's bytes, all of Pᵀ in the slice, and batches of more rows than one
 label sort holds. Bars as in test_flce_gpu: the oracle's loss to 1e-5, every grad_weight and
 grad_hidden element to the bf16 rounding budget of the probabilities, normwise 1e-4 where the
@@ -75,10 +76,11 @@ def test_transposed_schedule_peaked_rows(dev):
 
 
 def test_more_rows_than_one_label_sort(dev):
-    """8300 rows (two label sorts for the one-hot term of grad_weight), vocabulary ranges of
-    40-odd rows (partial tiles) because a Pᵀ row (16640 B) is longer than a grad_weight row."""
-    inp = random_flce(8300, 4096, 300, weight_sigma=0.05, bias=False, ignore_frac=0.1, seed=4)
-    res, names = kernels_run(lambda: run_flce(dev, inp, 1024))
+    """8300 rows (two label sorts for the one-hot term of grad_weight), grad_weight ranges of a
+    single 64-row panel (partial tiles) because a Pᵀ row takes as many bytes as a grad_weight
+    row (16640 B) and the slice holds only a few panels."""
+    inp = random_flce(8300, 4160, 300, weight_sigma=0.05, bias=False, ignore_frac=0.1, seed=4)
+    res, names = kernels_run(lambda: run_flce(dev, inp, 2048))
     assert TRANSPOSED in names
     assert res["status"] == 0
     check(inp, res)

@@ -106,7 +106,7 @@ def _flce_paired_cases(k=10, seed=2026):
     return out
 
 
-def _flce_transposed_cases(k=8, seed=2027):
+def _flce_transposed_cases(k=8, seed=2028):
     """Shapes where the stored-logits schedule keeps every row's probabilities transposed in
     grad_weight's bytes and the slice: chunks a multiple of 64, batches shorter than about
     2h, hidden widths whose grad_hidden rows hold a chunk's bookkeeping (2h >= 8 * ceil(v /
