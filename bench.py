@@ -80,7 +80,7 @@ KERNEL_NAMES = [
     ("EpiPartial", "flce_gemm_grad_hidden"), ("EpiGradWeight", "flce_gemm_grad_weight"),
     ("slice_row_lse_kernel", "flce_row_lse"), ("slice_bias_grad_kernel", "flce_bias_grad"),
     ("slice_to_probs_kernel", "flce_to_probs"), ("shifted_to_probs_kernel", "flce_to_probs"),
-    ("shifted_to_probs_t_kernel", "flce_probs_transposed"),
+    ("shifted_to_probs_p_kernel", "flce_probs_transposed"),
     ("shifted_bias_grad_kernel", "flce_bias_grad"), ("onehot_weight_fix_kernel", "flce_onehot_fix"),
     ("grad_hidden_reduce_kernel", "flce_grad_hidden_reduce"), ("fill_zero", "fill_zero"),
     ("label_rank_kernel", "flce_label_sort"), ("label_prep_kernel", "label_prep"),
