@@ -52,6 +52,21 @@ using gemm::View;
 using Wide = gemm::v2::CfgWide;  // the two large-K products
 using Pair = gemm::v2::CfgPair;  // grad_weight: fp32 read-modify-write epilogue
 
+// grad_weight over K = `rows` chunk rows into the fp32 accumulator. Two 256 × 128
+// workgroups per CU overlap one's read-modify-write epilogue with the other's MFMAs; from
+// K = 4096 on, a 256 × 256 tile's mainloop is long enough that its faster operand stream
+// wins back more than its exposed epilogue costs. Measured, ms per step on 256 × 128 against
+// 256 × 256: Llama3-8B head, K = 1024, 11.9 against 13.3; K = 2048, 9.00–9.05 against 9.07;
+// long-context workload, K = 4096, 65.7 against 64.2–64.4.
+constexpr int64_t kGradWeightWideK = 4096;
+template <class Epi>
+hipError_t launch_grad_weight(const View& A, const View& B, int64_t v, int64_t h, int64_t rows,
+                              const Epi& e, hipStream_t s) {
+  if (rows >= kGradWeightWideK)
+    return gemm::v2::launch<Wide, false, false>(A, B, v, h, rows, 1, false, e, s, true);
+  return gemm::v2::launch<Pair, false, false>(A, B, v, h, rows, 1, false, e, s, true);
+}
+
 __device__ __forceinline__ float flce_coef(const long long* count_dev, long long count_host,
                                            const float* gout) {
   const long long t = count_host >= 0 ? count_host : *count_dev;
@@ -1240,7 +1255,7 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
     EpiGradWeight ew{a.grad_weight, h, int(first && !accumulate), cnt, th, a.grad_output, 0.f};
     {
       TimedLaunch t(s, K_FLCE_GEMM_GRAD_WEIGHT);
-      hipError_t r = gemm::v2::launch<Pair, false, false>(Ap, Bh, v, h, rows, 1, false, ew, s, true);
+      hipError_t r = launch_grad_weight(Ap, Bh, v, h, rows, ew, s);
       if (r != hipSuccess) return r;
     }
     if (rows <= kSortMax) {
@@ -1796,9 +1811,7 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
     }
     if (a.grad_weight) {
       TimedLaunch t(s, K_FLCE_GEMM_GRAD_WEIGHT);
-      if ((e = gemm::v2::launch<Pair, false, false>(Ap, Bh, v, h, rows, 1, false, ew, s, true)) !=
-          hipSuccess)
-        return e;
+      if ((e = launch_grad_weight(Ap, Bh, v, h, rows, ew, s)) != hipSuccess) return e;
     }
     if (a.grad_hidden && splits > 1) {
       TimedLaunch t(s, K_FLCE_GRAD_HIDDEN_REDUCE);

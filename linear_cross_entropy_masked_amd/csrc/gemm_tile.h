@@ -674,7 +674,12 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
       if (gm < M) rtag[i] = epi.row_tag(gm);
     }
   }
-  if constexpr (Epi::kTileMax) {
+  // Each row's maximum over this wavefront's valid columns (the four lanes sharing the row
+  // reduced with shuffles): the shift of the row statistics and the start of the tile maximum.
+  float wmax[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) wmax[i] = -INFINITY;
+  if constexpr (Epi::kTileMax || Epi::kRowStats) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int64_t gm = m0 + wm * (C::BM / C::WM) + 16 * i + (lane & 15);
@@ -694,13 +699,15 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
         }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      tmax[i] = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      wmax[i] = fmaxf(mx, __shfl_xor(mx, 32, 64));
     }
+  }
+  if constexpr (Epi::kTileMax) {
     __syncthreads();  // every wavefront is past the main loop: the LDS ring is free
     float* red = reinterpret_cast<float*>(lds);  // [WN][BM]
     if ((lane >> 4) == 0) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i) red[wn * C::BM + wm * (C::BM / C::WM) + 16 * i + lane] = tmax[i];
+      for (int i = 0; i < TM; ++i) red[wn * C::BM + wm * (C::BM / C::WM) + 16 * i + lane] = wmax[i];
     }
     __syncthreads();
 #pragma unroll
@@ -754,15 +761,12 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
             epi.store4(gm, gn, acc[i0 + di][j], aux[di][j]);
           if constexpr (Epi::kColSums) cs[j] += epi.colvalue4(acc[i0 + di][j], aux[di][j]);
           if constexpr (Epi::kRowStats) {
+            // shift as (z − max) · log2 e: the wavefront's row maximum contributes exactly 1
             const f32x4_t z = epi.value4(acc[i0 + di][j], aux[di][j]);
-            const float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-            // shift as (z − max) · log2 e: the maximum contributes exactly 1
-            const float mn = fmaxf(rm[i0 + di], mx);
-            float t = rm[i0 + di] == mn ? rs[i0 + di]
-                                        : rs[i0 + di] * fast_exp2((rm[i0 + di] - mn) * kLog2e);
+            const float mw = wmax[i0 + di];
+            float t = rs[i0 + di];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) t += fast_exp2((z[q] - mn) * kLog2e);
-            rm[i0 + di] = mn;
+            for (int q = 0; q < 4; ++q) t += fast_exp2((z[q] - mw) * kLog2e);
             rs[i0 + di] = t;
           }
         } else {
@@ -773,13 +777,9 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
                 epi.put1m(gm, gn + q, acc[i0 + di][j][q], tmax[i0 + di], rtag[i0 + di]);
               else
                 epi(gm, gn + q, acc[i0 + di][j][q]);
-              if constexpr (Epi::kRowStats) {
-                const float z = epi.value1(gn + q, acc[i0 + di][j][q]);
-                float m1 = rm[i0 + di], s1 = rs[i0 + di];
-                lse_merge(m1, s1, z, 1.f);
-                rm[i0 + di] = m1;
-                rs[i0 + di] = s1;
-              }
+              if constexpr (Epi::kRowStats)
+                rs[i0 + di] +=
+                    fast_exp2((epi.value1(gn + q, acc[i0 + di][j][q]) - wmax[i0 + di]) * kLog2e);
             }
         }
       }
@@ -813,15 +813,13 @@ __device__ __forceinline__ void run_tile(const View& A, const View& B, int64_t M
     }
   }
   if constexpr (Epi::kRowStats) {
-    // lanes l, l ^ 16, l ^ 32 and l ^ 48 hold the same rows: merge them, then merge the WN
-    // wavefronts that share each row through LDS, in wavefront order
+    // lanes l, l ^ 16, l ^ 32 and l ^ 48 hold the same rows under the same shift: add their
+    // sums, then merge the WN wavefronts that share each row through LDS, in wavefront order
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-#pragma unroll
-      for (int off = 16; off <= 32; off <<= 1) {
-        const float m2 = __shfl_xor(rm[i], off, 64), s2 = __shfl_xor(rs[i], off, 64);
-        lse_merge(rm[i], rs[i], m2, s2);
-      }
+      rs[i] += __shfl_xor(rs[i], 16, 64);
+      rs[i] += __shfl_xor(rs[i], 32, 64);
+      rm[i] = wmax[i];
     }
     __syncthreads();  // every wavefront is past the main loop: the LDS ring is free
     float2* red = reinterpret_cast<float2*>(lds);  // [WN][BM]
