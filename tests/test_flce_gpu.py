@@ -328,6 +328,25 @@ def test_two_chunks_per_slice_accumulate(dev, n, chunk):
     check(inp, res, init=init)
 
 
+@pytest.mark.parametrize("recompute,accumulate", [(False, False), (False, True), (True, False)])
+def test_two_chunks_per_slice_wide_grad_weight(dev, recompute, accumulate):
+    """Pairs of 2048-row chunks: grad_weight over K = 4096 rows goes through 256 × 256 tiles
+    (read-modify-write when accumulating), the short last pair (2748 rows) through the two
+    256 × 128 workgroups per CU; both schedules, against the oracle element by element."""
+    n, h, v, chunk = 6844, 128, 1500, 2048
+    assert stores_16bit_logits(n, h, v, chunk)
+    inp = random_flce(n, h, v, weight_sigma=0.2, bias=True, ignore_frac=0.1,
+                      seed=4096 + 2 * int(recompute) + int(accumulate))
+    init = None
+    if accumulate:
+        rng = np.random.default_rng(4099)
+        init = (rng.normal(0, 0.01, (v, h)), rng.normal(0, 0.01, v))
+    res = run_flce(dev, inp, chunk, count=n - 7, g=0.5, recompute=recompute,
+                   accumulate_init=init, want_bias_grad=not recompute)
+    assert res["status"] == 0
+    check(inp, res, count=n - 7, g=0.5, init=init)
+
+
 def test_two_chunks_per_slice_without_grad_weight(dev):
     """Paired chunks when only grad_hidden is asked for: the grad_weight product and its
     one-hot term are skipped; grad_hidden, loss and lse are the full call's."""
