@@ -379,24 +379,24 @@ struct EpiGradWeight {
 
 // One chunk's rows sorted by label, stably (rows in increasing order within a label):
 // slab[p] is the chunk's p-th smallest label (rows without a label count as 0x7fffffff and
-// come last) and srow[p] its row. A row's position is the number of the chunk's rows before
-// it in that order. Workgroup b places rows 64 b .. 64 b + 63: its four wavefronts count over
-// one quarter each of the chunk's labels, held in LDS, and the four counts are added.
+// come last) and srow[p] its row. Each row's sort key is label · kSortMax + row, all keys
+// distinct, so a row's position is the number of keys below its own. Workgroup b places
+// rows 64 b .. 64 b + 63: its kRankWaves wavefronts count over one slice each of the keys,
+// held in LDS (one 64-bit compare per key), and the counts are added.
 constexpr int kSortMax = 8192;
-__global__ void __launch_bounds__(256) label_rank_kernel(const int32_t* __restrict__ labels,
-                                                         int64_t rows, int64_t v,
-                                                         int32_t ignore_index,
-                                                         int32_t* __restrict__ slab,
-                                                         int32_t* __restrict__ srow) {
-  __shared__ __attribute__((aligned(16))) int32_t k[kSortMax];
-  __shared__ int cnt[4][64];
+constexpr int kRankWaves = 16;
+__global__ void __launch_bounds__(64 * kRankWaves) label_rank_kernel(
+    const int32_t* __restrict__ labels, int64_t rows, int64_t v, int32_t ignore_index,
+    int32_t* __restrict__ slab, int32_t* __restrict__ srow) {
+  __shared__ __attribute__((aligned(16))) long long k[kSortMax];
+  __shared__ int cnt[kRankWaves][64];
   const int n = int(rows);
-  const int n4 = (n + 3) & ~3;  // padded with 0x7fffffff: never before any row
-  for (int i = threadIdx.x; i < n4; i += 256) {
-    int32_t key = 0x7fffffff;
+  const int n2 = (n + 1) & ~1;  // padded with the largest key: never below any row's
+  for (int i = threadIdx.x; i < n2; i += 64 * kRankWaves) {
+    long long key = 0x7fffffffffffffffLL;
     if (i < n) {
       const int32_t y = labels[i];
-      if (has_label(y, v, ignore_index)) key = y;
+      key = (long long)(has_label(y, v, ignore_index) ? y : 0x7fffffff) * kSortMax + i;
     }
     k[i] = key;
   }
@@ -405,22 +405,21 @@ __global__ void __launch_bounds__(256) label_rank_kernel(const int32_t* __restri
   const int i = int(blockIdx.x) * 64 + r;
   int rank = 0;
   if (i < n) {
-    const int32_t x = k[i];
-    const int per = ((n4 >> 2) + 3) & ~3;  // a multiple of 4 with 4 · per >= n4
-    const int lo = q * per, hi = lo + per < n4 ? lo + per : n4;
-    for (int j = lo; j < hi; j += 4) {
-      const int4 c = *reinterpret_cast<const int4*>(k + j);
-      rank += (c.x < x) | ((c.x == x) & (j < i));
-      rank += (c.y < x) | ((c.y == x) & (j + 1 < i));
-      rank += (c.z < x) | ((c.z == x) & (j + 2 < i));
-      rank += (c.w < x) | ((c.w == x) & (j + 3 < i));
+    const long long x = k[i];
+    const int per = ((n2 + kRankWaves - 1) / kRankWaves + 1) & ~1;  // even, kRankWaves · per >= n2
+    const int lo = q * per, hi = lo + per < n2 ? lo + per : n2;
+    for (int j = lo; j < hi; j += 2) {
+      const longlong2 c = *reinterpret_cast<const longlong2*>(k + j);
+      rank += int(c.x < x) + int(c.y < x);
     }
   }
   cnt[q][r] = rank;
   __syncthreads();
   if (q == 0 && i < n) {
-    const int p = cnt[0][r] + cnt[1][r] + cnt[2][r] + cnt[3][r];
-    slab[p] = k[i];
+    int p = 0;
+#pragma unroll
+    for (int w = 0; w < kRankWaves; ++w) p += cnt[w][r];
+    slab[p] = int32_t(k[i] / kSortMax);
     srow[p] = i;
   }
 }
@@ -1263,8 +1262,8 @@ hipError_t flce_paired(const FlceArgs& a, const FlceWs& ws, int64_t chunk, FlceS
       int32_t* srow = slab + rows;
       {
         TimedLaunch t(s, K_FLCE_LABEL_SORT);
-        hipLaunchKernelGGL(label_rank_kernel, dim3(unsigned((rows + 63) / 64)), dim3(256), 0, s,
-                           lab, rows, v, a.ignore_index, slab, srow);
+        hipLaunchKernelGGL(label_rank_kernel, dim3(unsigned((rows + 63) / 64)),
+                           dim3(64 * kRankWaves), 0, s, lab, rows, v, a.ignore_index, slab, srow);
         if ((e = hipGetLastError()) != hipSuccess) return e;
       }
       TimedLaunch t(s, K_FLCE_ONEHOT_FIX);
@@ -1554,8 +1553,9 @@ hipError_t flce_transposed(const FlceArgs& a, const FlceWs& ws, int64_t chunk,
     const int64_t rows = n - g0 < kSortMax ? n - g0 : kSortMax;
     {
       TimedLaunch t(s, K_FLCE_LABEL_SORT);
-      hipLaunchKernelGGL(label_rank_kernel, dim3(unsigned((rows + 63) / 64)), dim3(256), 0, s,
-                         a.labels + g0, rows, v, a.ignore_index, slab, srow);
+      hipLaunchKernelGGL(label_rank_kernel, dim3(unsigned((rows + 63) / 64)),
+                         dim3(64 * kRankWaves), 0, s, a.labels + g0, rows, v, a.ignore_index,
+                         slab, srow);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     TimedLaunch t(s, K_FLCE_ONEHOT_FIX);
@@ -1829,8 +1829,9 @@ hipError_t flce_run(const FlceArgs& a, hipStream_t s) {
         int32_t* srow = slab + rows;
         {
           TimedLaunch t(s, K_FLCE_LABEL_SORT);
-          hipLaunchKernelGGL(label_rank_kernel, dim3(unsigned((rows + 63) / 64)), dim3(256), 0, s,
-                             lab, rows, v, a.ignore_index, slab, srow);
+          hipLaunchKernelGGL(label_rank_kernel, dim3(unsigned((rows + 63) / 64)),
+                             dim3(64 * kRankWaves), 0, s, lab, rows, v, a.ignore_index, slab,
+                             srow);
           if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         TimedLaunch t(s, K_FLCE_ONEHOT_FIX);
